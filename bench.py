@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of multi-row speculative-verification decode attention on one MI355X.
+
+Workload (the full-attention single-GPU share): 1 KV head, 6 query heads,
+head_dim 128, 8 query rows with 4..8 live, causal mask at the boundary, bf16
+K/V/q ~ N(0,1), sink logits ~ N(0,1), KV capacity preallocated at 262,144
+keys, contexts 1K, 4K, 16K, 32K, 64K, 128K and 192K; split count chosen by
+the plan.  One step = one verify call (split + combine) at each of the seven
+contexts.
+
+Cold-cache rule: every context of every replica has its own 256K-capacity
+cache (6 replicas x 7 contexts); step i reads replica i % 6, so about 1.4 GB
+of distinct KV is streamed between two reads of the same bytes, more than
+the 256 MB Infinity Cache.  Capacity beyond each read extent is NaN: reading
+it would poison the output, which the full-size parity check below catches.
+
+Timing:
+  * value / ms_per_step: HIP events (torch's stream, where the library
+    launches) around `steps` back-to-back steps, no events inside.
+  * per-context kernel times and the roofline: a second pass with an event
+    pair around every split launch (and every combine launch) on the same
+    stream.
+The CPU baseline times the float64 oracle on the same stored bytes (one pass
+over the seven contexts) and doubles as a full-size parity check of the GPU
+outputs of replica 0.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+CONTEXTS = [1024, 4096, 16384, 32768, 65536, 131072, 196608]
+ROWS, HQ, HKV, D, CAP = 8, 6, 1, 128, 262144
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+REPLICAS = 6
+METRIC = "verify-attn µs/call and KV-read GB/s (% HBM peak), 8 rows×6 heads, 1K–192K ctx"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_config2_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "verify_attn.hip")
+
+
+def kv_bytes(hi):
+    """Algorithmic KV bytes of one call: every visible key's K and V once (bf16)."""
+    return hi * HKV * 4 * D
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ctx", type=int, action="append", help="restrict to these contexts")
+    ap.add_argument("--splits", type=int, default=0, help="force the split count (0: plan chooses)")
+    ap.add_argument("--replicas", type=int, default=REPLICAS)
+    ap.add_argument("--kernel-reps", type=int, default=30, help="event-timed launches per context")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+                  "the verification call is a single-GPU kernel and no multi-GPU path exists.", flush=True)
+        sys.exit(2)
+
+    import torch
+    import speculative_decode_verify_amd as va
+    from speculative_decode_verify_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    contexts = args.ctx or CONTEXTS
+    stream = torch.cuda.current_stream()
+
+    # ---------------- inputs ----------------
+    cases = []
+    for ctx in contexts:
+        g = synth.gen(2000 + ctx // 1024)
+        live = synth.live_count(g)
+        hi = ctx + live
+        q = synth.normal_bf16((ROWS, HQ, D), g).to(dev)
+        sink = synth.normal_f32((HQ,), g).to(dev)
+        plan = va.Plan(rows=ROWS, live_rows=live, q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
+                       first_pos=ctx, kv_capacity=CAP, scale=1 / math.sqrt(D), splits=args.splits)
+        kvs = []
+        for r in range(args.replicas):
+            k = torch.full((HKV, CAP, D), float("nan"), dtype=torch.bfloat16, device=dev)
+            v = torch.full((HKV, CAP, D), float("nan"), dtype=torch.bfloat16, device=dev)
+            k[:, :hi] = synth.normal_bf16_device((HKV, hi, D), 10_000 * r + ctx, dev)
+            v[:, :hi] = synth.normal_bf16_device((HKV, hi, D), 10_000 * r + ctx + 1, dev)
+            kvs.append((k, v))
+        ws = va.workspace_for(plan, dev)
+        out = torch.empty((ROWS, HQ, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((ROWS, HQ), dtype=torch.float32, device=dev)
+        cases.append(dict(ctx=ctx, live=live, hi=hi, q=q, sink=sink, plan=plan, kvs=kvs, ws=ws, out=out, lse=lse))
+    torch.cuda.synchronize()
+
+    def call(c, rep):
+        k, v = c["kvs"][rep]
+        va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=stream)
+        va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"], stream=stream)
+
+    def step(i):
+        for c in cases:
+            call(c, i % args.replicas)
+
+    # ---------------- parity of replica 0 at full size (kept for the CPU leg) ----------------
+    for c in cases:
+        call(c, 0)
+    torch.cuda.synchronize()
+    gpu_out0 = [(c["out"].double().cpu().numpy(), c["lse"].double().cpu().numpy()) for c in cases]
+
+    # ---------------- pass A: whole steps ----------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    bytes_per_step = sum(kv_bytes(c["hi"]) for c in cases)
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    # ---------------- pass B: per-launch kernel times ----------------
+    sweep = []
+    split_bytes, split_ms = 0.0, 0.0
+    for c in cases:
+        ts, tc = [], []
+        for i in range(args.kernel_reps):
+            k, v = c["kvs"][i % args.replicas]
+            a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=stream)
+            b.record(stream)
+            va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"], stream=stream)
+            d.record(stream)
+            ts.append((a, b))
+            tc.append((b, d))
+        torch.cuda.synchronize()
+        s_ms = sorted(x.elapsed_time(y) for x, y in ts)
+        c_ms = sorted(x.elapsed_time(y) for x, y in tc)
+        s_avg = sum(s_ms) / len(s_ms)
+        c_avg = sum(c_ms) / len(c_ms)
+        nb = kv_bytes(c["hi"])
+        split_bytes += nb * len(s_ms)
+        split_ms += sum(s_ms)
+        gbs = nb / (s_avg * 1e-3) / 1e9
+        sweep.append({
+            "ctx": c["ctx"], "live": c["live"], "splits": c["plan"].splits, "kv_bytes": nb,
+            "us_per_call": round((s_avg + c_avg) * 1e3, 2),
+            "split_us": round(s_avg * 1e3, 2), "split_us_median": round(s_ms[len(s_ms) // 2] * 1e3, 2),
+            "combine_us": round(c_avg * 1e3, 2),
+            "kv_gbs_split": round(gbs, 1), "pct_hbm_peak_split": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "kv_gbs_call": round(nb / ((s_avg + c_avg) * 1e-3) / 1e9, 1),
+        })
+    achieved = split_bytes / (split_ms * 1e-3) / 1e9
+    launches = len(cases) * args.kernel_reps
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_hash") == kernel_hash() and sorted(tr.get("contexts", [])) == sorted(contexts):
+                traffic = tr.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "split_kernel<128,3,1,0>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
+                "avg_launch_us": round(split_ms / launches * 1e3, 2), "launches": launches}
+
+    # ---------------- CPU baseline (oracle) + full-size parity ----------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import attn as oattn
+        from oracle.masks import Problem
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                          or [1])
+        except Exception:
+            threads = 1
+        t_cpu = 0.0
+        max_err, max_lse = 0.0, 0.0
+        ok = True
+        for c, (o_gpu, l_gpu) in zip(cases, gpu_out0):
+            k, v = c["kvs"][0]
+            kc = k[:, :c["hi"]].double().cpu().numpy()
+            vc = v[:, :c["hi"]].double().cpu().numpy()
+            qc = c["q"].double().cpu().numpy()
+            sc = c["sink"].double().cpu().numpy()
+            p = Problem("causal", ROWS, c["live"], first_pos=c["ctx"])
+            t = time.perf_counter()
+            ro, rl = oattn.verify_attn_ref(p, qc, oattn.Cache(kc, vc), 1 / math.sqrt(D), sc)
+            t_cpu += time.perf_counter() - t
+            L = c["live"]
+            err = np.abs(o_gpu[:L] - ro[:L])
+            ok &= bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ro[:L])))
+            ok &= bool(np.all(o_gpu[L:] == 0))
+            dl = np.abs(l_gpu[:L] - rl[:L])
+            ok &= bool(np.all(dl <= 1e-4))
+            max_err = max(max_err, float(err.max()))
+            max_lse = max(max_lse, float(dl.max()))
+        cpu = {"value": round(bytes_per_step / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"one pass over the {len(cases)} contexts (replica 0), float64 numpy, {t_cpu:.1f} s"}
+        parity = {"max_abs_err": max_err, "max_lse_err": max_lse, "pass": ok,
+                  "gate": "|err| <= 2e-3 + 1e-2|ref|, |dlse| <= 1e-4, padding rows 0"}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full-attention verify sweep: Hkv 1, Hq 6, D 128, 8 rows (4-8 live), "
+                               "causal, sink on, capacity 262144, ctx 1K-192K, cold KV",
+                   "contexts": contexts, "replicas": args.replicas, "splits": "plan" if not args.splits else args.splits},
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "sweep": sweep,
+        "wall_s_timed": round(t_wall, 4), "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

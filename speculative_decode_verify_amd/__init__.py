@@ -1,0 +1,11 @@
+"""MI355X (gfx950) multi-row speculative-verification decode attention.
+
+The compute runs in the HIP library lib/libverify_attn.so; this package only
+marshals arguments to its C ABI (include/verify_attn.h).  Loading happens on
+first use and raises if the library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    VAError, Plan, verify_attn_plan, verify_attn_plan_query, verify_attn_plan_split_range,
+    verify_attn_split, verify_attn_combine, swa_ring_write, verify_attn, workspace_for,
+    library_path, load_library, MASKS, KV_FORMATS,
+)

@@ -1,0 +1,266 @@
+"""ctypes binding of the C ABI in include/verify_attn.h: argument marshalling only.
+
+Tensors are torch tensors on the GPU; their device pointers, strides and the
+current HIP stream are handed to the library, which launches every kernel.
+There is no fallback: a missing library raises.
+"""
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libverify_attn.so")
+
+VA_MAX_ROWS = 16
+
+STATUS = {0: "VA_OK", 1: "VA_ERR_INVALID", 2: "VA_ERR_UNSUPPORTED", 3: "VA_ERR_CAPACITY",
+          4: "VA_ERR_WORKSPACE", 5: "VA_ERR_HIP"}
+MASKS = {"causal": 0, "window": 1, "tree": 2}
+KV_FORMATS = {"bf16": 0, "e4m3_wht_i8": 1}
+
+
+class VAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({_lib().va_status_string(status).decode()})")
+
+
+class va_problem(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("live_rows", ctypes.c_int32),
+        ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("mask", ctypes.c_int32), ("kv_fmt", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("ring_slots", ctypes.c_int32),
+        ("splits", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+        ("parent", ctypes.c_int32 * VA_MAX_ROWS),
+        ("first_pos", ctypes.c_int64), ("prefix_len", ctypes.c_int64),
+        ("kv_capacity", ctypes.c_int64), ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+class va_plan(ctypes.Structure):
+    _fields_ = [("words", ctypes.c_uint64 * 256)]
+
+
+class va_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("splits", ctypes.c_int32), ("matrix_rows", ctypes.c_int32),
+        ("lo", ctypes.c_int64), ("hi", ctypes.c_int64),
+        ("tile_lo", ctypes.c_int64), ("tiles", ctypes.c_int64),
+        ("row_lo", ctypes.c_int64 * VA_MAX_ROWS), ("row_hi", ctypes.c_int64 * VA_MAX_ROWS),
+        ("anc", ctypes.c_uint32 * VA_MAX_ROWS), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_LIB = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libverify_attn.so (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m speculative_decode_verify_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, V, I32, I64, SZ = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.verify_attn_plan.argtypes = [ctypes.POINTER(va_problem), ctypes.POINTER(va_plan), ctypes.POINTER(SZ)]
+    lib.verify_attn_plan_query.argtypes = [ctypes.POINTER(va_plan), ctypes.POINTER(va_plan_info)]
+    lib.verify_attn_plan_split_range.argtypes = [ctypes.POINTER(va_plan), I32, ctypes.POINTER(I64),
+                                                 ctypes.POINTER(I64)]
+    lib.verify_attn_split.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, I64, I64, I64, V, SZ, V]
+    lib.verify_attn_combine.argtypes = [ctypes.POINTER(va_plan), V, SZ, V, V, V, V]
+    lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
+    lib.va_status_string.argtypes = [ctypes.c_int]
+    lib.va_status_string.restype = ctypes.c_char_p
+    for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
+               "verify_attn_split", "verify_attn_combine", "swa_ring_write"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+_lib = load_library
+
+
+def _check(fn, status):
+    if status != 0:
+        raise VAError(fn, status)
+
+
+def _default_cus():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return int(torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count)
+    except Exception:
+        pass
+    return 256
+
+
+class Plan:
+    """A validated plan (host memory).  Keyword arguments mirror va_problem."""
+
+    def __init__(self, rows, live_rows, q_heads, kv_heads, head_dim, mask="causal", kv_fmt="bf16",
+                 first_pos=0, prefix_len=0, parent=None, window=0, ring_slots=0, kv_capacity=0,
+                 scale=None, splits=0, num_cus=None):
+        p = va_problem()
+        p.rows, p.live_rows, p.q_heads, p.kv_heads, p.head_dim = rows, live_rows, q_heads, kv_heads, head_dim
+        p.mask = MASKS[mask] if isinstance(mask, str) else int(mask)
+        p.kv_fmt = KV_FORMATS[kv_fmt] if isinstance(kv_fmt, str) else int(kv_fmt)
+        p.window, p.ring_slots, p.splits = window, ring_slots, splits
+        p.num_cus = _default_cus() if num_cus is None else num_cus
+        par = list(parent) if parent is not None else []
+        if len(par) > VA_MAX_ROWS:
+            raise ValueError("at most 16 tree nodes")
+        for i in range(VA_MAX_ROWS):
+            p.parent[i] = par[i] if i < len(par) else -1
+        p.first_pos, p.prefix_len, p.kv_capacity = first_pos, prefix_len, kv_capacity
+        p.scale = (1.0 / math.sqrt(head_dim)) if scale is None else scale
+        p.reserved = 0
+        self.problem = p
+        self.plan = va_plan()
+        ws = ctypes.c_size_t(0)
+        _check("verify_attn_plan", _lib().verify_attn_plan(ctypes.byref(p), ctypes.byref(self.plan), ctypes.byref(ws)))
+        self.workspace_bytes = ws.value
+        self.info = verify_attn_plan_query(self)
+        self.rows, self.live_rows, self.q_heads, self.kv_heads, self.head_dim = rows, live_rows, q_heads, kv_heads, head_dim
+        self.kv_fmt = p.kv_fmt
+
+    @property
+    def splits(self):
+        return self.info["splits"]
+
+
+def verify_attn_plan(**kw):
+    return Plan(**kw)
+
+
+def verify_attn_plan_query(plan):
+    info = va_plan_info()
+    _check("verify_attn_plan_query", _lib().verify_attn_plan_query(ctypes.byref(plan.plan), ctypes.byref(info)))
+    return {
+        "splits": info.splits, "matrix_rows": info.matrix_rows, "lo": info.lo, "hi": info.hi,
+        "tile_lo": info.tile_lo, "tiles": info.tiles, "row_lo": list(info.row_lo), "row_hi": list(info.row_hi),
+        "anc": list(info.anc), "workspace_bytes": info.workspace_bytes,
+    }
+
+
+def verify_attn_plan_split_range(plan, s):
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("verify_attn_plan_split_range",
+           _lib().verify_attn_plan_split_range(ctypes.byref(plan.plan), s, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtypes, device=True):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def workspace_for(plan, device=None):
+    import torch
+    n = (plan.workspace_bytes + 3) // 4
+    return torch.empty(max(n, 1), dtype=torch.float32, device=device or "cuda")
+
+
+def verify_attn_split(plan, q, k, v, workspace, v_scale=None, stream=None):
+    """q [rows, Hq, D] bf16 contiguous; k, v [Hkv, slots, D] (bf16, or uint8/int8
+    for the quantised format) with the last dimension contiguous; v_scale
+    [Hkv, slots] float32 for the quantised format."""
+    import torch
+    _require(q, "q", (torch.bfloat16,))
+    if not q.is_contiguous() or tuple(q.shape) != (plan.rows, plan.q_heads, plan.head_dim):
+        raise ValueError(f"q must be contiguous [{plan.rows}, {plan.q_heads}, {plan.head_dim}]")
+    if plan.kv_fmt == 0:
+        _require(k, "k", (torch.bfloat16,))
+        _require(v, "v", (torch.bfloat16,))
+    else:
+        _require(k, "k", (torch.uint8,))
+        _require(v, "v", (torch.int8,))
+        _require(v_scale, "v_scale", (torch.float32,))
+        if v_scale.stride(1) != 1:
+            raise ValueError("v_scale rows must be contiguous")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share shape and strides")
+    if k.dim() != 3 or k.shape[0] != plan.kv_heads or k.shape[2] != plan.head_dim or k.stride(2) != 1:
+        raise ValueError(f"k/v must be [{plan.kv_heads}, slots, {plan.head_dim}] with contiguous rows")
+    _require(workspace, "workspace", (torch.float32,))
+    ws_bytes = workspace.numel() * 4
+    _check("verify_attn_split", _lib().verify_attn_split(
+        ctypes.byref(plan.plan), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale),
+        v_scale.stride(0) if v_scale is not None else 0, k.stride(0), k.stride(1),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def verify_attn_combine(plan, workspace, out, lse=None, sink=None, stream=None):
+    """out [rows, Hq, D] float32 contiguous; lse [rows, Hq] float32 or None;
+    sink [Hq] float32 or None."""
+    import torch
+    _require(workspace, "workspace", (torch.float32,))
+    _require(out, "out", (torch.float32,))
+    if not out.is_contiguous() or tuple(out.shape) != (plan.rows, plan.q_heads, plan.head_dim):
+        raise ValueError("out must be contiguous [rows, Hq, D] float32")
+    if lse is not None:
+        _require(lse, "lse", (torch.float32,))
+        if not lse.is_contiguous() or tuple(lse.shape) != (plan.rows, plan.q_heads):
+            raise ValueError("lse must be contiguous [rows, Hq] float32")
+    if sink is not None:
+        _require(sink, "sink", (torch.float32,))
+        if not sink.is_contiguous() or sink.numel() != plan.q_heads:
+            raise ValueError("sink must be contiguous [Hq] float32")
+    _check("verify_attn_combine", _lib().verify_attn_combine(
+        ctypes.byref(plan.plan), _ptr(workspace), workspace.numel() * 4, _ptr(sink), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
+def swa_ring_write(k_new, v_new, first_pos, k_ring, v_ring, stream=None):
+    """k_new, v_new [rows, Hkv, D] bf16 contiguous; k_ring, v_ring [Hkv, C, D] bf16."""
+    import torch
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_ring, "k_ring"), (v_ring, "v_ring")):
+        _require(t, n, (torch.bfloat16,))
+    if not (k_new.is_contiguous() and v_new.is_contiguous()) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be contiguous [rows, Hkv, D]")
+    if k_ring.shape != v_ring.shape or k_ring.stride() != v_ring.stride() or k_ring.stride(2) != 1:
+        raise ValueError("k_ring/v_ring must share shape and strides, rows contiguous")
+    rows, hkv, d = k_new.shape
+    if k_ring.shape[0] != hkv or k_ring.shape[2] != d:
+        raise ValueError("ring shape does not match the new rows")
+    _check("swa_ring_write", _lib().swa_ring_write(
+        _ptr(k_new), _ptr(v_new), rows, first_pos, hkv, d, _ptr(k_ring), _ptr(v_ring), k_ring.shape[1],
+        k_ring.stride(0), k_ring.stride(1), _stream(stream)))
+
+
+def verify_attn(plan, q, k, v, sink=None, v_scale=None, workspace=None, out=None, lse=None, stream=None):
+    """Split then combine on one stream; allocates what is not passed in."""
+    import torch
+    dev = q.device
+    if workspace is None:
+        workspace = workspace_for(plan, dev)
+    if out is None:
+        out = torch.empty((plan.rows, plan.q_heads, plan.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((plan.rows, plan.q_heads), dtype=torch.float32, device=dev)
+    verify_attn_split(plan, q, k, v, workspace, v_scale=v_scale, stream=stream)
+    verify_attn_combine(plan, workspace, out, lse=lse, sink=sink, stream=stream)
+    return out, lse

@@ -1,0 +1,896 @@
+// Multi-row speculative-verification decode attention for gfx950 (CDNA4).
+//
+// Kernels:
+//   split_kernel    one workgroup per (split, KV head); four wave64s stream the
+//                   split's 32-key chunks, each wave keeping its own online
+//                   softmax state; QK^T and PV run on MFMA 16x16x32 bf16 with
+//                   FP32 accumulation; the waves merge through LDS and write
+//                   one partial (m, l, O) per matrix row.
+//   combine_kernel  one workgroup per (row, query head, 64-wide slice of D):
+//                   LSE merge of the partials plus the sink, with the partial
+//                   loads issued together into four independent FP32 chains.
+//   ring_write_kernel  copies the verification rows' K/V into the window ring.
+//
+// The method is the one on the IQuestRT report's section "Read only the KV
+// tiles needed by the current positions" (eight rows x six heads packed as
+// 48 matrix rows against one KV head, sequence splits, causal mask only at
+// the boundary, zero-value sink, separate combine with four FP32 chains,
+// 4,096 + 64-slot ring written before the read) and on "Qwen3.8-27B on one
+// RTX 4090" (tree mask; FP8 keys after a Hadamard rotation and INT8 values).
+// The data movement below is designed for CDNA4, not taken from the pages.
+//
+// MFMA layout used throughout (v_mfma_f32_16x16x32_bf16, wave64, lane l,
+// i = l % 16, g = l / 16):
+//   A operand: row i, contraction elements 8g..8g+7
+//   B operand: column i, contraction elements 8g..8g+7
+//   C/D:       column i, rows 4g..4g+3
+// Scores are computed transposed, S^T = K * Q^T (rows = keys, columns = query
+// matrix rows), so the C layout of S^T is directly the B operand of
+// O^T = V^T * P^T once each lane's keys are read in the order
+// {4g..4g+3, 16+4g..16+4g+3}; the same key order is used for V^T.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "plan_data.h"
+#include "verify_attn.h"
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+
+#define LOG2E_F 1.4426950408889634f
+#define LN2_F 0.6931471805599453f
+
+namespace va_detail {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 32;  // keys per wave step
+constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
+
+struct SplitArgs {
+  const uint8_t *q;  // bf16 [rows, Hq, D]
+  const uint8_t *k;
+  const uint8_t *v;
+  const float *v_scale;
+  float *ws_ml;
+  float *ws_o;
+  int64_t kv_head_stride_b;  // bytes
+  int64_t kv_row_stride_b;   // bytes
+  int64_t v_scale_head_stride;
+  int64_t base;  // absolute position of relative key 0 (= tile_lo * 64)
+  int32_t rows, live_rows, group, mrows, q_heads, kv_heads;
+  int32_t splits, tiles;
+  int32_t rel_lo, rel_hi;    // read extent, relative to base
+  int32_t full_lo, full_hi;  // every live row sees these keys (relative)
+  int32_t ring_slots, ring_base_slot;
+  int32_t tree, tree_lo;     // tree mode: relative position of node 0's key
+  float scale_log2;          // scale * log2(e)
+  int32_t row_lo[VA_MAX_ROWS], row_hi[VA_MAX_ROWS];  // relative, padding rows empty
+  uint32_t anc[VA_MAX_ROWS];
+};
+
+struct CombineArgs {
+  const float *ws_ml;
+  const float *ws_o;
+  const float *sink;
+  float *out;
+  float *lse;
+  int32_t rows, live_rows, group, mrows, q_heads, kv_heads, splits, head_dim;
+};
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max16x4(float x) {
+  // max over the four lanes that share lane % 16
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum16x4(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// E4M3FN pair -> two floats (exact), via the gfx950 OCP converter.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
+  typedef float f32x2 __attribute__((__vector_size__(8)));
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  out[0] = a[0];
+  out[1] = a[1];
+  out[2] = b[0];
+  out[3] = b[1];
+}
+
+// LDS DMA: lane l copies `bytes` from its global address to lds + bytes*l
+// (the LDS base is wave-uniform).  Kept out of the kernel templates: the
+// builtin exists only for the device.
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
+
+// Byte offset of relative key j (clamped into the extent by the caller).
+__device__ __forceinline__ int64_t key_offset(const SplitArgs &a, int32_t jrel) {
+  int64_t slot;
+  if (a.ring_slots) {
+    slot = (int64_t)(((uint32_t)a.ring_base_slot + (uint32_t)jrel) % (uint32_t)a.ring_slots);
+  } else {
+    slot = a.base + jrel;
+  }
+  return slot * a.kv_row_stride_b;
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel.
+//   D     head dim (64 or 128)
+//   NBW   16-row blocks of query matrix rows per wave (1..3)
+//   RG    row groups per workgroup (1: all four waves hold every row and
+//         stream different chunks; 2: wave pairs share a chunk, each wave
+//         holding half of the rows)
+//   FMT   0 = bf16 K/V; 1 = E4M3FN rotated K, INT8 V with per-key scale
+// ---------------------------------------------------------------------------
+template <int D, int NBW, int RG, int FMT>
+__global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
+  constexpr int KS = D / 32;       // QK contraction steps
+  constexpr int MD = D / 16;       // O^T row blocks over d
+  constexpr int STREAMS = kWaves / RG;
+  constexpr int ROWS_W = NBW * 16;
+  // Per-wave staging of one 32-key chunk, filled by LDS DMA: the K tile and
+  // the V tile, each 32 rows of KROW bytes made of 16-byte pieces, plus (INT8
+  // values) the chunk's scales.  Two such buffers per wave: the next chunk
+  // streams in while the current one is computed.
+  constexpr int KROW = FMT == 0 ? D * 2 : D;    // bytes per key row
+  constexpr int PIECES = KROW / 16;             // 16-byte pieces per row
+  constexpr int RPI = 64 / PIECES;              // rows per DMA instruction (1 KiB)
+  constexpr int NDMA = kChunk / RPI;            // DMA instructions per tile
+  constexpr int kTileB = kChunk * KROW;
+  constexpr int kScaleB = FMT == 1 ? 256 : 0;
+  constexpr int kBufB = 2 * kTileB + kScaleB;
+  constexpr int kStageBytes = kWaves * 2 * kBufB;
+
+  // LDS layout: [Q tile | staging] during the loop; the FP32 WHT scratch
+  // (quantised keys) overlays the staging area before the loop, and the
+  // cross-wave merge overlays both after it.
+  constexpr int QROWS = 16 * NBW * RG;               // padded query matrix rows
+  constexpr int kQT = QROWS * D * 2;                 // bf16 Q tile
+  constexpr int kWHT = FMT == 1 ? VA_MAX_MATRIX_ROWS * 128 * 4 : 0;
+  constexpr int kMergeBytes = 2 * ROWS_W * D * 4;    // two O^T tiles
+  constexpr int kLoop = kQT + (kStageBytes > kWHT ? kStageBytes : kWHT);
+  constexpr int kBig = kLoop > kMergeBytes ? kLoop : kMergeBytes;
+  constexpr int kML = kWaves * ROWS_W * 2 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kBig + kML];
+  uint16_t *qt = (uint16_t *)smem;  // [QROWS][D], 16-byte pieces XOR-swizzled by (row & 15)
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform: keeps chunk indices and mask decisions in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int rg = wave % RG;
+  const int stream = wave / RG;
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+
+  // ---------------- Q tile in LDS (B operand of S^T = K Q^T) ----------------
+  // Piece p (8 contraction elements) of matrix row m is stored at position
+  // p ^ (m % QP), so the lanes reading one operand spread over the banks.
+  constexpr int QP = D / 8;  // pieces per row
+  if constexpr (FMT == 0) {
+    for (int idx = threadIdx.x; idx < QROWS * QP; idx += kThreads) {
+      const int m = idx / QP, pc = idx % QP;
+      const int r = m / a.group;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (m < a.mrows && r < a.live_rows) {
+        const int h = kvh * a.group + (m - r * a.group);
+        w = *(const u32x4 *)(a.q + ((int64_t)(r * a.q_heads + h) * D + 8 * pc) * 2);
+      }
+      *(u32x4 *)(qt + m * D + 8 * (pc ^ (m & (QP - 1)))) = w;
+    }
+    __syncthreads();
+  } else {
+    // q' = H q / sqrt(128) in FP32 (natural-order Walsh-Hadamard), then bf16.
+    float *qs = (float *)(smem + kQT);
+    const int nrows = a.mrows;
+    for (int idx = threadIdx.x; idx < nrows * 128; idx += kThreads) {
+      const int m = idx >> 7, d = idx & 127;
+      const int r = m / a.group;
+      const int h = kvh * a.group + (m - r * a.group);
+      float x = 0.f;
+      if (r < a.live_rows) {
+        const uint16_t u = *(const uint16_t *)(a.q + ((int64_t)(r * a.q_heads + h) * 128 + d) * 2);
+        x = __uint_as_float((uint32_t)u << 16);
+      }
+      qs[idx] = x;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int hstep = 1; hstep < 128; hstep <<= 1) {
+      for (int idx = threadIdx.x; idx < nrows * 64; idx += kThreads) {
+        const int m = idx >> 6, kk = idx & 63;
+        const int i0 = (kk / hstep) * 2 * hstep + (kk % hstep);
+        float *row = qs + m * 128;
+        const float x0 = row[i0], x1 = row[i0 + hstep];
+        row[i0] = x0 + x1;
+        row[i0 + hstep] = x0 - x1;
+      }
+      __syncthreads();
+    }
+    const float inv = 0.08838834764831845f;  // 1/sqrt(128)
+    // Quantised keys use the contraction order: contraction piece p (8
+    // elements) holds d = 64*(p/8) + 16*(p%4) + 8*((p/4)%2) + e, so that one
+    // 16-byte load of E4M3 codes (d0..d0+15) serves two contraction steps.
+    for (int idx = threadIdx.x; idx < QROWS * QP; idx += kThreads) {
+      const int m = idx / QP, pc = idx % QP;
+      const int d0 = 64 * (pc >> 3) + 16 * (pc & 3) + 8 * ((pc >> 2) & 1);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x0 = 0.f, x1 = 0.f;
+        if (m < nrows) {
+          x0 = qs[m * 128 + d0 + 2 * e] * inv;
+          x1 = qs[m * 128 + d0 + 2 * e + 1] * inv;
+        }
+        w[e] = pack_bf16x2(x0, x1);
+      }
+      u32x4 wv = {w[0], w[1], w[2], w[3]};
+      *(u32x4 *)(qt + m * D + 8 * (pc ^ (m & (QP - 1)))) = wv;
+    }
+    __syncthreads();
+  }
+  // B operand for 16-row block nb of this wave, contraction step ks: lane
+  // (i16, g4) holds row 16*(rg*NBW+nb)+i16, contraction piece 4*ks+g4.
+  auto qop = [&](int nb, int ks) -> bf16x8 {
+    const int m = 16 * (rg * NBW + nb) + i16;
+    return __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + m * D + 8 * ((4 * ks + g4) ^ (m & (QP - 1)))));
+  };
+
+  // ---------------- per-lane row geometry for boundary masks ----------------
+  int32_t rlo[NBW], rhi[NBW];
+  uint32_t ranc[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int m = 16 * (rg * NBW + nb) + i16;
+    const int r = m / a.group;
+    const bool ok = (m < a.mrows) && (r < a.live_rows);
+    const int rr = ok ? r : 0;  // padded matrix rows never index past the row tables
+    rlo[nb] = ok ? a.row_lo[rr] : 0;
+    rhi[nb] = ok ? a.row_hi[rr] : 0;
+    ranc[nb] = ok ? a.anc[rr] : 0u;
+  }
+
+  // ---------------- online-softmax state ----------------
+  f32x4 o[MD][NBW];
+  float mref[NBW], mtrue[NBW], lrow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    mref[nb] = -INFINITY;
+    mtrue[nb] = -INFINITY;
+    lrow[nb] = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---------------- this split's chunk range ----------------
+  const int64_t T = a.tiles, S = a.splits;
+  const int32_t t0 = (int32_t)(((int64_t)split * T) / S);
+  const int32_t t1 = (int32_t)(((int64_t)(split + 1) * T) / S);
+  int32_t c_first = 2 * t0, c_last = 2 * t1;  // in 32-key chunks, relative
+  if (c_first < a.rel_lo / kChunk) c_first = a.rel_lo / kChunk;
+  const int32_t c_end_ext = (a.rel_hi + kChunk - 1) / kChunk;
+  if (c_last > c_end_ext) c_last = c_end_ext;
+  const int32_t nchunks = c_last > c_first ? c_last - c_first : 0;
+  // chunks handled by this wave: c_first + stream + STREAMS * n
+  const int32_t my_n = nchunks > stream ? (nchunks - stream + STREAMS - 1) / STREAMS : 0;
+
+  const uint8_t *kbase = a.k + (int64_t)kvh * a.kv_head_stride_b;
+  const uint8_t *vbase = a.v + (int64_t)kvh * a.kv_head_stride_b;
+  uint8_t *stage = smem + kQT + wave * 2 * kBufB;
+
+  // A chunk never straddles the ring's wrap (slots are 64-aligned), so every
+  // key of chunk c0 lives at row_of(c0) + (j - c0): one scalar base per chunk
+  // plus a 32-bit lane offset.  Keys outside [rel_lo, rel_hi) are clamped to
+  // the extent's ends (read, then masked), so nothing outside it is read.
+  auto chunk_row = [&](int32_t c0) -> int64_t {
+    return a.ring_slots ? (int64_t)(((uint32_t)a.ring_base_slot + (uint32_t)c0) % (uint32_t)a.ring_slots)
+                        : a.base + c0;
+  };
+  auto clampx = [&](int32_t x, int32_t c0) -> int32_t {
+    const int32_t lo = a.rel_lo - c0, hi = a.rel_hi - 1 - c0;
+    return x < lo ? lo : (x > hi ? hi : x);
+  };
+  const uint32_t rs = (uint32_t)a.kv_row_stride_b;
+
+  // Piece swizzle inside a staged K tile (position = piece ^ (row % PIECES)):
+  // the 16 lanes reading one A operand (16 keys, same piece) hit 16
+  // different positions.  The V tile is unswizzled so that every V^T gather
+  // address is one lane base plus an immediate.
+  auto fk = [](int row) { return row & (PIECES - 1); };
+  auto fv = [](int row) { return 0 * row; };
+
+  // Issue the LDS DMA of chunk n into buffer `buf` (lane l of instruction t
+  // stores 16 bytes at tile + 1024*t + 16*l).
+  auto issue = [&](int32_t n, int buf) {
+    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
+    const int64_t crow = chunk_row(c0);
+    const uint8_t *kc = kbase + crow * a.kv_row_stride_b;
+    const uint8_t *vc = vbase + crow * a.kv_row_stride_b;
+    uint8_t *kt = stage + buf * kBufB;
+    uint8_t *vt = kt + kTileB;
+#pragma unroll
+    for (int t = 0; t < NDMA; ++t) {
+      const int row = t * RPI + lane / PIECES;
+      const int pos = lane % PIECES;
+      const uint32_t roff = (uint32_t)clampx(row, c0) * rs;
+      dma16(kc + roff + 16 * (pos ^ fk(row)), kt + 1024 * t);
+      dma16(vc + roff + 16 * (pos ^ fv(row)), vt + 1024 * t);
+    }
+    if constexpr (FMT == 1) {
+      const float *sc = a.v_scale + (int64_t)kvh * a.v_scale_head_stride + crow;
+      dma4(sc + clampx(lane & 31, c0), vt + kTileB);
+    }
+  };
+
+  // vector-memory instructions per issued chunk (all of them LDS DMA)
+  constexpr int kVmPerChunk = 2 * NDMA + (FMT == 1 ? 1 : 0);
+
+  auto step = [&](int32_t n) {
+    const int buf = n & 1;
+    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
+    const uint8_t *kt = stage + buf * kBufB;
+    const uint8_t *vt = kt + kTileB;
+
+    // Chunk n's DMA must have landed.  Vector-memory operations complete in
+    // issue order and only this wave's DMA is in flight, so leaving chunk
+    // n+1's instructions outstanding is exact.  (The compiler does not track
+    // LDS written by DMA across loop iterations, hence the explicit waits;
+    // the memory clobber keeps the LDS reads below them.)
+    if (n + 1 < my_n) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmPerChunk) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // ---- read every operand of this chunk from LDS ----
+    bf16x8 kop[2][KS];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = 16 * mb + i16;
+      if constexpr (FMT == 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kop[mb][ks] = *(const bf16x8 *)(kt + row * KROW + 16 * ((4 * ks + g4) ^ fk(row)));
+      } else {
+#pragma unroll
+        for (int kp2 = 0; kp2 < KS / 2; ++kp2) {
+          // 16 E4M3 codes: first 8 -> step 2*kp2, last 8 -> step 2*kp2+1
+          const u32x4 w = *(const u32x4 *)(kt + row * KROW + 16 * ((4 * kp2 + g4) ^ fk(row)));
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            float f[8];
+            e4m3x4_to_f32(w[2 * half], f);
+            e4m3x4_to_f32(w[2 * half + 1], f + 4);
+            u32x4 o4 = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                        pack_bf16x2(f[6], f[7])};
+            kop[mb][2 * kp2 + half] = __builtin_bit_cast(bf16x8, o4);
+          }
+        }
+      }
+    }
+    // V^T operand for block md: lane (i16 = d within the block, g4) takes the
+    // keys {4g..4g+3, 16+4g..16+4g+3} of column d.
+    bf16x8 vop[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int d = 16 * md + i16;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4);
+        if constexpr (FMT == 0) {
+          const int pos = (d >> 3) ^ fv(row);
+          vop[md][t] = *(const __bf16 *)(vt + row * KROW + 16 * pos + 2 * (d & 7));
+        } else {
+          const int pos = (d >> 4) ^ fv(row);
+          const int8_t c = *(const int8_t *)(vt + row * KROW + 16 * pos + (d & 15));
+          vop[md][t] = (__bf16)(float)c;  // exact
+        }
+      }
+    }
+    float vs[8];
+    if constexpr (FMT == 1) {
+      const float *sct = (const float *)(vt + kTileB);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) vs[t] = sct[t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4)];
+    }
+
+    // ---- refill this buffer with chunk n+2 once its reads are done ----
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (n + 2 < my_n) issue(n + 2, buf);
+
+    // ---- S^T = K Q^T ----
+    f32x4 s[2][NBW];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16(kop[mb][ks], qop(nb, ks), acc);
+        s[mb][nb] = acc;
+      }
+
+    // ---- scale, boundary mask, row maxima ----
+    const bool full = (c0 >= a.full_lo) && (c0 + kChunk <= a.full_hi);
+    float xs[NBW][8], xmax[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      float *x = xs[nb];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * mb + e] = s[mb][nb][e] * a.scale_log2;
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          // branch-free: row interval, or (tree) an ancestor-or-self node key
+          const int32_t j = c0 + (t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4));
+          const uint32_t in_row = (uint32_t)(j - rlo[nb]) < (uint32_t)(rhi[nb] - rlo[nb]);
+          const uint32_t ti = (uint32_t)(j - a.tree_lo);
+          const uint32_t in_tree = (uint32_t)(ti < 16u) & (ranc[nb] >> (ti & 15u));
+          x[t] = ((in_row | in_tree) & 1u) ? x[t] : -INFINITY;
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
+      xmax[nb] = wave_max16x4(mx);
+    }
+
+    // ---- lazy reference maximum ----
+    // Exponents are taken against mref, which moves only when a row's chunk
+    // maximum exceeds it by more than kTau (so every p stays <= 2^kTau);
+    // moving it rescales that row's O and l.
+    bool need = false;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      mtrue[nb] = fmaxf(mtrue[nb], xmax[nb]);
+      need |= (mref[nb] != -INFINITY) && (xmax[nb] > mref[nb] + kTau);
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const bool mv = (xmax[nb] > mref[nb] + kTau) || (mref[nb] == -INFINITY);
+        const float nref = mv ? xmax[nb] : mref[nb];
+        const float alpha = (mref[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref[nb] - nref);
+        lrow[nb] *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[md][nb] *= alpha;
+        mref[nb] = nref;
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) mref[nb] = (mref[nb] == -INFINITY) ? xmax[nb] : mref[nb];
+    }
+
+    // ---- P^T (B operand of PV) and l ----
+    uint32_t pb[NBW][4];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const float m_use = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p[t] = __builtin_amdgcn_exp2f(xs[nb][t] - m_use);
+        psum += p[t];
+      }
+      lrow[nb] += psum;
+      if constexpr (FMT == 1) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) p[t] *= vs[t];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pb[nb][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+    }
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        u32x4 pw = {pb[nb][0], pb[nb][1], pb[nb][2], pb[nb][3]};
+        o[md][nb] = mfma16(vop[md], __builtin_bit_cast(bf16x8, pw), o[md][nb]);
+      }
+  };
+
+  if (my_n > 0) {
+    issue(0, 0);
+    if (my_n > 1) issue(1, 1);
+    for (int32_t n = 0; n < my_n; ++n) step(n);
+  }
+
+  // ---------------- normalise to the true maximum ----------------
+  float mrow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const float f = (mref[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref[nb] - mtrue[nb]);
+    lrow[nb] *= f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md][nb] *= f;
+    mrow[nb] = mtrue[nb];
+  }
+
+  // ---------------- merge the streams of each row group ----------------
+  __syncthreads();  // staging tiles are no longer read
+  float *sml = (float *)(smem + kBig);  // [wave][ROWS_W][2]
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const float lt = wave_sum16x4(lrow[nb]);
+    lrow[nb] = lt;
+    if (g4 == 0) {
+      sml[(wave * ROWS_W + nb * 16 + i16) * 2 + 0] = mrow[nb];
+      sml[(wave * ROWS_W + nb * 16 + i16) * 2 + 1] = lt;
+    }
+  }
+  __syncthreads();
+  float mfin[NBW], lfin[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < STREAMS; ++st) M = fmaxf(M, sml[((st * RG + rg) * ROWS_W + nb * 16 + i16) * 2]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int st = 0; st < STREAMS; ++st) {
+      const float mw = sml[((st * RG + rg) * ROWS_W + nb * 16 + i16) * 2];
+      const float lw = sml[((st * RG + rg) * ROWS_W + nb * 16 + i16) * 2 + 1];
+      L += lw * __builtin_amdgcn_exp2f(mw - Mu);
+    }
+    const float f = __builtin_amdgcn_exp2f(mrow[nb] - Mu);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md][nb] *= f;
+    mfin[nb] = M;
+    lfin[nb] = L;
+  }
+  // Tree add of the O^T tiles through LDS (C-layout order, 16 B per lane).
+  constexpr int kTile = ROWS_W * D;  // floats per wave tile
+  f32x4 *buf = (f32x4 *)smem;        // room for two tiles per row group
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) buf[(slot * kTile) / 4 + (md * NBW + nb) * 64 + lane] = o[md][nb];
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) o[md][nb] += buf[(slot * kTile) / 4 + (md * NBW + nb) * 64 + lane];
+  };
+  if constexpr (STREAMS == 4) {
+    if (stream >= 2) put(stream - 2);
+    __syncthreads();
+    if (stream < 2) add(stream);
+    __syncthreads();
+    if (stream == 1) put(0);
+    __syncthreads();
+    if (stream == 0) add(0);
+  } else {
+    if (stream == 1) put(rg);
+    __syncthreads();
+    if (stream == 0) add(rg);
+  }
+
+  // ---------------- write the partial ----------------
+  if (stream == 0) {
+    const int64_t unit0 = ((int64_t)split * a.kv_heads + kvh) * a.mrows;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int m = 16 * (rg * NBW + nb) + i16;
+      if (m < a.mrows) {
+        const int r = m / a.group;
+        const bool live = r < a.live_rows;
+        if (g4 == 0) {
+          a.ws_ml[(unit0 + m) * 2 + 0] = live ? mfin[nb] : -INFINITY;
+          a.ws_ml[(unit0 + m) * 2 + 1] = live ? lfin[nb] : 0.f;
+        }
+        float *op = a.ws_o + (unit0 + m) * D;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const f32x4 val = live ? o[md][nb] : (f32x4){0.f, 0.f, 0.f, 0.f};
+          *(f32x4 *)(op + 16 * md + 4 * g4) = val;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine kernel: grid (rows * Hq, D / 64), 256 threads.
+// ---------------------------------------------------------------------------
+constexpr int kMaxSplits = 4096;
+
+__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+  __shared__ float wts[kMaxSplits];
+  __shared__ float red[8];
+
+  const int rh = blockIdx.x;
+  const int r = rh / a.q_heads, h = rh % a.q_heads;
+  const int D = a.head_dim;
+  const int t = threadIdx.x;
+  const int dl = t & 63, grp = t >> 6;
+  const int d = 64 * blockIdx.y + dl;
+  float *outp = a.out + ((int64_t)r * a.q_heads + h) * D;
+
+  if (r >= a.live_rows) {
+    outp[d] = 0.f;
+    if (a.lse && blockIdx.y == 0 && t == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
+    return;
+  }
+  const int g = h / a.group;
+  const int mrow = r * a.group + (h - g * a.group);
+  const int S = a.splits;
+  const int64_t stride_unit = (int64_t)a.kv_heads * a.mrows;  // units between splits
+  const int64_t unit0 = (int64_t)g * a.mrows + mrow;
+  const float sink2 = a.sink ? a.sink[h] * LOG2E_F : -INFINITY;
+
+  // 1) max over splits (and the sink)
+  float mx = -INFINITY;
+  for (int s = t; s < S; s += 256) mx = fmaxf(mx, a.ws_ml[(unit0 + s * stride_unit) * 2]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  M = fmaxf(M, sink2);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  __syncthreads();
+
+  // 2) weights and denominator
+  float den = 0.f;
+  for (int s = t; s < S; s += 256) {
+    const float ms = a.ws_ml[(unit0 + s * stride_unit) * 2];
+    const float ls = a.ws_ml[(unit0 + s * stride_unit) * 2 + 1];
+    const float w = __builtin_amdgcn_exp2f(ms - Mu);
+    wts[s] = w;
+    den += w * ls;
+  }
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
+  if ((t & 63) == 0) red[4 + (t >> 6)] = den;
+  __syncthreads();
+  den = (red[4] + red[5]) + (red[6] + red[7]);
+  den += __builtin_amdgcn_exp2f(sink2 - Mu);
+
+  // 3) weighted sum of O: thread group grp takes splits s = grp (mod 4), four
+  //    independent chains over consecutive such splits, loads issued together.
+  const float *ob = a.ws_o + unit0 * D + d;
+  const int64_t sstride = stride_unit * D;
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int s = grp;
+  for (; s + 12 < S; s += 16) {
+    const float o0 = ob[(int64_t)s * sstride];
+    const float o1 = ob[(int64_t)(s + 4) * sstride];
+    const float o2 = ob[(int64_t)(s + 8) * sstride];
+    const float o3 = ob[(int64_t)(s + 12) * sstride];
+    acc0 = fmaf(wts[s], o0, acc0);
+    acc1 = fmaf(wts[s + 4], o1, acc1);
+    acc2 = fmaf(wts[s + 8], o2, acc2);
+    acc3 = fmaf(wts[s + 12], o3, acc3);
+  }
+  if (s < S) acc0 = fmaf(wts[s], ob[(int64_t)s * sstride], acc0);
+  if (s + 4 < S) acc1 = fmaf(wts[s + 4], ob[(int64_t)(s + 4) * sstride], acc1);
+  if (s + 8 < S) acc2 = fmaf(wts[s + 8], ob[(int64_t)(s + 8) * sstride], acc2);
+  const float acc = (acc0 + acc1) + (acc2 + acc3);
+
+  // 4) reduce the four groups
+  __shared__ float gsum[4][64];
+  gsum[grp][dl] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    const float tot = (gsum[0][dl] + gsum[1][dl]) + (gsum[2][dl] + gsum[3][dl]);
+    if (M == -INFINITY) {
+      outp[d] = 0.f;
+      if (a.lse && blockIdx.y == 0 && dl == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
+    } else {
+      outp[d] = tot / den;
+      if (a.lse && blockIdx.y == 0 && dl == 0)
+        a.lse[(int64_t)r * a.q_heads + h] = (Mu + __log2f(den)) * LN2_F;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ring write: one thread per 16-byte piece of K and of V.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ring_write_kernel(const uint8_t *k_new, const uint8_t *v_new, int rows,
+                                                         int kv_heads, int head_dim, uint8_t *k_ring,
+                                                         uint8_t *v_ring, int ring_slots, int slot0,
+                                                         int64_t head_stride_b, int64_t row_stride_b) {
+  const int pieces = head_dim / 8;
+  const int total = rows * kv_heads * pieces;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int pc = idx % pieces;
+  const int g = (idx / pieces) % kv_heads;
+  const int r = idx / (pieces * kv_heads);
+  const int slot = (int)(((uint32_t)slot0 + (uint32_t)r) % (uint32_t)ring_slots);
+  const int64_t src = ((int64_t)(r * kv_heads + g) * head_dim + pc * 8) * 2;
+  const int64_t dst = (int64_t)g * head_stride_b + (int64_t)slot * row_stride_b + pc * 16;
+  *(u32x4 *)(k_ring + dst) = *(const u32x4 *)(k_new + src);
+  *(u32x4 *)(v_ring + dst) = *(const u32x4 *)(v_new + src);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+const va_plan_data *plan_of(const va_plan *plan) {
+  if (!plan) return nullptr;
+  const va_plan_data *d = reinterpret_cast<const va_plan_data *>(plan);
+  return d->magic == VA_PLAN_MAGIC ? d : nullptr;
+}
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <int D, int NBW, int RG, int FMT>
+hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
+  dim3 grid(a.splits, a.kv_heads);
+  hipLaunchKernelGGL((split_kernel<D, NBW, RG, FMT>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int FMT>
+hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
+  switch (nb_total) {
+    case 1: return launch_split<D, 1, 1, FMT>(a, stream);
+    case 2: return launch_split<D, 2, 1, FMT>(a, stream);
+    case 3: return launch_split<D, 3, 1, FMT>(a, stream);
+    case 4: return launch_split<D, 2, 2, FMT>(a, stream);
+    case 5:
+    case 6: return launch_split<D, 3, 2, FMT>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace va_detail
+using namespace va_detail;
+
+extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const void *k, const void *v,
+                                       const float *v_scale, int64_t v_scale_head_stride,
+                                       int64_t kv_head_stride, int64_t kv_row_stride, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  const va_plan_data *d = plan_of(plan);
+  if (!d) return VA_ERR_INVALID;
+  if (!workspace || workspace_bytes < d->workspace_bytes) return VA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VA_ERR_INVALID;
+  if (d->splits > kMaxSplits) return VA_ERR_UNSUPPORTED;
+  const bool quant = d->kv_fmt == VA_KV_K_E4M3_WHT_V_I8;
+  const int64_t esz = quant ? 1 : 2;
+  if (d->hi > d->lo) {
+    if (!q || !k || !v) return VA_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return VA_ERR_INVALID;
+    if (kv_head_stride < 0 || kv_row_stride < d->head_dim) return VA_ERR_INVALID;
+    if (((kv_head_stride * esz) & 15) || ((kv_row_stride * esz) & 15)) return VA_ERR_INVALID;
+    // a lane's offset inside a 32-key chunk is a 32-bit row * stride product
+    if (kv_row_stride * esz > ((int64_t)1 << 26)) return VA_ERR_INVALID;
+    if (quant && (!v_scale || v_scale_head_stride < 0)) return VA_ERR_INVALID;
+  }
+  SplitArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = (const uint8_t *)q;
+  a.k = (const uint8_t *)k;
+  a.v = (const uint8_t *)v;
+  a.v_scale = v_scale;
+  a.ws_ml = (float *)workspace;
+  a.ws_o = (float *)((uint8_t *)workspace + d->ml_bytes);
+  a.kv_head_stride_b = kv_head_stride * esz;
+  a.kv_row_stride_b = kv_row_stride * esz;
+  a.v_scale_head_stride = v_scale_head_stride;
+  a.base = d->tile_lo * VA_TILE;
+  a.rows = d->rows;
+  a.live_rows = d->live_rows;
+  a.group = d->group;
+  a.mrows = d->matrix_rows;
+  a.q_heads = d->q_heads;
+  a.kv_heads = d->kv_heads;
+  a.splits = d->splits;
+  a.tiles = (int32_t)d->tiles;
+  a.rel_lo = (int32_t)(d->lo - a.base);
+  a.rel_hi = (int32_t)(d->hi - a.base);
+  a.full_lo = (int32_t)(d->full_lo - a.base);
+  a.full_hi = (int32_t)(d->full_hi - a.base);
+  if (a.full_lo < a.rel_lo) a.full_lo = a.rel_lo;
+  if (a.full_hi > a.rel_hi) a.full_hi = a.rel_hi;
+  if (a.full_hi < a.full_lo) a.full_hi = a.full_lo;
+  a.ring_slots = d->ring_slots;
+  a.ring_base_slot = d->ring_base_slot;
+  a.tree = d->mask == VA_MASK_TREE;
+  {
+    // tree keys relative to base; clamp far-away values into int32
+    int64_t tl = d->prefix_len - a.base;
+    a.tree_lo = (int32_t)(tl > (int64_t)1 << 30 ? (int64_t)1 << 30 : tl);
+  }
+  a.scale_log2 = d->scale * LOG2E_F;
+  for (int r = 0; r < VA_MAX_ROWS; ++r) {
+    int64_t lo = d->row_lo[r] - a.base, hi = d->row_hi[r] - a.base;
+    if (d->row_hi[r] <= d->row_lo[r]) lo = hi = 0;
+    if (lo < 0) lo = 0;
+    if (hi < lo) hi = lo;
+    a.row_lo[r] = (int32_t)lo;
+    a.row_hi[r] = (int32_t)hi;
+    a.anc[r] = d->anc[r];
+  }
+  const int nb_total = (d->matrix_rows + 15) / 16;
+  hipError_t e;
+  if (quant) {
+    e = dispatch_rows<128, 1>(a, nb_total, stream);
+  } else if (d->head_dim == 64) {
+    e = dispatch_rows<64, 0>(a, nb_total, stream);
+  } else {
+    e = dispatch_rows<128, 0>(a, nb_total, stream);
+  }
+  return e == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+extern "C" va_status verify_attn_combine(const va_plan *plan, const void *workspace, size_t workspace_bytes,
+                                         const float *sink, float *out, float *lse, hipStream_t stream) {
+  const va_plan_data *d = plan_of(plan);
+  if (!d || !out) return VA_ERR_INVALID;
+  if (!workspace || workspace_bytes < d->workspace_bytes) return VA_ERR_WORKSPACE;
+  if (d->splits > kMaxSplits) return VA_ERR_UNSUPPORTED;
+  CombineArgs a;
+  a.ws_ml = (const float *)workspace;
+  a.ws_o = (const float *)((const uint8_t *)workspace + d->ml_bytes);
+  a.sink = sink;
+  a.out = out;
+  a.lse = lse;
+  a.rows = d->rows;
+  a.live_rows = d->live_rows;
+  a.group = d->group;
+  a.mrows = d->matrix_rows;
+  a.q_heads = d->q_heads;
+  a.kv_heads = d->kv_heads;
+  a.splits = d->splits;
+  a.head_dim = d->head_dim;
+  dim3 grid(d->rows * d->q_heads, d->head_dim / 64);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+extern "C" va_status swa_ring_write(const void *k_new, const void *v_new, int32_t rows, int64_t first_pos,
+                                    int32_t kv_heads, int32_t head_dim, void *k_ring, void *v_ring,
+                                    int32_t ring_slots, int64_t kv_head_stride, int64_t kv_row_stride,
+                                    hipStream_t stream) {
+  if (rows < 0 || rows > VA_MAX_ROWS) return VA_ERR_INVALID;
+  if (rows == 0) return VA_OK;
+  if (first_pos < 0 || kv_heads < 1 || ring_slots < rows) return VA_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return VA_ERR_INVALID;
+  if (!k_new || !v_new || !k_ring || !v_ring) return VA_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_ring) || !aligned16(v_ring)) return VA_ERR_INVALID;
+  if (kv_head_stride < 0 || kv_row_stride < head_dim) return VA_ERR_INVALID;
+  if (((kv_head_stride * 2) & 15) || ((kv_row_stride * 2) & 15)) return VA_ERR_INVALID;
+  const int slot0 = (int)(first_pos % ring_slots);
+  const int total = rows * kv_heads * (head_dim / 8);
+  hipLaunchKernelGGL(ring_write_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
+                     (const uint8_t *)k_new, (const uint8_t *)v_new, rows, kv_heads, head_dim,
+                     (uint8_t *)k_ring, (uint8_t *)v_ring, ring_slots, slot0, kv_head_stride * 2,
+                     kv_row_stride * 2);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}

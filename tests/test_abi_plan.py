@@ -1,0 +1,196 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry
+point, rejects every malformed problem, and its host plan agrees bit-exactly
+with the oracle's visibility rules and split rule.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import speculative_decode_verify_amd as va
+from speculative_decode_verify_amd import _binding
+from oracle import masks
+from oracle.masks import Problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)) - {"sizeof"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = va.load_library()
+    names = declared_functions()
+    assert set(names) >= {"verify_attn_plan", "verify_attn_split", "verify_attn_combine", "swa_ring_write",
+                          "verify_attn_plan_query", "verify_attn_plan_split_range", "va_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    lib = va.load_library()
+    for s in range(6):
+        assert lib.va_status_string(s)
+    assert b"unknown" in lib.va_status_string(99)
+
+
+def test_struct_sizes_match_c_layout():
+    # va_problem: eleven int32, int32[16], (pad), three int64, float, int32
+    assert ctypes.sizeof(_binding.va_problem) == 144
+    assert ctypes.sizeof(_binding.va_plan) == 2048
+
+
+def _status(**kw):
+    try:
+        va.Plan(**kw)
+    except va.VAError as e:
+        return _binding.STATUS[e.status]
+    return "VA_OK"
+
+
+BASE = dict(rows=8, live_rows=5, q_heads=6, kv_heads=1, head_dim=64, first_pos=1019, kv_capacity=1032)
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(), "VA_OK"),
+    (dict(rows=0), "VA_ERR_INVALID"),
+    (dict(rows=17), "VA_ERR_INVALID"),
+    (dict(live_rows=9), "VA_ERR_INVALID"),
+    (dict(live_rows=-1), "VA_ERR_INVALID"),
+    (dict(q_heads=6, kv_heads=4), "VA_ERR_INVALID"),                     # 6 % 4 != 0
+    (dict(q_heads=7), "VA_OK"),                                           # G = 7, 56 matrix rows
+    (dict(kv_heads=0), "VA_ERR_INVALID"),
+    (dict(head_dim=96), "VA_ERR_UNSUPPORTED"),
+    (dict(q_heads=13, kv_heads=1, rows=8), "VA_ERR_UNSUPPORTED"),          # 8 * 13 > 96 rows
+    (dict(kv_fmt="e4m3_wht_i8"), "VA_ERR_UNSUPPORTED"),                  # quantised needs D = 128
+    (dict(scale=0.0), "VA_ERR_INVALID"),
+    (dict(scale=float("nan")), "VA_ERR_INVALID"),
+    (dict(scale=float("inf")), "VA_ERR_INVALID"),
+    (dict(first_pos=-1), "VA_ERR_INVALID"),
+    (dict(kv_capacity=1023), "VA_ERR_CAPACITY"),                          # live rows read up to 1023
+    (dict(kv_capacity=1024), "VA_OK"),
+    (dict(splits=-2), "VA_ERR_INVALID"),
+    (dict(mask=7), "VA_ERR_INVALID"),
+    (dict(ring_slots=4160), "VA_ERR_INVALID"),                            # ring only in window mode
+    (dict(mask="window", window=4096, ring_slots=4160), "VA_OK"),
+    (dict(mask="window", window=4096, ring_slots=4096), "VA_ERR_INVALID"),  # the rows' writes would evict
+    (dict(mask="window", window=4096, ring_slots=4100), "VA_ERR_INVALID"),  # not a multiple of 64
+    (dict(mask="window", window=0, ring_slots=4160), "VA_ERR_INVALID"),
+    (dict(mask="window", window=57, ring_slots=64), "VA_OK"),             # 57 + 8 - 1 = 64
+    (dict(mask="window", window=58, ring_slots=64), "VA_ERR_INVALID"),
+    (dict(mask="tree", prefix_len=100, parent=[-1, 0, 5], rows=3, live_rows=3), "VA_ERR_INVALID"),
+    (dict(mask="tree", prefix_len=100, parent=[-1, 0, -2], rows=3, live_rows=3), "VA_ERR_INVALID"),
+    (dict(mask="tree", prefix_len=100, parent=[0, 0, 1], rows=3, live_rows=3), "VA_ERR_INVALID"),
+    (dict(mask="tree", prefix_len=100, parent=[-1, 0, 1], rows=3, live_rows=3, kv_capacity=103), "VA_OK"),
+    (dict(mask="tree", prefix_len=100, parent=[-1, 0, 1], rows=3, live_rows=3, kv_capacity=102), "VA_ERR_CAPACITY"),
+    (dict(mask="tree", prefix_len=-1, parent=[-1], rows=1, live_rows=1), "VA_ERR_INVALID"),
+])
+def test_plan_validation(change, expect):
+    kw = dict(BASE)
+    kw.update(change)
+    assert _status(**kw) == expect
+
+
+def test_reserved_must_be_zero():
+    lib = va.load_library()
+    p = _binding.va_problem()
+    p.rows, p.live_rows, p.q_heads, p.kv_heads, p.head_dim, p.kv_capacity, p.scale = 8, 1, 6, 1, 64, 100, 1.0
+    plan = _binding.va_plan()
+    assert lib.verify_attn_plan(ctypes.byref(p), ctypes.byref(plan), None) == 0
+    p.reserved = 1
+    assert lib.verify_attn_plan(ctypes.byref(p), ctypes.byref(plan), None) == 1
+    assert lib.verify_attn_plan(None, ctypes.byref(plan), None) == 1
+
+
+def test_query_rejects_garbage_plan():
+    lib = va.load_library()
+    plan = _binding.va_plan()
+    info = _binding.va_plan_info()
+    assert lib.verify_attn_plan_query(ctypes.byref(plan), ctypes.byref(info)) == 1
+
+
+def _oracle_problem(kw):
+    return Problem(kw.get("mask", "causal"), kw["rows"], kw["live_rows"], first_pos=kw.get("first_pos", 0),
+                   prefix_len=kw.get("prefix_len", 0), parent=kw.get("parent"), window=kw.get("window", 0),
+                   ring_slots=kw.get("ring_slots", 0))
+
+
+def _cases():
+    rng = np.random.default_rng(7)
+    out = []
+    for P in (0, 1, 63, 64, 1019, 5000, 65536 + 17):
+        for live in (0, 1, 5, 8):
+            out.append(dict(rows=8, live_rows=live, q_heads=6, kv_heads=1, head_dim=128, first_pos=P,
+                            kv_capacity=P + 8))
+    for t0 in (0, 5, 4095, 5120, 51200, 194560):
+        for live in (1, 5, 8):
+            out.append(dict(rows=8, live_rows=live, q_heads=6, kv_heads=1, head_dim=64, mask="window",
+                            window=4096, ring_slots=4160, first_pos=t0))
+    for P in (0, 10, 2048, 8192, 32768):
+        for _ in range(3):
+            par = [-1] + [int(rng.integers(-1, i)) for i in range(1, 16)]
+            out.append(dict(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree",
+                            prefix_len=P, parent=par, kv_capacity=P + 16))
+    return out
+
+
+@pytest.mark.parametrize("kw", _cases())
+def test_plan_matches_oracle_geometry(kw):
+    plan = va.Plan(**kw)
+    info = plan.info
+    p = _oracle_problem(kw)
+    lo, hi = masks.union_extent_fast(p)
+    assert (info["lo"], info["hi"]) == (lo, hi)
+    if hi - lo < 20000:
+        assert masks.union_extent(p) == (lo, hi)
+    if kw.get("mask") == "tree":
+        anc = masks.tree_ancestors(p.parent)
+        for r in range(16):
+            assert info["anc"][r] == (anc[r] if r < p.live_rows else 0)
+    # per-row visible sets from the plan equal the oracle's, position by position
+    span_lo = max(0, lo - 70)
+    span_hi = hi + 70
+    vm = masks.visible_matrix(p, span_lo, span_hi)
+    j = np.arange(span_lo, span_hi)
+    for r in range(kw["rows"]):
+        mine = (j >= info["row_lo"][r]) & (j < info["row_hi"][r])
+        if kw.get("mask") == "tree":
+            i = j - kw["prefix_len"]
+            mine |= (i >= 0) & (i < 16) & ((np.int64(info["anc"][r]) >> np.clip(i, 0, 15)) & 1 == 1)
+        if r >= kw["live_rows"]:
+            assert not mine.any()
+        assert np.array_equal(mine, vm[r]), r
+    # split table equals the oracle's rule for the plan's own count and for others
+    for S in sorted({plan.splits, 1, 3, 8, 64}):
+        kw2 = dict(kw)
+        kw2["splits"] = S
+        plan2 = va.Plan(**kw2)
+        got = [va.verify_attn_plan_split_range(plan2, s) for s in range(S)]
+        exp = masks.split_key_ranges(lo, hi, S)
+        exp = [(a, b) if b > a else None for a, b in exp]
+        got = [(a, b) if b > a else None for a, b in got]
+        assert got == exp
+
+
+def test_workspace_size_formula():
+    plan = va.Plan(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=2048,
+                   parent=[-1] * 16, kv_capacity=2064, splits=10)
+    units = 10 * 4 * 96
+    ml = (units * 8 + 255) // 256 * 256
+    assert plan.workspace_bytes == ml + units * 128 * 4
+
+
+def test_chosen_splits_are_sane():
+    for P in (1024, 4096, 16384, 32768, 65536, 131072, 196608):
+        plan = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, first_pos=P,
+                       kv_capacity=262144, num_cus=256)
+        S, T = plan.splits, plan.info["tiles"]
+        assert 1 <= S <= T and S <= 4096
+        if S >= 8:
+            assert S % 8 == 0
