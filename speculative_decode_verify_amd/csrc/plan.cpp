@@ -15,11 +15,12 @@ static inline int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
 static inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // Splits: each workgroup streams a contiguous run of tiles.  Enough
-// workgroups to cover every CU (and the 8 XCDs evenly), but not so many that
-// the partials' traffic rivals the KV bytes: at least kMinTilesPerSplit tiles
-// per split.  The constants come from a measured sweep (bench.py --sweep-splits).
+// workgroups to cover every CU (and the 8 XCDs evenly) in a single round --
+// the split kernel's LDS footprint admits one workgroup per CU -- but not so
+// many that the partials' traffic rivals the KV bytes: at least
+// kMinTilesPerSplit tiles per split.
 static const int64_t kMinTilesPerSplit = 4;
-static const int64_t kWorkgroupsPerCU = 2;
+static const int64_t kWorkgroupsPerCU = 1;
 
 static int32_t choose_splits(int64_t tiles, int32_t kv_heads, int32_t num_cus) {
   if (tiles <= 0) return 1;

@@ -40,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef float f32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+typedef float f32x2 __attribute__((__vector_size__(8)));
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f
@@ -69,7 +70,11 @@ struct SplitArgs {
   int32_t ring_slots, ring_base_slot;
   int32_t tree, tree_lo;     // tree mode: relative position of node 0's key
   float scale_log2;          // scale * log2(e)
-  int32_t row_lo[VA_MAX_ROWS], row_hi[VA_MAX_ROWS];  // relative, padding rows empty
+  // Row geometry, relative to base.  Chain modes: row r sits at t0_rel + r and
+  // sees [max(t0_rel + r - window + 1, 0), t0_rel + r] (window = 0: from 0).
+  // Tree mode: every live row sees [0, tree_lo) plus the node keys whose
+  // bits are set in anc[r].
+  int32_t t0_rel, window;
   uint32_t anc[VA_MAX_ROWS];
 };
 
@@ -109,7 +114,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // E4M3FN pair -> two floats (exact), via the gfx950 OCP converter.
 __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
-  typedef float f32x2 __attribute__((__vector_size__(8)));
   f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
   f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
   out[0] = a[0];
@@ -126,6 +130,16 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
 }
 __device__ __forceinline__ void dma4(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, output lane n, element e is the (n % 4)-th 16-bit value of the 8
+// bytes addressed by lane 4e + n/4 of that group.  (Layout checked on the
+// GPU with an in-bounds probe.)
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // Byte offset of relative key j (clamped into the extent by the caller).
@@ -167,14 +181,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
   constexpr int kBufB = 2 * kTileB + kScaleB;
   constexpr int kStageBytes = kWaves * 2 * kBufB;
 
-  // LDS layout: [Q tile | staging] during the loop; the FP32 WHT scratch
-  // (quantised keys) overlays the staging area before the loop, and the
-  // cross-wave merge overlays both after it.
+  // LDS layout: [Q tile | staging | FP32 WHT scratch (quantised keys only)];
+  // the cross-wave merge overlays the Q tile and staging after the loop.
   constexpr int QROWS = 16 * NBW * RG;               // padded query matrix rows
   constexpr int kQT = QROWS * D * 2;                 // bf16 Q tile
   constexpr int kWHT = FMT == 1 ? VA_MAX_MATRIX_ROWS * 128 * 4 : 0;
   constexpr int kMergeBytes = 2 * ROWS_W * D * 4;    // two O^T tiles
-  constexpr int kLoop = kQT + (kStageBytes > kWHT ? kStageBytes : kWHT);
+  constexpr int kLoop = kQT + kStageBytes + kWHT;    // WHT scratch may not overlay early DMA
   constexpr int kBig = kLoop > kMergeBytes ? kLoop : kMergeBytes;
   constexpr int kML = kWaves * ROWS_W * 2 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kBig + kML];
@@ -191,36 +204,109 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
 
+  // ---------------- this split's chunk range ----------------
+  const int64_t T = a.tiles, S = a.splits;
+  const int32_t t0 = (int32_t)(((int64_t)split * T) / S);
+  const int32_t t1 = (int32_t)(((int64_t)(split + 1) * T) / S);
+  int32_t c_first = 2 * t0, c_last = 2 * t1;  // in 32-key chunks, relative
+  if (c_first < a.rel_lo / kChunk) c_first = a.rel_lo / kChunk;
+  const int32_t c_end_ext = (a.rel_hi + kChunk - 1) / kChunk;
+  if (c_last > c_end_ext) c_last = c_end_ext;
+  const int32_t nchunks = c_last > c_first ? c_last - c_first : 0;
+  // chunks handled by this wave: c_first + stream + STREAMS * n
+  const int32_t my_n = nchunks > stream ? (nchunks - stream + STREAMS - 1) / STREAMS : 0;
+
+  const uint8_t *kbase = a.k + (int64_t)kvh * a.kv_head_stride_b;
+  const uint8_t *vbase = a.v + (int64_t)kvh * a.kv_head_stride_b;
+  uint8_t *stage = smem + kQT + wave * 2 * kBufB;
+
+  // A chunk never straddles the ring's wrap (slots are 64-aligned), so every
+  // key of chunk c0 lives at row_of(c0) + (j - c0): one scalar base per chunk
+  // plus a 32-bit lane offset.  Keys outside [rel_lo, rel_hi) are clamped to
+  // the extent's ends (read, then masked), so nothing outside it is read.
+  auto chunk_row = [&](int32_t c0) -> int64_t {
+    return a.ring_slots ? (int64_t)(((uint32_t)a.ring_base_slot + (uint32_t)c0) % (uint32_t)a.ring_slots)
+                        : a.base + c0;
+  };
+  auto clampx = [&](int32_t x, int32_t c0) -> int32_t {
+    const int32_t lo = a.rel_lo - c0, hi = a.rel_hi - 1 - c0;
+    return x < lo ? lo : (x > hi ? hi : x);
+  };
+  const uint32_t rs = (uint32_t)a.kv_row_stride_b;
+
+  // Piece swizzles inside the staged tiles (position = piece ^ f(row)):
+  //   K: f = row % PIECES -> the 16 lanes reading one A operand (16 keys,
+  //      same piece) hit 16 different positions.
+  //   V (bf16): f = 2 * (row % (PIECES/2)), an even value, so a pair of
+  //      pieces {2k, 2k+1} stays a pair; the 16 rows of one transpose read
+  //      spread over all bank groups.  V (INT8) is read bytewise, unswizzled.
+  auto fk = [](int row) { return row & (PIECES - 1); };
+  auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
+
+  // Issue the LDS DMA of chunk n into buffer `buf` (lane l of instruction t
+  // stores 16 bytes at tile + 1024*t + 16*l).
+  auto issue = [&](int32_t n, int buf) {
+    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
+    const int64_t crow = chunk_row(c0);
+    const uint8_t *kc = kbase + crow * a.kv_row_stride_b;
+    const uint8_t *vc = vbase + crow * a.kv_row_stride_b;
+    uint8_t *kt = stage + buf * kBufB;
+    uint8_t *vt = kt + kTileB;
+#pragma unroll
+    for (int t = 0; t < NDMA; ++t) {
+      const int row = t * RPI + lane / PIECES;
+      const int pos = lane % PIECES;
+      const uint32_t roff = (uint32_t)clampx(row, c0) * rs;
+      dma16(kc + roff + 16 * (pos ^ fk(row)), kt + 1024 * t);
+      dma16(vc + roff + 16 * (pos ^ fv(row)), vt + 1024 * t);
+    }
+    if constexpr (FMT == 1) {
+      const float *sc = a.v_scale + (int64_t)kvh * a.v_scale_head_stride + crow;
+      dma4(sc + clampx(lane & 31, c0), vt + kTileB);
+    }
+  };
+
+  // The first two chunks start streaming before anything else is set up.
+  if (my_n > 0) issue(0, 0);
+  if (my_n > 1) issue(1, 1);
+
   // ---------------- Q tile in LDS (B operand of S^T = K Q^T) ----------------
   // Piece p (8 contraction elements) of matrix row m is stored at position
   // p ^ (m % QP), so the lanes reading one operand spread over the banks.
+  // Loads are unconditional (padded rows read row 0 and are zeroed), so they
+  // all issue before the first wait.
   constexpr int QP = D / 8;  // pieces per row
   if constexpr (FMT == 0) {
-    for (int idx = threadIdx.x; idx < QROWS * QP; idx += kThreads) {
+    constexpr int kIt = (QROWS * QP + kThreads - 1) / kThreads;
+    u32x4 qv[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int idx = threadIdx.x + it * kThreads;
       const int m = idx / QP, pc = idx % QP;
       const int r = m / a.group;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (m < a.mrows && r < a.live_rows) {
-        const int h = kvh * a.group + (m - r * a.group);
-        w = *(const u32x4 *)(a.q + ((int64_t)(r * a.q_heads + h) * D + 8 * pc) * 2);
-      }
-      *(u32x4 *)(qt + m * D + 8 * (pc ^ (m & (QP - 1)))) = w;
+      const bool ok = (idx < QROWS * QP) && (m < a.mrows) && (r < a.live_rows);
+      const int rr = ok ? r : 0, h = ok ? kvh * a.group + (m - r * a.group) : 0;
+      qv[it] = *(const u32x4 *)(a.q + ((int64_t)(rr * a.q_heads + h) * D + 8 * (ok ? pc : 0)) * 2);
+      if (!ok) qv[it] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int idx = threadIdx.x + it * kThreads;
+      const int m = idx / QP, pc = idx % QP;
+      if (idx < QROWS * QP) *(u32x4 *)(qt + m * D + 8 * (pc ^ (m & (QP - 1)))) = qv[it];
     }
     __syncthreads();
   } else {
     // q' = H q / sqrt(128) in FP32 (natural-order Walsh-Hadamard), then bf16.
-    float *qs = (float *)(smem + kQT);
+    float *qs = (float *)(smem + kQT + kStageBytes);
     const int nrows = a.mrows;
     for (int idx = threadIdx.x; idx < nrows * 128; idx += kThreads) {
       const int m = idx >> 7, d = idx & 127;
       const int r = m / a.group;
-      const int h = kvh * a.group + (m - r * a.group);
-      float x = 0.f;
-      if (r < a.live_rows) {
-        const uint16_t u = *(const uint16_t *)(a.q + ((int64_t)(r * a.q_heads + h) * 128 + d) * 2);
-        x = __uint_as_float((uint32_t)u << 16);
-      }
-      qs[idx] = x;
+      const bool ok = r < a.live_rows;
+      const int rr = ok ? r : 0, h = ok ? kvh * a.group + (m - r * a.group) : 0;
+      const uint16_t u = *(const uint16_t *)(a.q + ((int64_t)(rr * a.q_heads + h) * 128 + d) * 2);
+      qs[idx] = ok ? __uint_as_float((uint32_t)u << 16) : 0.f;
     }
     __syncthreads();
 #pragma unroll 1
@@ -265,6 +351,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
   };
 
   // ---------------- per-lane row geometry for boundary masks ----------------
+  // Computed from scalars (no per-lane loads): causal/window rows from their
+  // position, tree ancestor bits selected from the sixteen kernel arguments.
   int32_t rlo[NBW], rhi[NBW];
   uint32_t ranc[NBW];
 #pragma unroll
@@ -272,10 +360,22 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     const int m = 16 * (rg * NBW + nb) + i16;
     const int r = m / a.group;
     const bool ok = (m < a.mrows) && (r < a.live_rows);
-    const int rr = ok ? r : 0;  // padded matrix rows never index past the row tables
-    rlo[nb] = ok ? a.row_lo[rr] : 0;
-    rhi[nb] = ok ? a.row_hi[rr] : 0;
-    ranc[nb] = ok ? a.anc[rr] : 0u;
+    int32_t lo_r, hi_r;
+    uint32_t an = 0u;
+    if (a.tree) {
+      lo_r = 0;
+      hi_r = a.tree_lo;
+#pragma unroll
+      for (int i = 0; i < VA_MAX_ROWS; ++i) an = (r == i) ? a.anc[i] : an;
+    } else {
+      const int32_t t = a.t0_rel + r;
+      hi_r = t + 1;
+      lo_r = a.window ? t - a.window + 1 : INT32_MIN;
+      if (lo_r < 0) lo_r = 0;
+    }
+    rlo[nb] = ok ? lo_r : 0;
+    rhi[nb] = ok ? hi_r : 0;
+    ranc[nb] = ok ? an : 0u;
   }
 
   // ---------------- online-softmax state ----------------
@@ -289,66 +389,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) o[md][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-
-  // ---------------- this split's chunk range ----------------
-  const int64_t T = a.tiles, S = a.splits;
-  const int32_t t0 = (int32_t)(((int64_t)split * T) / S);
-  const int32_t t1 = (int32_t)(((int64_t)(split + 1) * T) / S);
-  int32_t c_first = 2 * t0, c_last = 2 * t1;  // in 32-key chunks, relative
-  if (c_first < a.rel_lo / kChunk) c_first = a.rel_lo / kChunk;
-  const int32_t c_end_ext = (a.rel_hi + kChunk - 1) / kChunk;
-  if (c_last > c_end_ext) c_last = c_end_ext;
-  const int32_t nchunks = c_last > c_first ? c_last - c_first : 0;
-  // chunks handled by this wave: c_first + stream + STREAMS * n
-  const int32_t my_n = nchunks > stream ? (nchunks - stream + STREAMS - 1) / STREAMS : 0;
-
-  const uint8_t *kbase = a.k + (int64_t)kvh * a.kv_head_stride_b;
-  const uint8_t *vbase = a.v + (int64_t)kvh * a.kv_head_stride_b;
-  uint8_t *stage = smem + kQT + wave * 2 * kBufB;
-
-  // A chunk never straddles the ring's wrap (slots are 64-aligned), so every
-  // key of chunk c0 lives at row_of(c0) + (j - c0): one scalar base per chunk
-  // plus a 32-bit lane offset.  Keys outside [rel_lo, rel_hi) are clamped to
-  // the extent's ends (read, then masked), so nothing outside it is read.
-  auto chunk_row = [&](int32_t c0) -> int64_t {
-    return a.ring_slots ? (int64_t)(((uint32_t)a.ring_base_slot + (uint32_t)c0) % (uint32_t)a.ring_slots)
-                        : a.base + c0;
-  };
-  auto clampx = [&](int32_t x, int32_t c0) -> int32_t {
-    const int32_t lo = a.rel_lo - c0, hi = a.rel_hi - 1 - c0;
-    return x < lo ? lo : (x > hi ? hi : x);
-  };
-  const uint32_t rs = (uint32_t)a.kv_row_stride_b;
-
-  // Piece swizzle inside a staged K tile (position = piece ^ (row % PIECES)):
-  // the 16 lanes reading one A operand (16 keys, same piece) hit 16
-  // different positions.  The V tile is unswizzled so that every V^T gather
-  // address is one lane base plus an immediate.
-  auto fk = [](int row) { return row & (PIECES - 1); };
-  auto fv = [](int row) { return 0 * row; };
-
-  // Issue the LDS DMA of chunk n into buffer `buf` (lane l of instruction t
-  // stores 16 bytes at tile + 1024*t + 16*l).
-  auto issue = [&](int32_t n, int buf) {
-    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
-    const int64_t crow = chunk_row(c0);
-    const uint8_t *kc = kbase + crow * a.kv_row_stride_b;
-    const uint8_t *vc = vbase + crow * a.kv_row_stride_b;
-    uint8_t *kt = stage + buf * kBufB;
-    uint8_t *vt = kt + kTileB;
-#pragma unroll
-    for (int t = 0; t < NDMA; ++t) {
-      const int row = t * RPI + lane / PIECES;
-      const int pos = lane % PIECES;
-      const uint32_t roff = (uint32_t)clampx(row, c0) * rs;
-      dma16(kc + roff + 16 * (pos ^ fk(row)), kt + 1024 * t);
-      dma16(vc + roff + 16 * (pos ^ fv(row)), vt + 1024 * t);
-    }
-    if constexpr (FMT == 1) {
-      const float *sc = a.v_scale + (int64_t)kvh * a.v_scale_head_stride + crow;
-      dma4(sc + clampx(lane & 31, c0), vt + kTileB);
-    }
-  };
 
   // vector-memory instructions per issued chunk (all of them LDS DMA)
   constexpr int kVmPerChunk = 2 * NDMA + (FMT == 1 ? 1 : 0);
@@ -399,18 +439,29 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     // V^T operand for block md: lane (i16 = d within the block, g4) takes the
     // keys {4g..4g+3, 16+4g..16+4g+3} of column d.
     bf16x8 vop[MD];
+    if constexpr (FMT == 0) {
+      // Two transpose reads per block: lane s of group g4 addresses row
+      // 4*g4 + s/4 (then +16), columns 16*md + 4*(s%4) .. +3, so output lane
+      // i16 receives V[4*g4 + e][16*md + i16], e = 0..3.
+      const int rowA = 4 * g4 + (i16 >> 2);
+      const int F = fv(rowA) >> 1;  // same for rowA + 16
+      const uint8_t *vb = vt + rowA * KROW + 8 * (i16 & 3);
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      const int d = 16 * md + i16;
+      for (int md = 0; md < MD; ++md) {
+        const uint8_t *pa = vb + 32 * (md ^ F);
+        const u32x2 lo = lds_read_tr16(pa);
+        const u32x2 hi = lds_read_tr16(pa + 16 * KROW);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        vop[md] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int row = t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4);
-        if constexpr (FMT == 0) {
-          const int pos = (d >> 3) ^ fv(row);
-          vop[md][t] = *(const __bf16 *)(vt + row * KROW + 16 * pos + 2 * (d & 7));
-        } else {
-          const int pos = (d >> 4) ^ fv(row);
-          const int8_t c = *(const int8_t *)(vt + row * KROW + 16 * pos + (d & 15));
+      for (int md = 0; md < MD; ++md) {
+        const int d = 16 * md + i16;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4);
+          const int8_t c = *(const int8_t *)(vt + row * KROW + d);
           vop[md][t] = (__bf16)(float)c;  // exact
         }
       }
@@ -521,11 +572,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
       }
   };
 
-  if (my_n > 0) {
-    issue(0, 0);
-    if (my_n > 1) issue(1, 1);
-    for (int32_t n = 0; n < my_n; ++n) step(n);
-  }
+  for (int32_t n = 0; n < my_n; ++n) step(n);
 
   // ---------------- normalise to the true maximum ----------------
   float mrow[NBW];
@@ -630,8 +677,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
 constexpr int kMaxSplits = 4096;
 
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+  constexpr int kPer = kMaxSplits / 256;  // (m, l) pairs per thread
   __shared__ float wts[kMaxSplits];
   __shared__ float red[8];
+  __shared__ float gsum[4][64];
 
   const int rh = blockIdx.x;
   const int r = rh / a.q_heads, h = rh % a.q_heads;
@@ -641,8 +690,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int d = 64 * blockIdx.y + dl;
   float *outp = a.out + ((int64_t)r * a.q_heads + h) * D;
 
-  if (r >= a.live_rows) {
-    outp[d] = 0.f;
+  if (r >= a.live_rows) {  // padding row: no read of the workspace
+    if (grp == 0) outp[d] = 0.f;
     if (a.lse && blockIdx.y == 0 && t == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
     return;
   }
@@ -653,25 +702,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int64_t unit0 = (int64_t)g * a.mrows + mrow;
   const float sink2 = a.sink ? a.sink[h] * LOG2E_F : -INFINITY;
 
-  // 1) max over splits (and the sink)
+  // 1) every (m, l) pair of this row, loads issued together, kept in registers
+  const f32x2 *ml = (const f32x2 *)a.ws_ml;
+  float mv[kPer], lv[kPer];
   float mx = -INFINITY;
-  for (int s = t; s < S; s += 256) mx = fmaxf(mx, a.ws_ml[(unit0 + s * stride_unit) * 2]);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = t + 256 * i;
+    f32x2 x = {-INFINITY, 0.f};
+    if (s < S) x = ml[unit0 + s * stride_unit];
+    mv[i] = x[0];
+    lv[i] = x[1];
+    mx = fmaxf(mx, x[0]);
+  }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   if ((t & 63) == 0) red[t >> 6] = mx;
   __syncthreads();
-  float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  M = fmaxf(M, sink2);
+  const float M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), sink2);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  __syncthreads();
 
-  // 2) weights and denominator
+  // 2) weights 2^(m_s - M) and the denominator
   float den = 0.f;
-  for (int s = t; s < S; s += 256) {
-    const float ms = a.ws_ml[(unit0 + s * stride_unit) * 2];
-    const float ls = a.ws_ml[(unit0 + s * stride_unit) * 2 + 1];
-    const float w = __builtin_amdgcn_exp2f(ms - Mu);
-    wts[s] = w;
-    den += w * ls;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = t + 256 * i;
+    if (s < S) {
+      const float w = __builtin_amdgcn_exp2f(mv[i] - Mu);
+      wts[s] = w;
+      den += w * lv[i];
+    }
   }
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
   if ((t & 63) == 0) red[4 + (t >> 6)] = den;
@@ -679,8 +738,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   den = (red[4] + red[5]) + (red[6] + red[7]);
   den += __builtin_amdgcn_exp2f(sink2 - Mu);
 
-  // 3) weighted sum of O: thread group grp takes splits s = grp (mod 4), four
-  //    independent chains over consecutive such splits, loads issued together.
+  // 3) weighted sum of O: thread group grp takes splits s = grp (mod 4);
+  //    four independent chains over consecutive such splits, loads issued together.
   const float *ob = a.ws_o + unit0 * D + d;
   const int64_t sstride = stride_unit * D;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
@@ -701,12 +760,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const float acc = (acc0 + acc1) + (acc2 + acc3);
 
   // 4) reduce the four groups
-  __shared__ float gsum[4][64];
   gsum[grp][dl] = acc;
   __syncthreads();
   if (grp == 0) {
     const float tot = (gsum[0][dl] + gsum[1][dl]) + (gsum[2][dl] + gsum[3][dl]);
-    if (M == -INFINITY) {
+    if (M == -INFINITY) {  // nothing visible and no sink
       outp[d] = 0.f;
       if (a.lse && blockIdx.y == 0 && dl == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
     } else {
@@ -828,15 +886,9 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
     a.tree_lo = (int32_t)(tl > (int64_t)1 << 30 ? (int64_t)1 << 30 : tl);
   }
   a.scale_log2 = d->scale * LOG2E_F;
-  for (int r = 0; r < VA_MAX_ROWS; ++r) {
-    int64_t lo = d->row_lo[r] - a.base, hi = d->row_hi[r] - a.base;
-    if (d->row_hi[r] <= d->row_lo[r]) lo = hi = 0;
-    if (lo < 0) lo = 0;
-    if (hi < lo) hi = lo;
-    a.row_lo[r] = (int32_t)lo;
-    a.row_hi[r] = (int32_t)hi;
-    a.anc[r] = d->anc[r];
-  }
+  a.t0_rel = (d->mask == VA_MASK_TREE) ? 0 : (int32_t)(d->first_pos - a.base);
+  a.window = (d->mask == VA_MASK_WINDOW) ? d->window : 0;
+  for (int r = 0; r < VA_MAX_ROWS; ++r) a.anc[r] = d->anc[r];
   const int nb_total = (d->matrix_rows + 15) / 16;
   hipError_t e;
   if (quant) {
