@@ -133,8 +133,9 @@ va_status verify_attn_plan(const va_problem *p, va_plan *plan, size_t *workspace
 va_status verify_attn_plan_query(const va_plan *plan, va_plan_info *info);
 
 /* Key range [*key_begin, *key_end) that split s covers (empty if begin ==
- * end): tiles floor(s*T/S)..floor((s+1)*T/S) from tile_lo, clipped to
- * [lo, hi).  Host only. */
+ * end).  With q = T / S and r = T % S, split s takes q + 1 tiles if s < r
+ * and q otherwise, contiguous from tile_lo; keys are clipped to [lo, hi).
+ * Host only. */
 va_status verify_attn_plan_split_range(const va_plan *plan, int32_t s,
                                        int64_t *key_begin, int64_t *key_end);
 

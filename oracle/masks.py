@@ -21,8 +21,9 @@ Readings where the pages leave a step open:
   node hangs off the last committed token, which is already in the prefix.
 * Ring slot of position p is p mod ring_slots.
 * Splits are contiguous runs of 64-key tiles starting at the tile holding the
-  lowest visible key; split s of S over T tiles gets tiles
-  [floor(s*T/S), floor((s+1)*T/S)).
+  lowest visible key, balanced to within one tile: with q = T // S and
+  r = T % S, split s takes q + 1 tiles if s < r and q tiles otherwise, in
+  order.
 """
 
 import numpy as np
@@ -159,9 +160,10 @@ def split_key_ranges(lo, hi, splits):
     t_hi = -(-hi // TILE)
     n = t_hi - t_lo
     out = []
+    q, r = divmod(n, splits)
     for s in range(splits):
-        a_t = t_lo + (s * n) // splits
-        b_t = t_lo + ((s + 1) * n) // splits
+        a_t = t_lo + s * q + min(s, r)
+        b_t = a_t + q + (1 if s < r else 0)
         a = max(lo, a_t * TILE)
         b = min(hi, b_t * TILE)
         out.append((a, b) if b > a else (a, a))

@@ -186,8 +186,9 @@ extern "C" va_status verify_attn_plan_split_range(const va_plan *plan, int32_t s
   const va_plan_data *d = as_data(plan);
   if (!d || !key_begin || !key_end || s < 0 || s >= d->splits) return VA_ERR_INVALID;
   const int64_t T = d->tiles, S = d->splits;
-  const int64_t t0 = d->tile_lo + (s * T) / S;
-  const int64_t t1 = d->tile_lo + ((s + 1) * T) / S;
+  const int64_t q = T / S, r = T % S;
+  const int64_t t0 = d->tile_lo + s * q + (s < r ? s : r);
+  const int64_t t1 = t0 + q + (s < r ? 1 : 0);
   int64_t a = imax64(d->lo, t0 * VA_TILE);
   int64_t b = imin64(d->hi, t1 * VA_TILE);
   if (b < a) b = a;

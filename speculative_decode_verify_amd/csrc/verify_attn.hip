@@ -64,7 +64,7 @@ struct SplitArgs {
   int64_t v_scale_head_stride;
   int64_t base;  // absolute position of relative key 0 (= tile_lo * 64)
   int32_t rows, live_rows, group, mrows, q_heads, kv_heads;
-  int32_t splits, tiles;
+  int32_t splits, tiles, tiles_q, tiles_r;  // tiles_q = tiles / splits, tiles_r = tiles % splits
   int32_t rel_lo, rel_hi;    // read extent, relative to base
   int32_t full_lo, full_hi;  // every live row sees these keys (relative)
   int32_t ring_slots, ring_base_slot;
@@ -142,17 +142,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Byte offset of relative key j (clamped into the extent by the caller).
-__device__ __forceinline__ int64_t key_offset(const SplitArgs &a, int32_t jrel) {
-  int64_t slot;
-  if (a.ring_slots) {
-    slot = (int64_t)(((uint32_t)a.ring_base_slot + (uint32_t)jrel) % (uint32_t)a.ring_slots);
-  } else {
-    slot = a.base + jrel;
-  }
-  return slot * a.kv_row_stride_b;
-}
-
 // ---------------------------------------------------------------------------
 // Split kernel.
 //   D     head dim (64 or 128)
@@ -186,10 +175,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
   constexpr int QROWS = 16 * NBW * RG;               // padded query matrix rows
   constexpr int kQT = QROWS * D * 2;                 // bf16 Q tile
   constexpr int kWHT = FMT == 1 ? VA_MAX_MATRIX_ROWS * 128 * 4 : 0;
-  constexpr int kMergeBytes = 2 * ROWS_W * D * 4;    // two O^T tiles
+  constexpr int kMergeBytes = kWaves * ROWS_W * D * 4;  // every wave's O^T tile
   constexpr int kLoop = kQT + kStageBytes + kWHT;    // WHT scratch may not overlay early DMA
   constexpr int kBig = kLoop > kMergeBytes ? kLoop : kMergeBytes;
-  constexpr int kML = kWaves * ROWS_W * 2 * 4;
+  constexpr int kML = kWaves * ROWS_W * 3 * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kBig + kML];
   uint16_t *qt = (uint16_t *)smem;  // [QROWS][D], 16-byte pieces XOR-swizzled by (row & 15)
 
@@ -205,34 +194,40 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
   const int kvh = blockIdx.y;
 
   // ---------------- this split's chunk range ----------------
-  const int64_t T = a.tiles, S = a.splits;
-  const int32_t t0 = (int32_t)(((int64_t)split * T) / S);
-  const int32_t t1 = (int32_t)(((int64_t)(split + 1) * T) / S);
+  // Everything the first DMA needs is read here, in straight-line code, so
+  // the kernel-argument loads issue together.
+  const int32_t tq = a.tiles_q, tr = a.tiles_r, rel_lo = a.rel_lo, rel_hi = a.rel_hi;
+  const int32_t ring_slots = a.ring_slots, ring_base = a.ring_base_slot;
+  const int64_t kv_base = a.base, row_stride = a.kv_row_stride_b, head_stride = a.kv_head_stride_b;
+  const uint8_t *kbase = a.k + (int64_t)kvh * head_stride;
+  const uint8_t *vbase = a.v + (int64_t)kvh * head_stride;
+  // split s takes q + 1 tiles if s < r, else q (q = T / S, r = T % S)
+  const int32_t t0 = split * tq + (split < tr ? split : tr);
+  const int32_t t1 = t0 + tq + (split < tr ? 1 : 0);
   int32_t c_first = 2 * t0, c_last = 2 * t1;  // in 32-key chunks, relative
-  if (c_first < a.rel_lo / kChunk) c_first = a.rel_lo / kChunk;
-  const int32_t c_end_ext = (a.rel_hi + kChunk - 1) / kChunk;
+  if (c_first < rel_lo / kChunk) c_first = rel_lo / kChunk;
+  const int32_t c_end_ext = (rel_hi + kChunk - 1) / kChunk;
   if (c_last > c_end_ext) c_last = c_end_ext;
   const int32_t nchunks = c_last > c_first ? c_last - c_first : 0;
   // chunks handled by this wave: c_first + stream + STREAMS * n
   const int32_t my_n = nchunks > stream ? (nchunks - stream + STREAMS - 1) / STREAMS : 0;
 
-  const uint8_t *kbase = a.k + (int64_t)kvh * a.kv_head_stride_b;
-  const uint8_t *vbase = a.v + (int64_t)kvh * a.kv_head_stride_b;
   uint8_t *stage = smem + kQT + wave * 2 * kBufB;
 
   // A chunk never straddles the ring's wrap (slots are 64-aligned), so every
   // key of chunk c0 lives at row_of(c0) + (j - c0): one scalar base per chunk
   // plus a 32-bit lane offset.  Keys outside [rel_lo, rel_hi) are clamped to
   // the extent's ends (read, then masked), so nothing outside it is read.
+  const uint32_t ring_div = ring_slots > 0 ? (uint32_t)ring_slots : 1u;
   auto chunk_row = [&](int32_t c0) -> int64_t {
-    return a.ring_slots ? (int64_t)(((uint32_t)a.ring_base_slot + (uint32_t)c0) % (uint32_t)a.ring_slots)
-                        : a.base + c0;
+    const int64_t ring_row = (int64_t)(((uint32_t)ring_base + (uint32_t)c0) % ring_div);
+    return ring_slots ? ring_row : kv_base + c0;
   };
   auto clampx = [&](int32_t x, int32_t c0) -> int32_t {
-    const int32_t lo = a.rel_lo - c0, hi = a.rel_hi - 1 - c0;
+    const int32_t lo = rel_lo - c0, hi = rel_hi - 1 - c0;
     return x < lo ? lo : (x > hi ? hi : x);
   };
-  const uint32_t rs = (uint32_t)a.kv_row_stride_b;
+  const uint32_t rs = (uint32_t)row_stride;
 
   // Piece swizzles inside the staged tiles (position = piece ^ f(row)):
   //   K: f = row % PIECES -> the 16 lanes reading one A operand (16 keys,
@@ -244,31 +239,71 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
   auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
 
   // Issue the LDS DMA of chunk n into buffer `buf` (lane l of instruction t
-  // stores 16 bytes at tile + 1024*t + 16*l).
-  auto issue = [&](int32_t n, int buf) {
-    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
-    const int64_t crow = chunk_row(c0);
-    const uint8_t *kc = kbase + crow * a.kv_row_stride_b;
-    const uint8_t *vc = vbase + crow * a.kv_row_stride_b;
-    uint8_t *kt = stage + buf * kBufB;
-    uint8_t *vt = kt + kTileB;
+  // stores 16 bytes at tile + 1024*t + 16*l).  Interior chunks use per-lane
+  // byte offsets computed once (row * stride + swizzled piece) on top of the
+  // chunk's scalar base; only a chunk that crosses the extent's ends clamps
+  // its rows.
+  uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
-    for (int t = 0; t < NDMA; ++t) {
-      const int row = t * RPI + lane / PIECES;
-      const int pos = lane % PIECES;
-      const uint32_t roff = (uint32_t)clampx(row, c0) * rs;
-      dma16(kc + roff + 16 * (pos ^ fk(row)), kt + 1024 * t);
-      dma16(vc + roff + 16 * (pos ^ fv(row)), vt + 1024 * t);
+  for (int t = 0; t < NDMA; ++t) {
+    const int row = t * RPI + lane / PIECES;
+    const int pos = lane % PIECES;
+    koff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ fk(row));
+    voff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ fv(row));
+  }
+  auto chunk_ptrs = [&](int32_t n, const uint8_t *base) -> const uint8_t * {
+    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
+    return base + chunk_row(c0) * row_stride;
+  };
+  // K group of chunk n: NDMA instructions into K buffer `buf`.
+  auto issueK = [&](int32_t n, int buf) {
+    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
+    const uint8_t *kc = chunk_ptrs(n, kbase);
+    uint8_t *kt = stage + buf * kBufB;
+    if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
+#pragma unroll
+      for (int t = 0; t < NDMA; ++t) dma16(kc + koff[t], kt + 1024 * t);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NDMA; ++t) {
+        const int row = t * RPI + lane / PIECES;
+        const int pos = lane % PIECES;
+        dma16(kc + (uint32_t)clampx(row, c0) * rs + 16 * (pos ^ fk(row)), kt + 1024 * t);
+      }
+    }
+  };
+  // V group of chunk n: NDMA instructions (+1 for the INT8 scales) into V buffer `buf`.
+  auto issueV = [&](int32_t n, int buf) {
+    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
+    const uint8_t *vc = chunk_ptrs(n, vbase);
+    uint8_t *vt = stage + buf * kBufB + kTileB;
+    if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
+#pragma unroll
+      for (int t = 0; t < NDMA; ++t) dma16(vc + voff[t], vt + 1024 * t);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NDMA; ++t) {
+        const int row = t * RPI + lane / PIECES;
+        const int pos = lane % PIECES;
+        dma16(vc + (uint32_t)clampx(row, c0) * rs + 16 * (pos ^ fv(row)), vt + 1024 * t);
+      }
     }
     if constexpr (FMT == 1) {
-      const float *sc = a.v_scale + (int64_t)kvh * a.v_scale_head_stride + crow;
+      const float *sc = a.v_scale + (int64_t)kvh * a.v_scale_head_stride + chunk_row(c0);
       dma4(sc + clampx(lane & 31, c0), vt + kTileB);
     }
   };
 
-  // The first two chunks start streaming before anything else is set up.
-  if (my_n > 0) issue(0, 0);
-  if (my_n > 1) issue(1, 1);
+  // The first two chunks start streaming before anything else is set up
+  // (issue order K0 V0 K1 V1; later groups follow the per-step order below).
+  if (my_n > 0) {
+    issueK(0, 0);
+    issueV(0, 0);
+  }
+  if (my_n > 1) {
+    issueK(1, 1);
+    issueV(1, 1);
+  }
 
   // ---------------- Q tile in LDS (B operand of S^T = K Q^T) ----------------
   // Piece p (8 contraction elements) of matrix row m is stored at position
@@ -390,27 +425,28 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     for (int md = 0; md < MD; ++md) o[md][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // vector-memory instructions per issued chunk (all of them LDS DMA)
-  constexpr int kVmPerChunk = 2 * NDMA + (FMT == 1 ? 1 : 0);
+  // DMA groups complete in issue order (vector-memory operations return in
+  // order and only this wave's DMA is in flight), so a wait leaves exactly
+  // the groups issued after the one needed.  Per step n the issue order is:
+  // [wait K(n)] K(n+2) [wait V(n)] V(n+2).  The compiler does not track LDS
+  // written by DMA across loop iterations, hence the explicit waits; their
+  // memory clobber keeps the LDS reads below them.
+  constexpr int kVmK = NDMA;
+  constexpr int kVmV = NDMA + (FMT == 1 ? 1 : 0);
 
   auto step = [&](int32_t n) {
     const int buf = n & 1;
     const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
     const uint8_t *kt = stage + buf * kBufB;
     const uint8_t *vt = kt + kTileB;
+    const bool more1 = n + 1 < my_n, more2 = n + 2 < my_n;
 
-    // Chunk n's DMA must have landed.  Vector-memory operations complete in
-    // issue order and only this wave's DMA is in flight, so leaving chunk
-    // n+1's instructions outstanding is exact.  (The compiler does not track
-    // LDS written by DMA across loop iterations, hence the explicit waits;
-    // the memory clobber keeps the LDS reads below them.)
-    if (n + 1 < my_n) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmPerChunk) : "memory");
+    // ---- K(n): after it were issued V(n), and K(n+1), V(n+1) if they exist ----
+    if (more1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmV + kVmK + kVmV) : "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmV) : "memory");
     }
-
-    // ---- read every operand of this chunk from LDS ----
     bf16x8 kop[2][KS];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -436,46 +472,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
         }
       }
     }
-    // V^T operand for block md: lane (i16 = d within the block, g4) takes the
-    // keys {4g..4g+3, 16+4g..16+4g+3} of column d.
-    bf16x8 vop[MD];
-    if constexpr (FMT == 0) {
-      // Two transpose reads per block: lane s of group g4 addresses row
-      // 4*g4 + s/4 (then +16), columns 16*md + 4*(s%4) .. +3, so output lane
-      // i16 receives V[4*g4 + e][16*md + i16], e = 0..3.
-      const int rowA = 4 * g4 + (i16 >> 2);
-      const int F = fv(rowA) >> 1;  // same for rowA + 16
-      const uint8_t *vb = vt + rowA * KROW + 8 * (i16 & 3);
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const uint8_t *pa = vb + 32 * (md ^ F);
-        const u32x2 lo = lds_read_tr16(pa);
-        const u32x2 hi = lds_read_tr16(pa + 16 * KROW);
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        vop[md] = __builtin_bit_cast(bf16x8, w);
-      }
-    } else {
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const int d = 16 * md + i16;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int row = t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4);
-          const int8_t c = *(const int8_t *)(vt + row * KROW + d);
-          vop[md][t] = (__bf16)(float)c;  // exact
-        }
-      }
-    }
-    float vs[8];
-    if constexpr (FMT == 1) {
-      const float *sct = (const float *)(vt + kTileB);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) vs[t] = sct[t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4)];
-    }
-
-    // ---- refill this buffer with chunk n+2 once its reads are done ----
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (n + 2 < my_n) issue(n + 2, buf);
+    if (more2) issueK(n + 2, buf);
 
     // ---- S^T = K Q^T ----
     f32x4 s[2][NBW];
@@ -519,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     // ---- lazy reference maximum ----
     // Exponents are taken against mref, which moves only when a row's chunk
     // maximum exceeds it by more than kTau (so every p stays <= 2^kTau);
-    // moving it rescales that row's O and l.
+    // moving it rescales that row's O and l (a rare, wave-uniform branch).
     bool need = false;
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
@@ -529,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const bool mv = (xmax[nb] > mref[nb] + kTau) || (mref[nb] == -INFINITY);
+        const bool mv = xmax[nb] > mref[nb] + kTau;
         const float nref = mv ? xmax[nb] : mref[nb];
         const float alpha = (mref[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref[nb] - nref);
         lrow[nb] *= alpha;
@@ -537,10 +535,54 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
         for (int md = 0; md < MD; ++md) o[md][nb] *= alpha;
         mref[nb] = nref;
       }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) mref[nb] = (mref[nb] == -INFINITY) ? xmax[nb] : mref[nb];
+
+    // ---- V(n): after it were issued K(n+1), V(n+1), K(n+2) if they exist ----
+    if (more2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmK + kVmV + kVmK) : "memory");
+    } else if (more1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmK + kVmV) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // V^T operand for block md: lane (i16 = d within the block, g4) takes the
+    // keys {4g..4g+3, 16+4g..16+4g+3} of column d.
+    bf16x8 vop[MD];
+    float vs[8];
+    if constexpr (FMT == 0) {
+      // Two transpose reads per block: lane s of group g4 addresses row
+      // 4*g4 + s/4 (then +16), columns 16*md + 4*(s%4) .. +3, so output lane
+      // i16 receives V[4*g4 + e][16*md + i16], e = 0..3.
+      const int rowA = 4 * g4 + (i16 >> 2);
+      const int F = fv(rowA) >> 1;  // same for rowA + 16
+      const uint8_t *vb = vt + rowA * KROW + 8 * (i16 & 3);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const uint8_t *pa = vb + 32 * (md ^ F);
+        const u32x2 lo = lds_read_tr16(pa);
+        const u32x2 hi = lds_read_tr16(pa + 16 * KROW);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        vop[md] = __builtin_bit_cast(bf16x8, w);
+      }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) mref[nb] = (mref[nb] == -INFINITY) ? xmax[nb] : mref[nb];
+      for (int md = 0; md < MD; ++md) {
+        const int d = 16 * md + i16;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4);
+          const int8_t c = *(const int8_t *)(vt + row * KROW + d);
+          vop[md][t] = (__bf16)(float)c;  // exact
+        }
+      }
+      const float *sct = (const float *)(vt + kTileB);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) vs[t] = sct[t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4)];
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (more2) issueV(n + 2, buf);
 
     // ---- P^T (B operand of PV) and l ----
     uint32_t pb[NBW][4];
@@ -574,113 +616,80 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
 
   for (int32_t n = 0; n < my_n; ++n) step(n);
 
-  // ---------------- normalise to the true maximum ----------------
-  float mrow[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const float f = (mref[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref[nb] - mtrue[nb]);
-    lrow[nb] *= f;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) o[md][nb] *= f;
-    mrow[nb] = mtrue[nb];
-  }
-
   // ---------------- merge the streams of each row group ----------------
-  __syncthreads();  // staging tiles are no longer read
-  float *sml = (float *)(smem + kBig);  // [wave][ROWS_W][2]
+  // Each wave publishes, per row, its exponent reference, its true maximum and
+  // its l, plus its unnormalised O^T tile.  Then every wave of a row group
+  // merges a 1/STREAMS share of the d blocks against the split's true
+  // maximum M (weight 2^(ref_w - M) per wave) and stores it.
+  __syncthreads();  // every wave has left its loop: the staging area is free
+  float *sml = (float *)(smem + kBig);  // [wave][ROWS_W][3]: ref, true max, l
+  f32x4 *otile = (f32x4 *)smem;         // [wave][MD][NBW][64 lanes]
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     const float lt = wave_sum16x4(lrow[nb]);
-    lrow[nb] = lt;
     if (g4 == 0) {
-      sml[(wave * ROWS_W + nb * 16 + i16) * 2 + 0] = mrow[nb];
-      sml[(wave * ROWS_W + nb * 16 + i16) * 2 + 1] = lt;
+      float *e = sml + (wave * ROWS_W + nb * 16 + i16) * 3;
+      e[0] = mref[nb];
+      e[1] = mtrue[nb];
+      e[2] = lt;
     }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) otile[((wave * MD + md) * NBW + nb) * 64 + lane] = o[md][nb];
   }
   __syncthreads();
-  float mfin[NBW], lfin[NBW];
+
+  constexpr int MPW = MD / STREAMS;  // d blocks merged and stored by each wave
+  const int64_t unit0 = ((int64_t)split * a.kv_heads + kvh) * a.mrows;
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
+    const int row = nb * 16 + i16;
     float M = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < STREAMS; ++st) M = fmaxf(M, sml[((st * RG + rg) * ROWS_W + nb * 16 + i16) * 2]);
+    for (int st = 0; st < STREAMS; ++st) M = fmaxf(M, sml[((st * RG + rg) * ROWS_W + row) * 3 + 1]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
+    float f[STREAMS], L = 0.f;
 #pragma unroll
     for (int st = 0; st < STREAMS; ++st) {
-      const float mw = sml[((st * RG + rg) * ROWS_W + nb * 16 + i16) * 2];
-      const float lw = sml[((st * RG + rg) * ROWS_W + nb * 16 + i16) * 2 + 1];
-      L += lw * __builtin_amdgcn_exp2f(mw - Mu);
+      const float *e = sml + ((st * RG + rg) * ROWS_W + row) * 3;
+      f[st] = (e[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(e[0] - Mu);
+      L += f[st] * e[2];
     }
-    const float f = __builtin_amdgcn_exp2f(mrow[nb] - Mu);
+    const int m = 16 * (rg * NBW + nb) + i16;
+    if (m < a.mrows) {
+      const int r = m / a.group;
+      const bool live = r < a.live_rows;
+      if (stream == 0 && g4 == 0) {
+        a.ws_ml[(unit0 + m) * 2 + 0] = live ? M : -INFINITY;
+        a.ws_ml[(unit0 + m) * 2 + 1] = live ? L : 0.f;
+      }
+      float *op = a.ws_o + (unit0 + m) * D;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) o[md][nb] *= f;
-    mfin[nb] = M;
-    lfin[nb] = L;
-  }
-  // Tree add of the O^T tiles through LDS (C-layout order, 16 B per lane).
-  constexpr int kTile = ROWS_W * D;  // floats per wave tile
-  f32x4 *buf = (f32x4 *)smem;        // room for two tiles per row group
-  auto put = [&](int slot) {
+      for (int mi = 0; mi < MPW; ++mi) {
+        const int md = stream * MPW + mi;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) buf[(slot * kTile) / 4 + (md * NBW + nb) * 64 + lane] = o[md][nb];
-  };
-  auto add = [&](int slot) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) o[md][nb] += buf[(slot * kTile) / 4 + (md * NBW + nb) * 64 + lane];
-  };
-  if constexpr (STREAMS == 4) {
-    if (stream >= 2) put(stream - 2);
-    __syncthreads();
-    if (stream < 2) add(stream);
-    __syncthreads();
-    if (stream == 1) put(0);
-    __syncthreads();
-    if (stream == 0) add(0);
-  } else {
-    if (stream == 1) put(rg);
-    __syncthreads();
-    if (stream == 0) add(rg);
-  }
-
-  // ---------------- write the partial ----------------
-  if (stream == 0) {
-    const int64_t unit0 = ((int64_t)split * a.kv_heads + kvh) * a.mrows;
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int m = 16 * (rg * NBW + nb) + i16;
-      if (m < a.mrows) {
-        const int r = m / a.group;
-        const bool live = r < a.live_rows;
-        if (g4 == 0) {
-          a.ws_ml[(unit0 + m) * 2 + 0] = live ? mfin[nb] : -INFINITY;
-          a.ws_ml[(unit0 + m) * 2 + 1] = live ? lfin[nb] : 0.f;
-        }
-        float *op = a.ws_o + (unit0 + m) * D;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const f32x4 val = live ? o[md][nb] : (f32x4){0.f, 0.f, 0.f, 0.f};
-          *(f32x4 *)(op + 16 * md + 4 * g4) = val;
-        }
+        for (int st = 0; st < STREAMS; ++st) acc += f[st] * otile[(((st * RG + rg) * MD + md) * NBW + nb) * 64 + lane];
+        if (!live) acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+        *(f32x4 *)(op + 16 * md + 4 * g4) = acc;
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: grid (rows * Hq, D / 64), 256 threads.
+// Combine kernel: grid (rows * Hq, D / 64), 1024 threads.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 4096;
 
-__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  constexpr int kPer = kMaxSplits / 256;  // (m, l) pairs per thread
+constexpr int kCombThreads = 1024;
+constexpr int kCombGroups = kCombThreads / 64;  // split groups per block
+constexpr int kCombBatch = 16;                  // O loads each thread keeps in flight
+
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs a) {
+  constexpr int kPer = kMaxSplits / kCombThreads;  // (m, l) pairs per thread
   __shared__ float wts[kMaxSplits];
-  __shared__ float red[8];
-  __shared__ float gsum[4][64];
+  __shared__ float red[2][kCombThreads / 64];
+  __shared__ float gsum[kCombGroups][64];
 
   const int rh = blockIdx.x;
   const int r = rh / a.q_heads, h = rh % a.q_heads;
@@ -708,7 +717,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int s = t + 256 * i;
+    const int s = t + kCombThreads * i;
     f32x2 x = {-INFINITY, 0.f};
     if (s < S) x = ml[unit0 + s * stride_unit];
     mv[i] = x[0];
@@ -716,16 +725,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     mx = fmaxf(mx, x[0]);
   }
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((t & 63) == 0) red[t >> 6] = mx;
+  if ((t & 63) == 0) red[0][t >> 6] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), sink2);
+  float M = sink2;
+#pragma unroll
+  for (int i = 0; i < kCombThreads / 64; ++i) M = fmaxf(M, red[0][i]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
 
   // 2) weights 2^(m_s - M) and the denominator
   float den = 0.f;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int s = t + 256 * i;
+    const int s = t + kCombThreads * i;
     if (s < S) {
       const float w = __builtin_amdgcn_exp2f(mv[i] - Mu);
       wts[s] = w;
@@ -733,37 +744,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     }
   }
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
-  if ((t & 63) == 0) red[4 + (t >> 6)] = den;
+  if ((t & 63) == 0) red[1][t >> 6] = den;
   __syncthreads();
-  den = (red[4] + red[5]) + (red[6] + red[7]);
-  den += __builtin_amdgcn_exp2f(sink2 - Mu);
+  float dsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCombThreads / 64; ++i) dsum += red[1][i];
+  den = dsum + __builtin_amdgcn_exp2f(sink2 - Mu);
 
-  // 3) weighted sum of O: thread group grp takes splits s = grp (mod 4);
-  //    four independent chains over consecutive such splits, loads issued together.
+  // 3) weighted sum of O.  Thread group grp takes splits s = grp (mod 16); it
+  //    issues up to kCombBatch loads at once, then folds them into four
+  //    independent FP32 accumulation chains.
   const float *ob = a.ws_o + unit0 * D + d;
   const int64_t sstride = stride_unit * D;
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  int s = grp;
-  for (; s + 12 < S; s += 16) {
-    const float o0 = ob[(int64_t)s * sstride];
-    const float o1 = ob[(int64_t)(s + 4) * sstride];
-    const float o2 = ob[(int64_t)(s + 8) * sstride];
-    const float o3 = ob[(int64_t)(s + 12) * sstride];
-    acc0 = fmaf(wts[s], o0, acc0);
-    acc1 = fmaf(wts[s + 4], o1, acc1);
-    acc2 = fmaf(wts[s + 8], o2, acc2);
-    acc3 = fmaf(wts[s + 12], o3, acc3);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = grp; s0 < S; s0 += kCombGroups * kCombBatch) {
+    float o[kCombBatch];
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) {
+      const int s = s0 + kCombGroups * j;
+      o[j] = s < S ? ob[(int64_t)s * sstride] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) {
+      const int s = s0 + kCombGroups * j;
+      if (s < S) acc[j & 3] = fmaf(wts[s], o[j], acc[j & 3]);
+    }
   }
-  if (s < S) acc0 = fmaf(wts[s], ob[(int64_t)s * sstride], acc0);
-  if (s + 4 < S) acc1 = fmaf(wts[s + 4], ob[(int64_t)(s + 4) * sstride], acc1);
-  if (s + 8 < S) acc2 = fmaf(wts[s + 8], ob[(int64_t)(s + 8) * sstride], acc2);
-  const float acc = (acc0 + acc1) + (acc2 + acc3);
-
-  // 4) reduce the four groups
-  gsum[grp][dl] = acc;
+  gsum[grp][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
+
+  // 4) reduce the groups and finish
   if (grp == 0) {
-    const float tot = (gsum[0][dl] + gsum[1][dl]) + (gsum[2][dl] + gsum[3][dl]);
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombGroups; ++i) tot += gsum[i][dl];
     if (M == -INFINITY) {  // nothing visible and no sink
       outp[d] = 0.f;
       if (a.lse && blockIdx.y == 0 && dl == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
@@ -870,6 +884,8 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   a.kv_heads = d->kv_heads;
   a.splits = d->splits;
   a.tiles = (int32_t)d->tiles;
+  a.tiles_q = (int32_t)(d->tiles / d->splits);
+  a.tiles_r = (int32_t)(d->tiles % d->splits);
   a.rel_lo = (int32_t)(d->lo - a.base);
   a.rel_hi = (int32_t)(d->hi - a.base);
   a.full_lo = (int32_t)(d->full_lo - a.base);
@@ -922,7 +938,7 @@ extern "C" va_status verify_attn_combine(const va_plan *plan, const void *worksp
   a.splits = d->splits;
   a.head_dim = d->head_dim;
   dim3 grid(d->rows * d->q_heads, d->head_dim / 64);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 

@@ -248,25 +248,18 @@ def _q_rounding_bound(q_rot, keys_dec, scale, vis_hi):
     return out
 
 
-@pytest.mark.parametrize("variant", ["normal", "all_codes"])
-def test_config5_quantized_tree(variant):
+def test_config5_quantized_tree():
     """Config 4's tree and heads at 64K: keys E4M3 after the 128-point WHT,
-    values INT8 with one FP32 scale per (token, head).  `all_codes` draws key
-    codes uniformly from all 254 finite E4M3 codes (smaller context)."""
-    P = 65536 if variant == "normal" else 4096
+    values INT8 with one FP32 scale per (token, head)."""
+    P = 65536
     rows, live, Hq, Hkv, D = 16, 16, 24, 4, 128
-    g = synth.gen(5000 + (0 if variant == "normal" else 1))
+    g = synth.gen(5000)
     parent = synth.random_tree(rows, g)
     cap = P + rows + 64
     hi = P + live
     q = synth.normal_bf16((rows, Hq, D), g)
-    if variant == "normal":
-        k_raw = synth.normal_f32((Hkv, hi, D), g).double().numpy()
-        k_codes = ocodec.e4m3_encode(ocodec.wht(k_raw))
-    else:
-        finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
-        idx = torch.randint(0, len(finite), (Hkv, hi, D), generator=g).numpy()
-        k_codes = finite[idx]
+    k_raw = synth.normal_f32((Hkv, hi, D), g).double().numpy()
+    k_codes = ocodec.e4m3_encode(ocodec.wht(k_raw))
     v_raw = synth.normal_f32((Hkv, hi, D), g).double().numpy()
     v_codes, v_sc = ocodec.i8_encode(v_raw)
     k_store = torch.full((Hkv, cap, D), 0x7F, dtype=torch.uint8)       # NaN codes beyond the extent
@@ -275,11 +268,8 @@ def test_config5_quantized_tree(variant):
     k_store[:, :hi] = torch.from_numpy(k_codes)
     v_store[:, :hi] = torch.from_numpy(v_codes)
     sc_store[:, :hi] = torch.from_numpy(v_sc)
-    # all_codes: keys reach +-448, so a smaller score scale keeps the softmax
-    # away from ties that the bf16 rounding of q' could flip
-    scale = 1 / math.sqrt(D) if variant == "normal" else 1 / (32 * math.sqrt(D))
     plan = plan_for(rows, live, Hq, Hkv, D, "tree", kv_fmt="e4m3_wht_i8", prefix_len=P, parent=parent,
-                    kv_capacity=cap, scale=scale)
+                    kv_capacity=cap, scale=1 / math.sqrt(D))
     out, lse, ws = run(plan, q.to(DEV), k_store.to(DEV), v_store.to(DEV), None, sc_store.to(DEV))
     k_dec = ocodec.e4m3_decode(k_codes)
     v_dec = ocodec.i8_decode(v_codes, v_sc)
@@ -287,7 +277,62 @@ def test_config5_quantized_tree(variant):
     p = Problem("tree", rows, live, prefix_len=P, parent=parent)
     ro, rl = oattn.verify_attn_ref(p, q_rot, oattn.Cache(k_dec, v_dec), plan.problem.scale)
     bound = TOL_LSE + _q_rounding_bound(q_rot, k_dec, plan.problem.scale, hi)
-    check(out, lse, ro, rl, live, f"config5 {variant} S={plan.splits}", lse_tol=bound)
+    check(out, lse, ro, rl, live, f"config5 S={plan.splits}", lse_tol=bound)
+
+
+@pytest.mark.parametrize("call", [0, 1, 2])
+def test_quantized_decode_every_code(call):
+    """Every finite E4M3 key code and every INT8 value through the kernel.
+
+    A star tree over an empty prefix makes row r see key r alone.  Query
+    q = H[:, i] / 8 (exact in bf16) rotates to sqrt(2) e_i, so row r, head h
+    reads one coordinate i of its key: lse = scale * sqrt(2) * decode(code),
+    up to the bf16 rounding of sqrt(2) (relative 2^-8); a wrong decode is off
+    by at least one E4M3 step (relative 2^-3).  Values carry scale 1, so the
+    output equals the INT8 codes exactly."""
+    rows, Hq, Hkv, D = 16, 6, 1, 128
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.int64)
+    H = ocodec.hadamard(D)
+    # coordinate read by (row r, head h), and the code placed there
+    coord = np.zeros((rows, Hq), dtype=np.int64)
+    k_codes = np.zeros((Hkv, rows + 64, D), dtype=np.uint8)
+    rng = np.random.default_rng(40 + call)
+    k_codes[:, :rows] = rng.choice(finite, size=(Hkv, rows, D)).astype(np.uint8)
+    q = np.zeros((rows, Hq, D))
+    want = []
+    for r in range(rows):
+        for h in range(Hq):
+            idx = call * rows * Hq + r * Hq + h
+            i = (7 * idx + call) % D
+            coord[r, h] = i
+            k_codes[0, r, i] = finite[idx % len(finite)]
+            want.append(finite[idx % len(finite)])
+            q[r, h] = H[:, i] / 8.0
+    if call == 2:
+        assert set(want) | set(finite[:2 * rows * Hq]) >= set(finite.tolist())
+    v_codes = np.zeros((Hkv, rows + 64, D), dtype=np.int8)
+    v_codes[0, :rows] = ((np.arange(rows * D).reshape(rows, D) + 37 * call) % 255 - 127).astype(np.int8)
+    v_sc = np.ones((Hkv, rows + 64), dtype=np.float32)
+    parent = [-1] * rows
+    plan = plan_for(rows, rows, Hq, Hkv, D, "tree", kv_fmt="e4m3_wht_i8", prefix_len=0, parent=parent,
+                    kv_capacity=rows + 64, scale=0.01)
+    qt = torch.from_numpy(q).to(torch.bfloat16)
+    assert torch.equal(qt.double(), torch.from_numpy(q))              # q is exact in bf16
+    out, lse, ws = run(plan, qt.to(DEV), torch.from_numpy(k_codes).to(DEV), torch.from_numpy(v_codes).to(DEV),
+                       None, torch.from_numpy(v_sc).to(DEV))
+    # values: exact
+    o = out.double().numpy()
+    for r in range(rows):
+        for h in range(Hq):
+            assert np.array_equal(o[r, h], v_codes[0, r].astype(np.float64)), (r, h)
+    # keys: lse against scale * sqrt(2) * decoded code
+    dec = ocodec.e4m3_decode(k_codes[0, :rows])
+    l = lse.double().numpy()
+    for r in range(rows):
+        for h in range(Hq):
+            ref = 0.01 * math.sqrt(2.0) * dec[r, coord[r, h]]
+            tol = 1e-5 + abs(ref) * 2.0 ** -8
+            assert abs(l[r, h] - ref) <= tol, (r, h, k_codes[0, r, coord[r, h]], l[r, h], ref)
 
 
 # ----------------------------------------------------------------------------- exact gates
