@@ -1,11 +1,12 @@
 // Multi-row speculative-verification decode attention for gfx950 (CDNA4).
 //
 // Kernels:
-//   split_kernel    one workgroup per (split, KV head); four wave64s stream the
-//                   split's 32-key chunks, each wave keeping its own online
-//                   softmax state; QK^T and PV run on MFMA 16x16x32 bf16 with
-//                   FP32 accumulation; the waves merge through LDS and write
-//                   one partial (m, l, O) per matrix row.
+//   split_kernel    one workgroup per (split, KV head); one wave64 per 16
+//                   query matrix rows walks the split's 32-key chunks, which
+//                   a producer wave streams into a ring of LDS stages by LDS
+//                   DMA; QK^T and PV run on MFMA 16x16x32 bf16 with FP32
+//                   accumulation; each wave writes its rows' partials
+//                   (m, l, O) directly.
 //   combine_kernel  one workgroup per (row, query head, 64-wide slice of D):
 //                   LSE merge of the partials plus the sink, with the partial
 //                   loads issued together into four independent FP32 chains.
@@ -47,9 +48,7 @@ typedef float f32x2 __attribute__((__vector_size__(8)));
 
 namespace va_detail {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 32;  // keys per wave step
+constexpr int kChunk = 32;  // keys per step
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
 struct SplitArgs {
@@ -64,6 +63,7 @@ struct SplitArgs {
   int64_t v_scale_head_stride;
   int64_t base;  // absolute position of relative key 0 (= tile_lo * 64)
   int32_t rows, live_rows, group, mrows, q_heads, kv_heads;
+  float inv_group;           // 1 / group (row of matrix row m: (m + 0.5) * inv_group)
   int32_t splits, tiles, tiles_q, tiles_r;  // tiles_q = tiles / splits, tiles_r = tiles % splits
   int32_t rel_lo, rel_hi;    // read extent, relative to base
   int32_t full_lo, full_hi;  // every live row sees these keys (relative)
@@ -91,17 +91,23 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the lanes that share
+// lane % 16), on the VALU: v_permlane32_swap pairs each lane with lane ^ 32,
+// v_permlane16_swap with lane ^ 16 (each returns the lane's own value in one
+// output and its partner's in the other).  Every lane gets the same result
+// (IEEE max and + are commutative).
 __device__ __forceinline__ float wave_max16x4(float x) {
-  // max over the four lanes that share lane % 16
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum16x4(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -143,310 +149,319 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel.
-//   D     head dim (64 or 128)
-//   NBW   16-row blocks of query matrix rows per wave (1..3)
-//   RG    row groups per workgroup (1: all four waves hold every row and
-//         stream different chunks; 2: wave pairs share a chunk, each wave
-//         holding half of the rows)
-//   FMT   0 = bf16 K/V; 1 = E4M3FN rotated K, INT8 V with per-key scale
+// Split kernel: one workgroup per (split, KV head) with W + 1 wave64s.
+//   Waves 0..W-1 (consumers): wave w owns query matrix rows [16w, 16w + 16)
+//     for the whole split and keeps their online-softmax state in registers;
+//     every consumer walks all of the split's 32-key chunks in order.
+//   Wave W (producer): fills a ring of NST LDS stages with the chunks' K and
+//     V tiles by LDS DMA, NST - 1 chunks ahead of the consumers.
+// One workgroup barrier per chunk both publishes chunk n (the producer waited
+// for its DMA just before) and frees the stage of chunk n - 1, which the
+// producer refills right after.  No cross-wave merge: each wave writes its
+// own rows' partials.
+//   D    head dim (64 or 128)
+//   W    16-row blocks of query matrix rows (1..6)
+//   FMT  0 = bf16 K/V; 1 = E4M3FN rotated K, INT8 V with per-key scale
+//   NST  LDS stages
 // ---------------------------------------------------------------------------
-template <int D, int NBW, int RG, int FMT>
-__global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
-  constexpr int KS = D / 32;       // QK contraction steps
-  constexpr int MD = D / 16;       // O^T row blocks over d
-  constexpr int STREAMS = kWaves / RG;
-  constexpr int ROWS_W = NBW * 16;
-  // Per-wave staging of one 32-key chunk, filled by LDS DMA: the K tile and
-  // the V tile, each 32 rows of KROW bytes made of 16-byte pieces, plus (INT8
-  // values) the chunk's scales.  Two such buffers per wave: the next chunk
-  // streams in while the current one is computed.
-  constexpr int KROW = FMT == 0 ? D * 2 : D;    // bytes per key row
-  constexpr int PIECES = KROW / 16;             // 16-byte pieces per row
-  constexpr int RPI = 64 / PIECES;              // rows per DMA instruction (1 KiB)
-  constexpr int NDMA = kChunk / RPI;            // DMA instructions per tile
-  constexpr int kTileB = kChunk * KROW;
-  constexpr int kScaleB = FMT == 1 ? 256 : 0;
-  constexpr int kBufB = 2 * kTileB + kScaleB;
-  constexpr int kStageBytes = kWaves * 2 * kBufB;
+template <int D, int FMT>
+struct StageGeom {
+  static constexpr int KROW = FMT == 0 ? D * 2 : D;      // bytes per key row
+  static constexpr int PIECES = KROW / 16;               // 16-byte pieces per row
+  static constexpr int RPI = 64 / PIECES;                // rows per DMA instruction (1 KiB)
+  static constexpr int NDMA = kChunk / RPI;              // DMA instructions per tile
+  static constexpr int kTileB = kChunk * KROW;
+  static constexpr int kScaleB = FMT == 1 ? 256 : 0;
+  static constexpr int kStageB = 2 * kTileB + kScaleB;
+  static constexpr int kVm = 2 * NDMA + (FMT == 1 ? 1 : 0);  // DMA instructions per chunk
+};
 
-  // LDS layout: [Q tile | staging | FP32 WHT scratch (quantised keys only)];
-  // the cross-wave merge overlays the Q tile and staging after the loop.
-  constexpr int QROWS = 16 * NBW * RG;               // padded query matrix rows
-  constexpr int kQT = QROWS * D * 2;                 // bf16 Q tile
-  constexpr int kWHT = FMT == 1 ? VA_MAX_MATRIX_ROWS * 128 * 4 : 0;
-  constexpr int kMergeBytes = kWaves * ROWS_W * D * 4;  // every wave's O^T tile
-  constexpr int kLoop = kQT + kStageBytes + kWHT;    // WHT scratch may not overlay early DMA
-  constexpr int kBig = kLoop > kMergeBytes ? kLoop : kMergeBytes;
-  constexpr int kML = kWaves * ROWS_W * 3 * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kBig + kML];
-  uint16_t *qt = (uint16_t *)smem;  // [QROWS][D], 16-byte pieces XOR-swizzled by (row & 15)
+// s_waitcnt vmcnt(KV * k) for a run-time k in [0, K] (the count is an
+// immediate, so each value has its own instruction).
+template <int KV, int K>
+__device__ __forceinline__ void wait_chunks(int k) {
+  if constexpr (K > 0) {
+    if (k >= K) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KV * K) : "memory");
+      return;
+    }
+    wait_chunks<KV, K - 1>(k);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Kernel arguments live in memory and reach SGPRs through scalar loads; the
+// compiler issues each load where the value is first needed, so arguments
+// used in different places cost separate round trips.  Naming every argument
+// in an empty asm statement at the kernel's entry makes all of those loads
+// issue together, in one round trip.
+__device__ __forceinline__ void pin(int32_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(int64_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
+
+template <int D, int W, int FMT, int NST>
+__global__ __launch_bounds__(64 * (W + 1)) void split_kernel(const SplitArgs a) {
+  using G = StageGeom<D, FMT>;
+  constexpr int KS = D / 32;  // QK contraction steps
+  constexpr int MD = D / 16;  // O^T row blocks over d
+  constexpr int KROW = G::KROW, PIECES = G::PIECES, RPI = G::RPI, NDMA = G::NDMA;
+  constexpr int kTileB = G::kTileB, kStageB = G::kStageB, kVm = G::kVm;
+  static_assert(NST >= 2 && (NST - 2) * kVm <= 63, "vmcnt counts at most 63 loads");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * kStageB];
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps chunk indices and mask decisions in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15;
   const int g4 = lane >> 4;
-  const int rg = wave % RG;
-  const int stream = wave / RG;
-
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
 
   // ---------------- this split's chunk range ----------------
-  // Everything the first DMA needs is read here, in straight-line code, so
-  // the kernel-argument loads issue together.
+  // split s takes q + 1 tiles if s < r, else q (q = T / S, r = T % S)
   const int32_t tq = a.tiles_q, tr = a.tiles_r, rel_lo = a.rel_lo, rel_hi = a.rel_hi;
   const int32_t ring_slots = a.ring_slots, ring_base = a.ring_base_slot;
   const int64_t kv_base = a.base, row_stride = a.kv_row_stride_b, head_stride = a.kv_head_stride_b;
-  const uint8_t *kbase = a.k + (int64_t)kvh * head_stride;
-  const uint8_t *vbase = a.v + (int64_t)kvh * head_stride;
-  // split s takes q + 1 tiles if s < r, else q (q = T / S, r = T % S)
-  const int32_t t0 = split * tq + (split < tr ? split : tr);
-  const int32_t t1 = t0 + tq + (split < tr ? 1 : 0);
-  int32_t c_first = 2 * t0, c_last = 2 * t1;  // in 32-key chunks, relative
-  if (c_first < rel_lo / kChunk) c_first = rel_lo / kChunk;
-  const int32_t c_end_ext = (rel_hi + kChunk - 1) / kChunk;
-  if (c_last > c_end_ext) c_last = c_end_ext;
-  const int32_t nchunks = c_last > c_first ? c_last - c_first : 0;
-  // chunks handled by this wave: c_first + stream + STREAMS * n
-  const int32_t my_n = nchunks > stream ? (nchunks - stream + STREAMS - 1) / STREAMS : 0;
-
-  uint8_t *stage = smem + kQT + wave * 2 * kBufB;
-
-  // A chunk never straddles the ring's wrap (slots are 64-aligned), so every
-  // key of chunk c0 lives at row_of(c0) + (j - c0): one scalar base per chunk
-  // plus a 32-bit lane offset.  Keys outside [rel_lo, rel_hi) are clamped to
-  // the extent's ends (read, then masked), so nothing outside it is read.
-  const uint32_t ring_div = ring_slots > 0 ? (uint32_t)ring_slots : 1u;
-  auto chunk_row = [&](int32_t c0) -> int64_t {
-    const int64_t ring_row = (int64_t)(((uint32_t)ring_base + (uint32_t)c0) % ring_div);
-    return ring_slots ? ring_row : kv_base + c0;
-  };
-  auto clampx = [&](int32_t x, int32_t c0) -> int32_t {
-    const int32_t lo = rel_lo - c0, hi = rel_hi - 1 - c0;
-    return x < lo ? lo : (x > hi ? hi : x);
-  };
-  const uint32_t rs = (uint32_t)row_stride;
-
-  // Piece swizzles inside the staged tiles (position = piece ^ f(row)):
-  //   K: f = row % PIECES -> the 16 lanes reading one A operand (16 keys,
-  //      same piece) hit 16 different positions.
-  //   V (bf16): f = 2 * (row % (PIECES/2)), an even value, so a pair of
-  //      pieces {2k, 2k+1} stays a pair; the 16 rows of one transpose read
-  //      spread over all bank groups.  V (INT8) is read bytewise, unswizzled.
-  auto fk = [](int row) { return row & (PIECES - 1); };
-  auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
-
-  // Issue the LDS DMA of chunk n into buffer `buf` (lane l of instruction t
-  // stores 16 bytes at tile + 1024*t + 16*l).  Interior chunks use per-lane
-  // byte offsets computed once (row * stride + swizzled piece) on top of the
-  // chunk's scalar base; only a chunk that crosses the extent's ends clamps
-  // its rows.
-  uint32_t koff[NDMA], voff[NDMA];
+  const uint8_t *kptr = a.k, *vptr = a.v;
+  const float *vsc = a.v_scale;
+  const int64_t vsc_stride = a.v_scale_head_stride;
+  const float inv_group = a.inv_group, scale_log2 = a.scale_log2;
+  const int32_t mrows = a.mrows, live_rows = a.live_rows, group = a.group, q_heads = a.q_heads;
+  const int32_t tree = a.tree, tree_lo = a.tree_lo, t0_rel = a.t0_rel, window = a.window;
+  const int32_t full_lo = a.full_lo, full_hi = a.full_hi, kv_heads = a.kv_heads;
+  const uint8_t *qptr = a.q;
+  float *ws_ml = a.ws_ml, *ws_o = a.ws_o;
+  uint32_t anc[VA_MAX_ROWS];
 #pragma unroll
-  for (int t = 0; t < NDMA; ++t) {
-    const int row = t * RPI + lane / PIECES;
-    const int pos = lane % PIECES;
-    koff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ fk(row));
-    voff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ fv(row));
-  }
-  auto chunk_ptrs = [&](int32_t n, const uint8_t *base) -> const uint8_t * {
-    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
-    return base + chunk_row(c0) * row_stride;
+  for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = a.anc[i];
+  pin(tq), pin(tr), pin(rel_lo), pin(rel_hi), pin(ring_slots), pin(ring_base), pin(kv_base);
+  pin(row_stride), pin(head_stride), pin(kptr), pin(vptr);
+  if constexpr (FMT == 1) pin(vsc), pin(vsc_stride);
+  pin(inv_group), pin(scale_log2), pin(mrows), pin(live_rows), pin(group), pin(q_heads), pin(tree);
+  pin(tree_lo), pin(t0_rel), pin(window), pin(full_lo), pin(full_hi), pin(kv_heads), pin(qptr);
+  pin(ws_ml), pin(ws_o);
+#pragma unroll
+  for (int i = 0; i < VA_MAX_ROWS; ++i) pin(anc[i]);
+
+  int32_t c_first = 0, nch = 0;
+  auto chunk_range = [&]() {
+    const int32_t t0 = split * tq + (split < tr ? split : tr);
+    const int32_t t1 = t0 + tq + (split < tr ? 1 : 0);
+    int32_t c0 = 2 * t0, c1 = 2 * t1;  // in 32-key chunks, relative
+    if (c0 < rel_lo / kChunk) c0 = rel_lo / kChunk;
+    const int32_t c_end_ext = (rel_hi + kChunk - 1) / kChunk;
+    if (c1 > c_end_ext) c1 = c_end_ext;
+    c_first = c0;
+    nch = c1 > c0 ? c1 - c0 : 0;
   };
-  // K group of chunk n: NDMA instructions into K buffer `buf`.
-  auto issueK = [&](int32_t n, int buf) {
-    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
-    const uint8_t *kc = chunk_ptrs(n, kbase);
-    uint8_t *kt = stage + buf * kBufB;
-    if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
+
+  if (wave == W) {
+    // ================= producer =================
+    chunk_range();
+    const uint8_t *kbase = kptr + (int64_t)kvh * head_stride;
+    const uint8_t *vbase = vptr + (int64_t)kvh * head_stride;
+    const uint32_t rs = (uint32_t)row_stride;
+    // A chunk never straddles the ring's wrap (slots are 64-aligned), so every
+    // key of chunk c0 lives at row_of(c0) + (j - c0): one scalar base per
+    // chunk plus a 32-bit lane offset.  Keys outside [rel_lo, rel_hi) are
+    // clamped to the extent's ends (read, then masked), so nothing outside it
+    // is read.
+    const uint32_t ring_div = ring_slots > 0 ? (uint32_t)ring_slots : 1u;
+    auto chunk_row = [&](int32_t c0) -> int64_t {
+      const int64_t ring_row = (int64_t)(((uint32_t)ring_base + (uint32_t)c0) % ring_div);
+      return ring_slots ? ring_row : kv_base + c0;
+    };
+    auto clampx = [&](int32_t x, int32_t c0) -> int32_t {
+      const int32_t lo = rel_lo - c0, hi = rel_hi - 1 - c0;
+      return x < lo ? lo : (x > hi ? hi : x);
+    };
+    // Piece swizzles inside the staged tiles (position = piece ^ f(row)):
+    //   K: f = row % PIECES -> the 16 lanes reading one A operand (16 keys,
+    //      same piece) hit 16 different positions.
+    //   V (bf16): f = 2 * (row % (PIECES/2)), an even value, so a pair of
+    //      pieces {2k, 2k+1} stays a pair; the 16 rows of one transpose read
+    //      spread over all bank groups.  V (INT8) is read bytewise, unswizzled.
+    uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
-      for (int t = 0; t < NDMA; ++t) dma16(kc + koff[t], kt + 1024 * t);
-    } else {
+    for (int t = 0; t < NDMA; ++t) {
+      const int row = t * RPI + lane / PIECES;
+      const int pos = lane % PIECES;
+      koff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ (row & (PIECES - 1)));
+      voff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ (FMT == 0 ? (2 * row) & (PIECES - 2) : 0));
+    }
+    // Chunk n into stage `st`: lane l of instruction t stores 16 bytes at
+    // tile + 1024*t + 16*l.  Issue order per chunk: K tile, V tile, scales.
+    auto issue = [&](int32_t n, int st) {
+      const int32_t c0 = (c_first + n) * kChunk;
+      const int64_t row0 = chunk_row(c0);
+      const uint8_t *kc = kbase + row0 * row_stride;
+      const uint8_t *vc = vbase + row0 * row_stride;
+      uint8_t *kt = smem + st * kStageB;
+      uint8_t *vt = kt + kTileB;
+      if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
 #pragma unroll
-      for (int t = 0; t < NDMA; ++t) {
-        const int row = t * RPI + lane / PIECES;
-        const int pos = lane % PIECES;
-        dma16(kc + (uint32_t)clampx(row, c0) * rs + 16 * (pos ^ fk(row)), kt + 1024 * t);
+        for (int t = 0; t < NDMA; ++t) dma16(kc + koff[t], kt + 1024 * t);
+#pragma unroll
+        for (int t = 0; t < NDMA; ++t) dma16(vc + voff[t], vt + 1024 * t);
+      } else {
+#pragma unroll
+        for (int t = 0; t < NDMA; ++t) {
+          const int row = t * RPI + lane / PIECES;
+          const uint32_t x = (uint32_t)clampx(row, c0) * rs;
+          dma16(kc + x + (koff[t] - (uint32_t)row * rs), kt + 1024 * t);
+        }
+#pragma unroll
+        for (int t = 0; t < NDMA; ++t) {
+          const int row = t * RPI + lane / PIECES;
+          const uint32_t x = (uint32_t)clampx(row, c0) * rs;
+          dma16(vc + x + (voff[t] - (uint32_t)row * rs), vt + 1024 * t);
+        }
       }
-    }
-  };
-  // V group of chunk n: NDMA instructions (+1 for the INT8 scales) into V buffer `buf`.
-  auto issueV = [&](int32_t n, int buf) {
-    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
-    const uint8_t *vc = chunk_ptrs(n, vbase);
-    uint8_t *vt = stage + buf * kBufB + kTileB;
-    if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
-#pragma unroll
-      for (int t = 0; t < NDMA; ++t) dma16(vc + voff[t], vt + 1024 * t);
-    } else {
-#pragma unroll
-      for (int t = 0; t < NDMA; ++t) {
-        const int row = t * RPI + lane / PIECES;
-        const int pos = lane % PIECES;
-        dma16(vc + (uint32_t)clampx(row, c0) * rs + 16 * (pos ^ fv(row)), vt + 1024 * t);
+      if constexpr (FMT == 1) {
+        const float *sc = vsc + (int64_t)kvh * vsc_stride + row0;
+        dma4(sc + clampx(lane & 31, c0), vt + kTileB);
       }
+    };
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+      if (j < nch) issue(j, j);
+    int st_prev = NST - 1;  // stage of chunk n - 1
+    for (int32_t n = 0; n < nch; ++n) {
+      // chunks issued after n: n+1 .. min(n + NST - 2, nch - 1); DMA groups
+      // complete in issue order, so this wait leaves exactly those in flight.
+      const int32_t later = nch - 1 - n;
+      wait_chunks<kVm, NST - 2>(later < NST - 2 ? later : NST - 2);
+      wg_barrier();
+      if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
+      st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
     }
-    if constexpr (FMT == 1) {
-      const float *sc = a.v_scale + (int64_t)kvh * a.v_scale_head_stride + chunk_row(c0);
-      dma4(sc + clampx(lane & 31, c0), vt + kTileB);
-    }
-  };
-
-  // The first two chunks start streaming before anything else is set up
-  // (issue order K0 V0 K1 V1; later groups follow the per-step order below).
-  if (my_n > 0) {
-    issueK(0, 0);
-    issueV(0, 0);
-  }
-  if (my_n > 1) {
-    issueK(1, 1);
-    issueV(1, 1);
+    return;
   }
 
-  // ---------------- Q tile in LDS (B operand of S^T = K Q^T) ----------------
-  // Piece p (8 contraction elements) of matrix row m is stored at position
-  // p ^ (m % QP), so the lanes reading one operand spread over the banks.
-  // Loads are unconditional (padded rows read row 0 and are zeroed), so they
-  // all issue before the first wait.
-  constexpr int QP = D / 8;  // pieces per row
+  // ================= consumers =================
+  chunk_range();
+
+  // lane column i16 of this wave is query matrix row m = 16*wave + i16 =
+  // r*G + (h - kvh*G); live matrix rows are [0, live_rows * G).
+  const int m = 16 * wave + i16;
+  const int r = (int)(((float)m + 0.5f) * inv_group);  // m / G: exact for every m < 96, G <= 96
+  const bool row_ok = (m < mrows) && (r < live_rows);
+  const bool active = 16 * wave < live_rows * group;  // wave-uniform
+  const int rr = row_ok ? r : 0;
+  const int h = kvh * group + (row_ok ? m - r * group : 0);
+  const uint8_t *qrow = qptr + (int64_t)(rr * q_heads + h) * D * 2;
+
+  // ---------------- Q^T operands (B operand of S^T = K Q^T) ----------------
+  // lane (i16, g4) holds row m, contraction piece 4*ks + g4 of step ks.
+  bf16x8 qop[KS];
   if constexpr (FMT == 0) {
-    constexpr int kIt = (QROWS * QP + kThreads - 1) / kThreads;
-    u32x4 qv[kIt];
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int idx = threadIdx.x + it * kThreads;
-      const int m = idx / QP, pc = idx % QP;
-      const int r = m / a.group;
-      const bool ok = (idx < QROWS * QP) && (m < a.mrows) && (r < a.live_rows);
-      const int rr = ok ? r : 0, h = ok ? kvh * a.group + (m - r * a.group) : 0;
-      qv[it] = *(const u32x4 *)(a.q + ((int64_t)(rr * a.q_heads + h) * D + 8 * (ok ? pc : 0)) * 2);
-      if (!ok) qv[it] = (u32x4){0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = *(const u32x4 *)(qrow + (32 * ks + 8 * g4) * 2);
+      if (!row_ok) w = (u32x4){0u, 0u, 0u, 0u};
+      qop[ks] = __builtin_bit_cast(bf16x8, w);
     }
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int idx = threadIdx.x + it * kThreads;
-      const int m = idx / QP, pc = idx % QP;
-      if (idx < QROWS * QP) *(u32x4 *)(qt + m * D + 8 * (pc ^ (m & (QP - 1)))) = qv[it];
-    }
-    __syncthreads();
   } else {
     // q' = H q / sqrt(128) in FP32 (natural-order Walsh-Hadamard), then bf16.
-    float *qs = (float *)(smem + kQT + kStageBytes);
-    const int nrows = a.mrows;
-    for (int idx = threadIdx.x; idx < nrows * 128; idx += kThreads) {
-      const int m = idx >> 7, d = idx & 127;
-      const int r = m / a.group;
-      const bool ok = r < a.live_rows;
-      const int rr = ok ? r : 0, h = ok ? kvh * a.group + (m - r * a.group) : 0;
-      const uint16_t u = *(const uint16_t *)(a.q + ((int64_t)(rr * a.q_heads + h) * 128 + d) * 2);
-      qs[idx] = ok ? __uint_as_float((uint32_t)u << 16) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int hstep = 1; hstep < 128; hstep <<= 1) {
-      for (int idx = threadIdx.x; idx < nrows * 64; idx += kThreads) {
-        const int m = idx >> 6, kk = idx & 63;
-        const int i0 = (kk / hstep) * 2 * hstep + (kk % hstep);
-        float *row = qs + m * 128;
-        const float x0 = row[i0], x1 = row[i0 + hstep];
-        row[i0] = x0 + x1;
-        row[i0 + hstep] = x0 - x1;
-      }
-      __syncthreads();
-    }
-    const float inv = 0.08838834764831845f;  // 1/sqrt(128)
-    // Quantised keys use the contraction order: contraction piece p (8
-    // elements) holds d = 64*(p/8) + 16*(p%4) + 8*((p/4)%2) + e, so that one
-    // 16-byte load of E4M3 codes (d0..d0+15) serves two contraction steps.
-    for (int idx = threadIdx.x; idx < QROWS * QP; idx += kThreads) {
-      const int m = idx / QP, pc = idx % QP;
-      const int d0 = 64 * (pc >> 3) + 16 * (pc & 3) + 8 * ((pc >> 2) & 1);
-      uint32_t w[4];
+    // Quantised keys use the contraction order in which piece p holds
+    // d = 64*(p/8) + 16*(p%4) + 8*((p/4)%2) + e, so lane (i16, g4) needs
+    // d = 64*(j/16) + 16*g4 + j%16 for j = 0..31 -- and those 32 values are
+    // closed under the butterflies on d bits 0-3 and 6, which stay in the
+    // lane; d bits 4 and 5 (g4) pair lanes 16 and 32 apart.
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 w = *(const u32x4 *)(qrow + (64 * (c >> 1) + 16 * g4 + 8 * (c & 1)) * 2);
+      if (!row_ok) w = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x0 = 0.f, x1 = 0.f;
-        if (m < nrows) {
-          x0 = qs[m * 128 + d0 + 2 * e] * inv;
-          x1 = qs[m * 128 + d0 + 2 * e + 1] * inv;
-        }
-        w[e] = pack_bf16x2(x0, x1);
+        x[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+        x[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
-      u32x4 wv = {w[0], w[1], w[2], w[3]};
-      *(u32x4 *)(qt + m * D + 8 * (pc ^ (m & (QP - 1)))) = wv;
     }
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {  // d bits 0..3 (butterfly widths 1, 2, 4, 8)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (j & (1 << b)) continue;
+        const float u = x[j], v = x[j | (1 << b)];
+        x[j] = u + v;
+        x[j | (1 << b)] = u - v;
+      }
+    }
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {  // d bits 4, 5 (widths 16, 32)
+      const bool upper = (lane & sh) != 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float p = __shfl_xor(x[j], sh, 64);
+        x[j] = upper ? p - x[j] : x[j] + p;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {  // d bit 6 (width 64)
+      const float u = x[j], v = x[j + 16];
+      x[j] = u + v;
+      x[j + 16] = u - v;
+    }
+    const float inv = 0.08838834764831845f;  // 1/sqrt(128)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * ks + 2 * e] * inv, x[8 * ks + 2 * e + 1] * inv);
+      qop[ks] = __builtin_bit_cast(bf16x8, w);
+    }
   }
-  // B operand for 16-row block nb of this wave, contraction step ks: lane
-  // (i16, g4) holds row 16*(rg*NBW+nb)+i16, contraction piece 4*ks+g4.
-  auto qop = [&](int nb, int ks) -> bf16x8 {
-    const int m = 16 * (rg * NBW + nb) + i16;
-    return __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + m * D + 8 * ((4 * ks + g4) ^ (m & (QP - 1)))));
-  };
 
-  // ---------------- per-lane row geometry for boundary masks ----------------
-  // Computed from scalars (no per-lane loads): causal/window rows from their
-  // position, tree ancestor bits selected from the sixteen kernel arguments.
-  int32_t rlo[NBW], rhi[NBW];
-  uint32_t ranc[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int m = 16 * (rg * NBW + nb) + i16;
-    const int r = m / a.group;
-    const bool ok = (m < a.mrows) && (r < a.live_rows);
+  // ---------------- row geometry for boundary masks ----------------
+  // Chain modes: row r sits at t0_rel + r and sees [max(t0_rel + r - window
+  // + 1, 0), t0_rel + r] (window 0: from 0).  Tree mode: [0, tree_lo) plus
+  // the node keys whose bits are set in anc[r].
+  int32_t rlo, rhi;
+  uint32_t ranc = 0u;
+  {
     int32_t lo_r, hi_r;
-    uint32_t an = 0u;
-    if (a.tree) {
+    if (tree) {
       lo_r = 0;
-      hi_r = a.tree_lo;
+      hi_r = tree_lo;
 #pragma unroll
-      for (int i = 0; i < VA_MAX_ROWS; ++i) an = (r == i) ? a.anc[i] : an;
+      for (int i = 0; i < VA_MAX_ROWS; ++i) ranc = (r == i) ? anc[i] : ranc;
     } else {
-      const int32_t t = a.t0_rel + r;
+      const int32_t t = t0_rel + r;
       hi_r = t + 1;
-      lo_r = a.window ? t - a.window + 1 : INT32_MIN;
+      lo_r = window ? t - window + 1 : 0;
       if (lo_r < 0) lo_r = 0;
     }
-    rlo[nb] = ok ? lo_r : 0;
-    rhi[nb] = ok ? hi_r : 0;
-    ranc[nb] = ok ? an : 0u;
+    rlo = row_ok ? lo_r : 0;
+    rhi = row_ok ? hi_r : 0;
+    ranc = row_ok ? ranc : 0u;
   }
 
   // ---------------- online-softmax state ----------------
-  f32x4 o[MD][NBW];
-  float mref[NBW], mtrue[NBW], lrow[NBW];
+  f32x4 o[MD];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    mref[nb] = -INFINITY;
-    mtrue[nb] = -INFINITY;
-    lrow[nb] = 0.f;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) o[md][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int md = 0; md < MD; ++md) o[md] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float mref = -INFINITY, mtrue = -INFINITY, lrow = 0.f;
 
-  // DMA groups complete in issue order (vector-memory operations return in
-  // order and only this wave's DMA is in flight), so a wait leaves exactly
-  // the groups issued after the one needed.  Per step n the issue order is:
-  // [wait K(n)] K(n+2) [wait V(n)] V(n+2).  The compiler does not track LDS
-  // written by DMA across loop iterations, hence the explicit waits; their
-  // memory clobber keeps the LDS reads below them.
-  constexpr int kVmK = NDMA;
-  constexpr int kVmV = NDMA + (FMT == 1 ? 1 : 0);
+  // Swizzles of the staged tiles (must match the producer's).
+  auto fk = [](int row) { return row & (PIECES - 1); };
+  auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
 
-  auto step = [&](int32_t n) {
-    const int buf = n & 1;
-    const int32_t c0 = (c_first + stream + STREAMS * n) * kChunk;
-    const uint8_t *kt = stage + buf * kBufB;
+  auto step = [&](int32_t n, const uint8_t *kt) {
     const uint8_t *vt = kt + kTileB;
-    const bool more1 = n + 1 < my_n, more2 = n + 2 < my_n;
+    const int32_t c0 = (c_first + n) * kChunk;
 
-    // ---- K(n): after it were issued V(n), and K(n+1), V(n+1) if they exist ----
-    if (more1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmV + kVmK + kVmV) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmV) : "memory");
-    }
+    // ---- K operands: A operand of block mb is keys 16*mb + i16 ----
     bf16x8 kop[2][KS];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -472,83 +487,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
         }
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (more2) issueK(n + 2, buf);
-
-    // ---- S^T = K Q^T ----
-    f32x4 s[2][NBW];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16(kop[mb][ks], qop(nb, ks), acc);
-        s[mb][nb] = acc;
-      }
-
-    // ---- scale, boundary mask, row maxima ----
-    const bool full = (c0 >= a.full_lo) && (c0 + kChunk <= a.full_hi);
-    float xs[NBW][8], xmax[NBW];
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      float *x = xs[nb];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * mb + e] = s[mb][nb][e] * a.scale_log2;
-      if (!full) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          // branch-free: row interval, or (tree) an ancestor-or-self node key
-          const int32_t j = c0 + (t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4));
-          const uint32_t in_row = (uint32_t)(j - rlo[nb]) < (uint32_t)(rhi[nb] - rlo[nb]);
-          const uint32_t ti = (uint32_t)(j - a.tree_lo);
-          const uint32_t in_tree = (uint32_t)(ti < 16u) & (ranc[nb] >> (ti & 15u));
-          x[t] = ((in_row | in_tree) & 1u) ? x[t] : -INFINITY;
-        }
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
-      xmax[nb] = wave_max16x4(mx);
-    }
-
-    // ---- lazy reference maximum ----
-    // Exponents are taken against mref, which moves only when a row's chunk
-    // maximum exceeds it by more than kTau (so every p stays <= 2^kTau);
-    // moving it rescales that row's O and l (a rare, wave-uniform branch).
-    bool need = false;
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      mtrue[nb] = fmaxf(mtrue[nb], xmax[nb]);
-      need |= (mref[nb] != -INFINITY) && (xmax[nb] > mref[nb] + kTau);
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const bool mv = xmax[nb] > mref[nb] + kTau;
-        const float nref = mv ? xmax[nb] : mref[nb];
-        const float alpha = (mref[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref[nb] - nref);
-        lrow[nb] *= alpha;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[md][nb] *= alpha;
-        mref[nb] = nref;
-      }
-    }
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) mref[nb] = (mref[nb] == -INFINITY) ? xmax[nb] : mref[nb];
-
-    // ---- V(n): after it were issued K(n+1), V(n+1), K(n+2) if they exist ----
-    if (more2) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmK + kVmV + kVmK) : "memory");
-    } else if (more1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kVmK + kVmV) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    // V^T operand for block md: lane (i16 = d within the block, g4) takes the
-    // keys {4g..4g+3, 16+4g..16+4g+3} of column d.
+    // ---- V^T operands: lane (i16 = d within block md, g4) takes the keys
+    //      {4g..4g+3, 16+4g..16+4g+3} of column d ----
     bf16x8 vop[MD];
     float vs[8];
     if constexpr (FMT == 0) {
@@ -581,126 +521,146 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const SplitArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) vs[t] = sct[t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4)];
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (more2) issueV(n + 2, buf);
 
-    // ---- P^T (B operand of PV) and l ----
-    uint32_t pb[NBW][4];
+    // ---- S^T = K Q^T ----
+    f32x4 s[2];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const float m_use = (mref[nb] == -INFINITY) ? 0.f : mref[nb];
-      float p[8], psum = 0.f;
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16(kop[mb][ks], qop[ks], acc);
+      s[mb] = acc;
+    }
+
+    // ---- scale, boundary mask, row maximum ----
+    float x[8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * mb + e] = s[mb][e] * scale_log2;
+    if (!(c0 >= full_lo && c0 + kChunk <= full_hi)) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        p[t] = __builtin_amdgcn_exp2f(xs[nb][t] - m_use);
-        psum += p[t];
+        // branch-free: row interval, or (tree) an ancestor-or-self node key
+        const int32_t j = c0 + (t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4));
+        const uint32_t in_row = (uint32_t)(j - rlo) < (uint32_t)(rhi - rlo);
+        const uint32_t ti = (uint32_t)(j - tree_lo);
+        const uint32_t in_tree = (uint32_t)(ti < 16u) & (ranc >> (ti & 15u));
+        x[t] = ((in_row | in_tree) & 1u) ? x[t] : -INFINITY;
       }
-      lrow[nb] += psum;
-      if constexpr (FMT == 1) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) p[t] *= vs[t];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pb[nb][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
     }
+    float mx = x[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
+    mx = wave_max16x4(mx);
+
+    // ---- lazy reference maximum ----
+    // Exponents are taken against mref, which moves only when a row's chunk
+    // maximum exceeds it by more than kTau (so every p stays <= 2^kTau);
+    // moving it rescales that row's O and l (a rare, wave-uniform branch).
+    mtrue = fmaxf(mtrue, mx);
+    const bool need = (mref != -INFINITY) && (mx > mref + kTau);
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float nref = need ? mx : mref;
+      const float alpha = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - nref);
+      lrow *= alpha;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md] *= alpha;
+      mref = nref;
+    }
+    mref = (mref == -INFINITY) ? mx : mref;
+
+    // ---- P^T (B operand of PV) and l ----
+    const float m_use = (mref == -INFINITY) ? 0.f : mref;
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      p[t] = __builtin_amdgcn_exp2f(x[t] - m_use);
+      psum += p[t];
+    }
+    lrow += psum;
+    if constexpr (FMT == 1) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) p[t] *= vs[t];
+    }
+    u32x4 pw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        u32x4 pw = {pb[nb][0], pb[nb][1], pb[nb][2], pb[nb][3]};
-        o[md][nb] = mfma16(vop[md], __builtin_bit_cast(bf16x8, pw), o[md][nb]);
-      }
+    for (int md = 0; md < MD; ++md) o[md] = mfma16(vop[md], pb, o[md]);
   };
 
-  for (int32_t n = 0; n < my_n; ++n) step(n);
-
-  // ---------------- merge the streams of each row group ----------------
-  // Each wave publishes, per row, its exponent reference, its true maximum and
-  // its l, plus its unnormalised O^T tile.  Then every wave of a row group
-  // merges a 1/STREAMS share of the d blocks against the split's true
-  // maximum M (weight 2^(ref_w - M) per wave) and stores it.
-  __syncthreads();  // every wave has left its loop: the staging area is free
-  float *sml = (float *)(smem + kBig);  // [wave][ROWS_W][3]: ref, true max, l
-  f32x4 *otile = (f32x4 *)smem;         // [wave][MD][NBW][64 lanes]
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const float lt = wave_sum16x4(lrow[nb]);
-    if (g4 == 0) {
-      float *e = sml + (wave * ROWS_W + nb * 16 + i16) * 3;
-      e[0] = mref[nb];
-      e[1] = mtrue[nb];
-      e[2] = lt;
-    }
-#pragma unroll
-    for (int md = 0; md < MD; ++md) otile[((wave * MD + md) * NBW + nb) * 64 + lane] = o[md][nb];
+  int st = 0;  // stage of chunk n
+  for (int32_t n = 0; n < nch; ++n) {
+    wg_barrier();  // chunk n is in LDS; every consumer has left chunk n - 1
+    if (active) step(n, smem + st * kStageB);
+    st = st + 1 == NST ? 0 : st + 1;
   }
-  __syncthreads();
 
-  constexpr int MPW = MD / STREAMS;  // d blocks merged and stored by each wave
-  const int64_t unit0 = ((int64_t)split * a.kv_heads + kvh) * a.mrows;
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int row = nb * 16 + i16;
-    float M = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < STREAMS; ++st) M = fmaxf(M, sml[((st * RG + rg) * ROWS_W + row) * 3 + 1]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float f[STREAMS], L = 0.f;
-#pragma unroll
-    for (int st = 0; st < STREAMS; ++st) {
-      const float *e = sml + ((st * RG + rg) * ROWS_W + row) * 3;
-      f[st] = (e[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(e[0] - Mu);
-      L += f[st] * e[2];
+  // ---------------- partials of this wave's rows ----------------
+  // Normalised to the true maximum M of the split: m = M, l = sum 2^(x - M),
+  // O = sum 2^(x - M) v.
+  if (m < mrows) {
+    const float lt = wave_sum16x4(lrow);
+    const float f = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - mtrue);
+    const int64_t unit = ((int64_t)split * kv_heads + kvh) * mrows + m;
+    if (g4 == 0) {
+      *(f32x2 *)(ws_ml + unit * 2) = row_ok ? (f32x2){mtrue, lt * f} : (f32x2){-INFINITY, 0.f};
     }
-    const int m = 16 * (rg * NBW + nb) + i16;
-    if (m < a.mrows) {
-      const int r = m / a.group;
-      const bool live = r < a.live_rows;
-      if (stream == 0 && g4 == 0) {
-        a.ws_ml[(unit0 + m) * 2 + 0] = live ? M : -INFINITY;
-        a.ws_ml[(unit0 + m) * 2 + 1] = live ? L : 0.f;
-      }
-      float *op = a.ws_o + (unit0 + m) * D;
+    float *op = ws_o + unit * D;
+    const float fo = row_ok ? f : 0.f;
 #pragma unroll
-      for (int mi = 0; mi < MPW; ++mi) {
-        const int md = stream * MPW + mi;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < STREAMS; ++st) acc += f[st] * otile[(((st * RG + rg) * MD + md) * NBW + nb) * 64 + lane];
-        if (!live) acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        *(f32x4 *)(op + 16 * md + 4 * g4) = acc;
-      }
-    }
+    for (int md = 0; md < MD; ++md) *(f32x4 *)(op + 16 * md + 4 * g4) = o[md] * fo;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: grid (rows * Hq, D / 64), 1024 threads.
+// Combine kernel: grid (rows * Hq, D / 32), 256 threads; a workgroup merges
+// 32 consecutive d of one (row, query head).  Thread t owns four of them
+// (dq = t % 8) and the splits s = sg, sg + 32, sg + 64, ... (sg = t / 8),
+// which it folds into four FP32 chains (one per d) against a running maximum
+// that moves only when a batch brings a larger m.  All loads of a batch (up to
+// kCombBatch splits: their (m, l) and O) are issued together, so S <= 512
+// takes one memory round trip.  The 32 chains of each d are then merged by
+// lane exchanges inside each wave and once through LDS across the four waves,
+// with the sink.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 4096;
+constexpr int kCombThreads = 256;
+constexpr int kCombD = 32;                    // d per workgroup
+constexpr int kCombDQ = kCombD / 4;           // threads per split group
+constexpr int kCombNSG = kCombThreads / kCombDQ;  // split groups
+constexpr int kCombBatch = 16;
 
-constexpr int kCombThreads = 1024;
-constexpr int kCombGroups = kCombThreads / 64;  // split groups per block
-constexpr int kCombBatch = 16;                  // O loads each thread keeps in flight
+__device__ __forceinline__ float xor_max3(float x) {  // over lanes l ^ 8, 16, 32
+  x = fmaxf(x, __shfl_xor(x, 8, 64));
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float xor_sum3(float x) {
+  x += __shfl_xor(x, 8, 64);
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
 
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs a) {
-  constexpr int kPer = kMaxSplits / kCombThreads;  // (m, l) pairs per thread
-  __shared__ float wts[kMaxSplits];
-  __shared__ float red[2][kCombThreads / 64];
-  __shared__ float gsum[kCombGroups][64];
+  __shared__ f32x4 wacc[kCombThreads / 64][kCombDQ];
+  __shared__ float wm[kCombThreads / 64], wden[kCombThreads / 64];
 
   const int rh = blockIdx.x;
   const int r = rh / a.q_heads, h = rh % a.q_heads;
   const int D = a.head_dim;
   const int t = threadIdx.x;
-  const int dl = t & 63, grp = t >> 6;
-  const int d = 64 * blockIdx.y + dl;
+  const int lane = t & 63, wave = t >> 6;
+  const int dq = t % kCombDQ, sg = t / kCombDQ;
+  const int d0 = kCombD * blockIdx.y + 4 * dq;
   float *outp = a.out + ((int64_t)r * a.q_heads + h) * D;
 
   if (r >= a.live_rows) {  // padding row: no read of the workspace
-    if (grp == 0) outp[d] = 0.f;
+    if (sg == 0) *(f32x4 *)(outp + d0) = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (a.lse && blockIdx.y == 0 && t == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
     return;
   }
@@ -709,82 +669,83 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs
   const int S = a.splits;
   const int64_t stride_unit = (int64_t)a.kv_heads * a.mrows;  // units between splits
   const int64_t unit0 = (int64_t)g * a.mrows + mrow;
-  const float sink2 = a.sink ? a.sink[h] * LOG2E_F : -INFINITY;
+  const f32x2 *ml = (const f32x2 *)a.ws_ml + unit0;
+  const f32x4 *ob = (const f32x4 *)(a.ws_o + unit0 * D + d0);
+  const int64_t ostride = stride_unit * (D / 4);  // f32x4 between splits
 
-  // 1) every (m, l) pair of this row, loads issued together, kept in registers
-  const f32x2 *ml = (const f32x2 *)a.ws_ml;
-  float mv[kPer], lv[kPer];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = t + kCombThreads * i;
-    f32x2 x = {-INFINITY, 0.f};
-    if (s < S) x = ml[unit0 + s * stride_unit];
-    mv[i] = x[0];
-    lv[i] = x[1];
-    mx = fmaxf(mx, x[0]);
-  }
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((t & 63) == 0) red[0][t >> 6] = mx;
-  __syncthreads();
-  float M = sink2;
-#pragma unroll
-  for (int i = 0; i < kCombThreads / 64; ++i) M = fmaxf(M, red[0][i]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-
-  // 2) weights 2^(m_s - M) and the denominator
-  float den = 0.f;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = t + kCombThreads * i;
-    if (s < S) {
-      const float w = __builtin_amdgcn_exp2f(mv[i] - Mu);
-      wts[s] = w;
-      den += w * lv[i];
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
-  if ((t & 63) == 0) red[1][t >> 6] = den;
-  __syncthreads();
-  float dsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kCombThreads / 64; ++i) dsum += red[1][i];
-  den = dsum + __builtin_amdgcn_exp2f(sink2 - Mu);
-
-  // 3) weighted sum of O.  Thread group grp takes splits s = grp (mod 16); it
-  //    issues up to kCombBatch loads at once, then folds them into four
-  //    independent FP32 accumulation chains.
-  const float *ob = a.ws_o + unit0 * D + d;
-  const int64_t sstride = stride_unit * D;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = grp; s0 < S; s0 += kCombGroups * kCombBatch) {
-    float o[kCombBatch];
+  float M = -INFINITY, den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < S; s0 += kCombNSG * kCombBatch) {
+    f32x2 mlv[kCombBatch];
+    f32x4 ov[kCombBatch];
 #pragma unroll
     for (int j = 0; j < kCombBatch; ++j) {
-      const int s = s0 + kCombGroups * j;
-      o[j] = s < S ? ob[(int64_t)s * sstride] : 0.f;
+      const int s = s0 + kCombNSG * j;
+      mlv[j] = (f32x2){-INFINITY, 0.f};
+      ov[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (s < S) {
+        mlv[j] = ml[(int64_t)s * stride_unit];
+        ov[j] = ob[(int64_t)s * ostride];
+      }
     }
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) bm = fmaxf(bm, mlv[j][0]);
+    if (bm > M) {
+      const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - bm);
+      den *= alpha;
+      acc *= alpha;
+      M = bm;
+    }
+    const float Mu = (M == -INFINITY) ? 0.f : M;
 #pragma unroll
     for (int j = 0; j < kCombBatch; ++j) {
-      const int s = s0 + kCombGroups * j;
-      if (s < S) acc[j & 3] = fmaf(wts[s], o[j], acc[j & 3]);
+      const float w = __builtin_amdgcn_exp2f(mlv[j][0] - Mu);  // 0 for m = -inf
+      den = fmaf(w, mlv[j][1], den);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = fmaf(w, ov[j][c], acc[c]);
     }
   }
-  gsum[grp][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+
+  // merge the eight split groups of this wave (lanes dq, dq + 8, ..., dq + 56)
+  const float Mw = xor_max3(M);
+  const float f = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mw);
+  den = xor_sum3(den * f);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = xor_sum3(acc[c] * f);
+  if (lane < kCombDQ) {
+    wacc[wave][lane] = acc;
+    if (lane == 0) {
+      wm[wave] = Mw;
+      wden[wave] = den;
+    }
+  }
   __syncthreads();
 
-  // 4) reduce the groups and finish
-  if (grp == 0) {
-    float tot = 0.f;
+  if (t < kCombDQ) {  // wave 0, one lane per dq: merge the waves and the sink
+    const float sink2 = a.sink ? a.sink[h] * LOG2E_F : -INFINITY;
+    float Mt = sink2;
 #pragma unroll
-    for (int i = 0; i < kCombGroups; ++i) tot += gsum[i][dl];
-    if (M == -INFINITY) {  // nothing visible and no sink
-      outp[d] = 0.f;
-      if (a.lse && blockIdx.y == 0 && dl == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
+    for (int i = 0; i < kCombThreads / 64; ++i) Mt = fmaxf(Mt, wm[i]);
+    const float Mu = (Mt == -INFINITY) ? 0.f : Mt;
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float dt = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombThreads / 64; ++i) {
+      const float fi = (wm[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wm[i] - Mu);
+      dt = fmaf(fi, wden[i], dt);
+      const f32x4 c = wacc[i][dq];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tot[k] = fmaf(fi, c[k], tot[k]);
+    }
+    dt += __builtin_amdgcn_exp2f(sink2 - Mu);  // 0 without a sink
+    const bool lse_lane = a.lse && blockIdx.y == 0 && dq == 0;
+    if (Mt == -INFINITY) {  // nothing visible and no sink
+      *(f32x4 *)(outp + d0) = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (lse_lane) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
     } else {
-      outp[d] = tot / den;
-      if (a.lse && blockIdx.y == 0 && dl == 0)
-        a.lse[(int64_t)r * a.q_heads + h] = (Mu + __log2f(den)) * LN2_F;
+      *(f32x4 *)(outp + d0) = tot / dt;
+      if (lse_lane) a.lse[(int64_t)r * a.q_heads + h] = (Mu + __log2f(dt)) * LN2_F;
     }
   }
 }
@@ -821,22 +782,35 @@ const va_plan_data *plan_of(const va_plan *plan) {
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-template <int D, int NBW, int RG, int FMT>
+// LDS stages per format (each stage is one 32-key chunk of K and V): the
+// bf16 D=128 ring (4 x 16 KiB) leaves room for two workgroups per CU; the
+// smaller chunks of the other formats run deeper rings in the same space.
+#ifndef VA_NST_BF16_D128
+#define VA_NST_BF16_D128 4
+#endif
+#ifndef VA_NST_BF16_D64
+#define VA_NST_BF16_D64 8
+#endif
+#ifndef VA_NST_QUANT
+#define VA_NST_QUANT 8
+#endif
+
+template <int D, int W, int FMT, int NST>
 hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   dim3 grid(a.splits, a.kv_heads);
-  hipLaunchKernelGGL((split_kernel<D, NBW, RG, FMT>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST>), grid, dim3(64 * (W + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int FMT>
+template <int D, int FMT, int NST>
 hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
   switch (nb_total) {
-    case 1: return launch_split<D, 1, 1, FMT>(a, stream);
-    case 2: return launch_split<D, 2, 1, FMT>(a, stream);
-    case 3: return launch_split<D, 3, 1, FMT>(a, stream);
-    case 4: return launch_split<D, 2, 2, FMT>(a, stream);
-    case 5:
-    case 6: return launch_split<D, 3, 2, FMT>(a, stream);
+    case 1: return launch_split<D, 1, FMT, NST>(a, stream);
+    case 2: return launch_split<D, 2, FMT, NST>(a, stream);
+    case 3: return launch_split<D, 3, FMT, NST>(a, stream);
+    case 4: return launch_split<D, 4, FMT, NST>(a, stream);
+    case 5: return launch_split<D, 5, FMT, NST>(a, stream);
+    case 6: return launch_split<D, 6, FMT, NST>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -879,6 +853,7 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   a.rows = d->rows;
   a.live_rows = d->live_rows;
   a.group = d->group;
+  a.inv_group = 1.0f / (float)d->group;
   a.mrows = d->matrix_rows;
   a.q_heads = d->q_heads;
   a.kv_heads = d->kv_heads;
@@ -908,11 +883,11 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   const int nb_total = (d->matrix_rows + 15) / 16;
   hipError_t e;
   if (quant) {
-    e = dispatch_rows<128, 1>(a, nb_total, stream);
+    e = dispatch_rows<128, 1, VA_NST_QUANT>(a, nb_total, stream);
   } else if (d->head_dim == 64) {
-    e = dispatch_rows<64, 0>(a, nb_total, stream);
+    e = dispatch_rows<64, 0, VA_NST_BF16_D64>(a, nb_total, stream);
   } else {
-    e = dispatch_rows<128, 0>(a, nb_total, stream);
+    e = dispatch_rows<128, 0, VA_NST_BF16_D128>(a, nb_total, stream);
   }
   return e == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
@@ -937,7 +912,7 @@ extern "C" va_status verify_attn_combine(const va_plan *plan, const void *worksp
   a.kv_heads = d->kv_heads;
   a.splits = d->splits;
   a.head_dim = d->head_dim;
-  dim3 grid(d->rows * d->q_heads, d->head_dim / 64);
+  dim3 grid(d->rows * d->q_heads, d->head_dim / kCombD);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
