@@ -42,7 +42,8 @@ ROWS, HQ, HKV, D, CAP = 8, 6, 1, 128, 262144
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 REPLICAS = 6
 METRIC = "verify-attn µs/call and KV-read GB/s (% HBM peak), 8 rows×6 heads, 1K–192K ctx"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_config2_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep_traffic.json")
+COPY_PROBE_MIB = 1024
 KERNEL_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "verify_attn.hip")
 
 
@@ -56,6 +57,103 @@ def kernel_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def summarize_profiles(d):
+    """Turn the rocprofv3 outputs of one profiling session into the committed
+    summaries: kernel durations (kernel trace) and HBM bytes per split launch
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+    plain copy of known size).  `d` holds trace/, pmc_fetch/, pmc_write/,
+    pmc_copy_fetch/, pmc_copy_write/ and the bench logs trace.log, fetch.log,
+    write.log written by the commands listed in the summaries."""
+    import csv
+    import collections
+
+    def bench_line(log):
+        for line in open(os.path.join(d, log)):
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+        raise SystemExit(f"no bench line in {log}")
+
+    def counters(sub, name):
+        rows = list(csv.DictReader(open(os.path.join(d, sub, name))))
+        return [(r["Kernel_Name"], int(r["Grid_Size"]) // int(r["Workgroup_Size"]), float(r["Counter_Value"]))
+                for r in rows]
+
+    hashes = {bench_line(x)["kernel_hash"] for x in ("trace.log", "fetch.log", "write.log")}
+    if len(hashes) != 1 or kernel_hash() not in hashes:
+        raise SystemExit(f"profiles were taken of another kernel source: {hashes} vs {kernel_hash()}")
+    copy_bytes = COPY_PROBE_MIB << 20
+    cf = [v for n, g, v in counters("pmc_copy_fetch", "copy_counter_collection.csv") if "copyBuffer" in n]
+    cw = [v for n, g, v in counters("pmc_copy_write", "copy_counter_collection.csv") if "copyBuffer" in n]
+    f_scale = copy_bytes / (sum(cf) / len(cf) * 1024)
+    w_scale = copy_bytes / (sum(cw) / len(cw) * 1024)
+    fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if "split_kernel" in n]
+    wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if "split_kernel" in n]
+    if len(fe) != len(wr):
+        raise SystemExit("fetch and write runs saw different split launches")
+    per_launch = [f * f_scale * 1024 + w * w_scale * 1024 for (_, f), (_, w) in zip(fe, wr)]
+    traffic = sum(per_launch) / len(per_launch)
+    contexts = bench_line("fetch.log")["config"]["contexts"]
+    json.dump({"kernel_hash": kernel_hash(), "contexts": contexts, "hbm_bytes_per_launch": round(traffic),
+               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "launches": len(per_launch)},
+              open(TRAFFIC_FILE, "w"), indent=1)
+
+    trace = list(csv.DictReader(open(os.path.join(d, "trace", "bench_kernel_trace.csv"))))
+    dur = collections.defaultdict(list)
+    for r in trace:
+        n = r["Kernel_Name"]
+        kind = "split_kernel" if "split_kernel" in n else "combine_kernel" if "combine_kernel" in n else None
+        if kind:
+            dur[(kind, n, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_X"]))].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    bl = bench_line("trace.log")
+    py = "python -u bench.py"
+    out = []
+    out.append("# split_kernel / combine_kernel, full-attention verify sweep (Hkv 1, Hq 6, D 128, 8 rows, ctx 1K-192K)")
+    out.append("")
+    out.append(f"kernel source sha256[:16]: {kernel_hash()}")
+    out.append("")
+    out.append("## Kernel durations (rocprofv3 kernel trace)")
+    out.append("")
+    out.append(f"command: rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace -o bench -- {py} --steps 10 --warmup 3")
+    out.append("")
+    out.append("| kernel | workgroups | launches | avg us | min us | max us |")
+    out.append("|---|---|---|---|---|---|")
+    tot = collections.defaultdict(list)
+    for (kind, n, wgs), v in sorted(dur.items(), key=lambda x: (x[0][0], x[0][2])):
+        tot[kind] += v
+        out.append(f"| {kind} | {wgs} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    for kind, v in sorted(tot.items()):
+        out.append(f"| {kind} | all | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    out.append("")
+    out.append("bench line of the same command (events; the trace itself slows the launches): "
+               f"roofline avg_launch_us {bl['roofline']['avg_launch_us']}, value {bl['value']} GB/s")
+    out.append("")
+    out.append("## HBM traffic of split_kernel (rocprofv3 --pmc, one counter per run)")
+    out.append("")
+    out.append(f"command: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/pmc_fetch -o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline")
+    out.append(f"command: rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/pmc_write -o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline")
+    out.append(f"calibration: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE ... -- {py} --copy-probe {COPY_PROBE_MIB}"
+               f" (device copy of {COPY_PROBE_MIB} MiB: FETCH_SIZE reads {sum(cf) / len(cf):.0f} KiB,"
+               f" WRITE_SIZE {sum(cw) / len(cw):.0f} KiB -> scale {f_scale:.4f} / {w_scale:.4f})")
+    out.append("")
+    out.append("| workgroups | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |")
+    out.append("|---|---|---|---|---|")
+    byg = collections.defaultdict(list)
+    for (g, f), (_, w) in zip(fe, wr):
+        byg[g].append((f, w))
+    for g in sorted(byg):
+        v = byg[g]
+        fa = sum(x[0] for x in v) / len(v)
+        wa = sum(x[1] for x in v) / len(v)
+        out.append(f"| {g} | {len(v)} | {fa:.1f} | {wa:.1f} | {(fa * f_scale + wa * w_scale) * 1024:.0f} |")
+    out.append("")
+    out.append(f"mean HBM bytes per split launch over the sweep: {traffic:.0f}"
+               f" (algorithmic KV bytes per launch: {bl['roofline']['algorithmic_bytes_per_launch']})")
+    name = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep.md")
+    open(name, "w").write("\n".join(out) + "\n")
+    print(f"wrote {name} and {TRAFFIC_FILE}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -66,7 +164,14 @@ def main():
     ap.add_argument("--replicas", type=int, default=REPLICAS)
     ap.add_argument("--kernel-reps", type=int, default=30, help="event-timed launches per context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from one profiling session's outputs (no GPU)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     if args.gpus != 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -74,12 +179,22 @@ def main():
                   "the verification call is a single-GPU kernel and no multi-GPU path exists.", flush=True)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import speculative_decode_verify_amd as va
     from speculative_decode_verify_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
     contexts = args.ctx or CONTEXTS
     stream = torch.cuda.current_stream()
 
@@ -107,9 +222,11 @@ def main():
     torch.cuda.synchronize()
 
     def call(c, rep):
+        # launched on the current stream: the timing stream, or a graph's capture stream
         k, v = c["kvs"][rep]
-        va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=stream)
-        va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"], stream=stream)
+        cur = torch.cuda.current_stream()
+        va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=cur)
+        va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"], stream=cur)
 
     def step(i):
         for c in cases:
@@ -121,16 +238,36 @@ def main():
     torch.cuda.synchronize()
     gpu_out0 = [(c["out"].double().cpu().numpy(), c["lse"].double().cpu().numpy()) for c in cases]
 
+    # ---------------- HIP graphs of the work ----------------
+    # Launching from Python costs ~10 us of host time per call, more than a
+    # small-context kernel runs, so timed work is replayed from HIP graphs
+    # (as a serving loop would launch it); the eager rate is reported beside.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    step_graphs = [capture(lambda r=r: [call(c, r) for c in cases]) for r in range(args.replicas)]
+    torch.cuda.synchronize()
+    # a replayed step must reproduce the eager result bit for bit
+    step_graphs[0].replay()
+    torch.cuda.synchronize()
+    for c, (o0, l0) in zip(cases, gpu_out0):
+        if not (np.array_equal(c["out"].double().cpu().numpy(), o0) and
+                np.array_equal(c["lse"].double().cpu().numpy(), l0)):
+            raise SystemExit("graph replay differs from the eager launch")
+
     # ---------------- pass A: whole steps ----------------
     for i in range(args.warmup):
-        step(i)
+        step_graphs[i % args.replicas].replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step_graphs[(args.warmup + i) % args.replicas].replay()
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -139,35 +276,51 @@ def main():
     bytes_per_step = sum(kv_bytes(c["hi"]) for c in cases)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
-    # ---------------- pass B: per-launch kernel times ----------------
+    # eager launches, for reference (host-bound at small contexts)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---------------- pass B: per-kernel times ----------------
+    # Each kernel is timed over kernel_reps back-to-back launches replayed
+    # from a graph on the launch stream; the split launches rotate over the
+    # cold replicas like pass A.
     sweep = []
     split_bytes, split_ms = 0.0, 0.0
     for c in cases:
-        ts, tc = [], []
-        for i in range(args.kernel_reps):
-            k, v = c["kvs"][i % args.replicas]
-            a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            a.record(stream)
-            va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=stream)
-            b.record(stream)
-            va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"], stream=stream)
-            d.record(stream)
-            ts.append((a, b))
-            tc.append((b, d))
+        def splits(c=c):
+            for i in range(args.kernel_reps):
+                k, v = c["kvs"][i % args.replicas]
+                va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=torch.cuda.current_stream())
+
+        def combines(c=c):
+            for i in range(args.kernel_reps):
+                va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"],
+                                       stream=torch.cuda.current_stream())
+        gs, gc = capture(splits), capture(combines)
+        gs.replay()
+        gc.replay()
+        a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        gs.replay()
+        b.record(stream)
+        gc.replay()
+        d.record(stream)
         torch.cuda.synchronize()
-        s_ms = sorted(x.elapsed_time(y) for x, y in ts)
-        c_ms = sorted(x.elapsed_time(y) for x, y in tc)
-        s_avg = sum(s_ms) / len(s_ms)
-        c_avg = sum(c_ms) / len(c_ms)
+        del gs, gc
+        s_avg = a.elapsed_time(b) / args.kernel_reps
+        c_avg = b.elapsed_time(d) / args.kernel_reps
         nb = kv_bytes(c["hi"])
-        split_bytes += nb * len(s_ms)
-        split_ms += sum(s_ms)
+        split_bytes += nb * args.kernel_reps
+        split_ms += s_avg * args.kernel_reps
         gbs = nb / (s_avg * 1e-3) / 1e9
         sweep.append({
             "ctx": c["ctx"], "live": c["live"], "splits": c["plan"].splits, "kv_bytes": nb,
             "us_per_call": round((s_avg + c_avg) * 1e3, 2),
-            "split_us": round(s_avg * 1e3, 2), "split_us_median": round(s_ms[len(s_ms) // 2] * 1e3, 2),
-            "combine_us": round(c_avg * 1e3, 2),
+            "split_us": round(s_avg * 1e3, 2), "combine_us": round(c_avg * 1e3, 2),
             "kv_gbs_split": round(gbs, 1), "pct_hbm_peak_split": round(100 * gbs / HBM_PEAK_GBS, 1),
             "kv_gbs_call": round(nb / ((s_avg + c_avg) * 1e-3) / 1e9, 1),
         })
@@ -185,14 +338,13 @@ def main():
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "split_kernel<D=128,W=3,bf16,NST=4>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
+                "kernel": "split_kernel<D=128,W=3,bf16,NST=4,NPW=2>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
                 "avg_launch_us": round(split_ms / launches * 1e3, 2), "launches": launches}
 
     # ---------------- CPU baseline (oracle) + full-size parity ----------------
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        import numpy as np
         from oracle import attn as oattn
         from oracle.masks import Problem
         try:
@@ -234,7 +386,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "full-attention verify sweep: Hkv 1, Hq 6, D 128, 8 rows (4-8 live), "
                                "causal, sink on, capacity 262144, ctx 1K-192K, cold KV",
-                   "contexts": contexts, "replicas": args.replicas, "splits": "plan" if not args.splits else args.splits},
+                   "contexts": contexts, "replicas": args.replicas, "splits": "plan" if not args.splits else args.splits,
+                   "launch": "HIP graph replay"},
+        "eager_launch_ms_per_step": round(eager_ms_per_step, 4),
         "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "sweep": sweep,
         "wall_s_timed": round(t_wall, 4), "kernel_hash": kernel_hash(),
     }

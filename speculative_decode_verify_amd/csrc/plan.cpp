@@ -14,12 +14,13 @@
 static inline int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
 static inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Splits: each workgroup streams a contiguous run of tiles.  Enough
-// workgroups to cover every CU (and the 8 XCDs evenly) in a single round --
-// the split kernel's LDS footprint admits one workgroup per CU -- but not so
-// many that the partials' traffic rivals the KV bytes: at least
-// kMinTilesPerSplit tiles per split.
-static const int64_t kMinTilesPerSplit = 4;
+// Splits: each workgroup streams a contiguous run of tiles, and a workgroup
+// runs its chunks one after another, so the shortest split kernel gives every
+// workgroup as few tiles as possible: one tile per split, up to one
+// workgroup per CU over all KV heads (more than one per CU measured slower:
+// the extra partials cost more than the extra overlap gains).  A capped count
+// of 8 or more is kept a multiple of 8, one share per XCD.
+static const int64_t kMinTilesPerSplit = 1;
 static const int64_t kWorkgroupsPerCU = 1;
 
 static int32_t choose_splits(int64_t tiles, int32_t kv_heads, int32_t num_cus) {
@@ -27,11 +28,10 @@ static int32_t choose_splits(int64_t tiles, int32_t kv_heads, int32_t num_cus) {
   if (num_cus <= 0) num_cus = 256;
   int64_t cap = (kWorkgroupsPerCU * num_cus) / kv_heads;
   if (cap < 1) cap = 1;
-  int64_t s = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
-  if (s > cap) s = cap;
+  const int64_t want = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+  if (want <= cap) return (int32_t)want;  // every split gets its minimum
+  int64_t s = cap;
   if (s >= 8) s = (s / 8) * 8;  // keep whole rounds over the 8 XCDs
-  if (s < 1) s = 1;
-  if (s > tiles) s = tiles;
   return (int32_t)s;
 }
 

@@ -149,20 +149,23 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel: one workgroup per (split, KV head) with W + 1 wave64s.
-//   Waves 0..W-1 (consumers): wave w owns query matrix rows [16w, 16w + 16)
+// Split kernel: one workgroup per (split, KV head) with W + NPW wave64s.
+//   Consumers, waves 0..W-1: wave w owns query matrix rows [16w, 16w + 16)
 //     for the whole split and keeps their online-softmax state in registers;
 //     every consumer walks all of the split's 32-key chunks in order.
-//   Wave W (producer): fills a ring of NST LDS stages with the chunks' K and
-//     V tiles by LDS DMA, NST - 1 chunks ahead of the consumers.
-// One workgroup barrier per chunk both publishes chunk n (the producer waited
-// for its DMA just before) and frees the stage of chunk n - 1, which the
-// producer refills right after.  No cross-wave merge: each wave writes its
-// own rows' partials.
+//   Producers, waves W..W+NPW-1: fill a ring of NST LDS stages (chunk j in
+//     stage j % NST) with the chunks' K and V tiles by LDS DMA, NST - 1
+//     chunks ahead of the consumers; each producer issues its share of every
+//     chunk's DMA instructions.
+// One workgroup barrier per chunk both publishes chunk n (each producer waited
+// for its share of the DMA just before) and frees the stage of chunk n - 1,
+// which the producers refill right after.  No cross-wave merge: each
+// consumer writes its own rows' partials.
 //   D    head dim (64 or 128)
 //   W    16-row blocks of query matrix rows (1..6)
 //   FMT  0 = bf16 K/V; 1 = E4M3FN rotated K, INT8 V with per-key scale
 //   NST  LDS stages
+//   NPW  producer waves
 // ---------------------------------------------------------------------------
 template <int D, int FMT>
 struct StageGeom {
@@ -208,14 +211,19 @@ __device__ __forceinline__ void pin(int64_t x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
 
-template <int D, int W, int FMT, int NST>
-__global__ __launch_bounds__(64 * (W + 1)) void split_kernel(const SplitArgs a) {
+template <int D, int W, int FMT, int NST, int NPW>
+__global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a) {
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
   constexpr int MD = D / 16;  // O^T row blocks over d
   constexpr int KROW = G::KROW, PIECES = G::PIECES, RPI = G::RPI, NDMA = G::NDMA;
   constexpr int kTileB = G::kTileB, kStageB = G::kStageB, kVm = G::kVm;
-  static_assert(NST >= 2 && (NST - 2) * kVm <= 63, "vmcnt counts at most 63 loads");
+  static_assert(NST >= 2, "a ring of at least two stages");
+  constexpr int U = 2 * NDMA / NPW;           // DMA instructions per chunk and producer
+  constexpr int kVmP = U + (FMT == 1 ? 1 : 0);  // the same, with the quantised scales
+  static_assert(FMT == 0 || NPW == 1, "the scale DMA belongs to a single producer");
+  static_assert((2 * NDMA) % NPW == 0, "producers share a chunk's DMA evenly");
+  static_assert((NST - 2) * kVmP <= 63, "vmcnt counts at most 63 loads");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NST * kStageB];
 
   const int lane = threadIdx.x & 63;
@@ -264,8 +272,8 @@ __global__ __launch_bounds__(64 * (W + 1)) void split_kernel(const SplitArgs a) 
     nch = c1 > c0 ? c1 - c0 : 0;
   };
 
-  if (wave == W) {
-    // ================= producer =================
+  if (wave >= W) {
+    // ================= producers =================
     chunk_range();
     const uint8_t *kbase = kptr + (int64_t)kvh * head_stride;
     const uint8_t *vbase = vptr + (int64_t)kvh * head_stride;
@@ -290,45 +298,46 @@ __global__ __launch_bounds__(64 * (W + 1)) void split_kernel(const SplitArgs a) 
     //   V (bf16): f = 2 * (row % (PIECES/2)), an even value, so a pair of
     //      pieces {2k, 2k+1} stays a pair; the 16 rows of one transpose read
     //      spread over all bank groups.  V (INT8) is read bytewise, unswizzled.
-    uint32_t koff[NDMA], voff[NDMA];
+    // A chunk's DMA is 2*NDMA instructions: u < NDMA copies K rows
+    // [u*RPI, u*RPI + RPI), the rest V; instruction u lands at stage + 1024*u
+    // (the V tile starts NDMA KiB into the stage).  Producer wave pw issues
+    // instructions [pw*U, pw*U + U) of every chunk.
+    const int pw = wave - W;
+    uint32_t off[U];
+    bool isv[U];
 #pragma unroll
-    for (int t = 0; t < NDMA; ++t) {
+    for (int i = 0; i < U; ++i) {
+      const int u = pw * U + i;
+      isv[i] = u >= NDMA;
+      const int t = isv[i] ? u - NDMA : u;
       const int row = t * RPI + lane / PIECES;
       const int pos = lane % PIECES;
-      koff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ (row & (PIECES - 1)));
-      voff[t] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ (FMT == 0 ? (2 * row) & (PIECES - 2) : 0));
+      const int f = isv[i] ? (FMT == 0 ? (2 * row) & (PIECES - 2) : 0) : (row & (PIECES - 1));
+      off[i] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ f);
     }
-    // Chunk n into stage `st`: lane l of instruction t stores 16 bytes at
-    // tile + 1024*t + 16*l.  Issue order per chunk: K tile, V tile, scales.
+    // Chunk n into stage `st` (lane l of instruction u stores 16 bytes at
+    // stage + 1024*u + 16*l), then (quantised values) the chunk's scales.
     auto issue = [&](int32_t n, int st) {
       const int32_t c0 = (c_first + n) * kChunk;
       const int64_t row0 = chunk_row(c0);
       const uint8_t *kc = kbase + row0 * row_stride;
       const uint8_t *vc = vbase + row0 * row_stride;
-      uint8_t *kt = smem + st * kStageB;
-      uint8_t *vt = kt + kTileB;
+      uint8_t *stg = smem + st * kStageB + 1024 * pw * U;
       if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
 #pragma unroll
-        for (int t = 0; t < NDMA; ++t) dma16(kc + koff[t], kt + 1024 * t);
-#pragma unroll
-        for (int t = 0; t < NDMA; ++t) dma16(vc + voff[t], vt + 1024 * t);
+        for (int i = 0; i < U; ++i) dma16((isv[i] ? vc : kc) + off[i], stg + 1024 * i);
       } else {
 #pragma unroll
-        for (int t = 0; t < NDMA; ++t) {
-          const int row = t * RPI + lane / PIECES;
+        for (int i = 0; i < U; ++i) {
+          const int u = pw * U + i;
+          const int row = (isv[i] ? u - NDMA : u) * RPI + lane / PIECES;
           const uint32_t x = (uint32_t)clampx(row, c0) * rs;
-          dma16(kc + x + (koff[t] - (uint32_t)row * rs), kt + 1024 * t);
-        }
-#pragma unroll
-        for (int t = 0; t < NDMA; ++t) {
-          const int row = t * RPI + lane / PIECES;
-          const uint32_t x = (uint32_t)clampx(row, c0) * rs;
-          dma16(vc + x + (voff[t] - (uint32_t)row * rs), vt + 1024 * t);
+          dma16((isv[i] ? vc : kc) + x + (off[i] - (uint32_t)row * rs), stg + 1024 * i);
         }
       }
       if constexpr (FMT == 1) {
         const float *sc = vsc + (int64_t)kvh * vsc_stride + row0;
-        dma4(sc + clampx(lane & 31, c0), vt + kTileB);
+        dma4(sc + clampx(lane & 31, c0), smem + st * kStageB + 2 * kTileB);
       }
     };
 #pragma unroll
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(64 * (W + 1)) void split_kernel(const SplitArgs a) 
       // chunks issued after n: n+1 .. min(n + NST - 2, nch - 1); DMA groups
       // complete in issue order, so this wait leaves exactly those in flight.
       const int32_t later = nch - 1 - n;
-      wait_chunks<kVm, NST - 2>(later < NST - 2 ? later : NST - 2);
+      wait_chunks<kVmP, NST - 2>(later < NST - 2 ? later : NST - 2);
       wg_barrier();
       if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
       st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
@@ -603,9 +612,9 @@ __global__ __launch_bounds__(64 * (W + 1)) void split_kernel(const SplitArgs a) 
   // ---------------- partials of this wave's rows ----------------
   // Normalised to the true maximum M of the split: m = M, l = sum 2^(x - M),
   // O = sum 2^(x - M) v.
+  const float lt = wave_sum16x4(lrow);
+  const float f = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - mtrue);
   if (m < mrows) {
-    const float lt = wave_sum16x4(lrow);
-    const float f = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - mtrue);
     const int64_t unit = ((int64_t)split * kv_heads + kvh) * mrows + m;
     if (g4 == 0) {
       *(f32x2 *)(ws_ml + unit * 2) = row_ok ? (f32x2){mtrue, lt * f} : (f32x2){-INFINITY, 0.f};
@@ -782,35 +791,33 @@ const va_plan_data *plan_of(const va_plan *plan) {
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// LDS stages per format (each stage is one 32-key chunk of K and V): the
-// bf16 D=128 ring (4 x 16 KiB) leaves room for two workgroups per CU; the
-// smaller chunks of the other formats run deeper rings in the same space.
-#ifndef VA_NST_BF16_D128
-#define VA_NST_BF16_D128 4
-#endif
-#ifndef VA_NST_BF16_D64
-#define VA_NST_BF16_D64 8
-#endif
-#ifndef VA_NST_QUANT
-#define VA_NST_QUANT 8
-#endif
+// Producer waves and LDS stages per format.  Measured on the full-attention
+// sweep: one or two producers and three to five bf16 stages stream alike
+// (the kernel runs at the chip's streaming rate once the ring has two or
+// more chunks in flight); two producers halve each one's issue work.
+template <int FMT>
+constexpr int producers_for() { return FMT == 1 ? 1 : 2; }
+template <int D, int FMT>
+constexpr int stages_for() { return FMT == 1 ? 8 : (D == 64 ? 8 : 4); }
 
-template <int D, int W, int FMT, int NST>
+template <int D, int W, int FMT>
 hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
+  constexpr int NPW = producers_for<FMT>();
+  constexpr int NST = stages_for<D, FMT>();
   dim3 grid(a.splits, a.kv_heads);
-  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST>), grid, dim3(64 * (W + 1)), 0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW>), grid, dim3(64 * (W + NPW)), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int FMT, int NST>
+template <int D, int FMT>
 hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
   switch (nb_total) {
-    case 1: return launch_split<D, 1, FMT, NST>(a, stream);
-    case 2: return launch_split<D, 2, FMT, NST>(a, stream);
-    case 3: return launch_split<D, 3, FMT, NST>(a, stream);
-    case 4: return launch_split<D, 4, FMT, NST>(a, stream);
-    case 5: return launch_split<D, 5, FMT, NST>(a, stream);
-    case 6: return launch_split<D, 6, FMT, NST>(a, stream);
+    case 1: return launch_split<D, 1, FMT>(a, stream);
+    case 2: return launch_split<D, 2, FMT>(a, stream);
+    case 3: return launch_split<D, 3, FMT>(a, stream);
+    case 4: return launch_split<D, 4, FMT>(a, stream);
+    case 5: return launch_split<D, 5, FMT>(a, stream);
+    case 6: return launch_split<D, 6, FMT>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -883,11 +890,11 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   const int nb_total = (d->matrix_rows + 15) / 16;
   hipError_t e;
   if (quant) {
-    e = dispatch_rows<128, 1, VA_NST_QUANT>(a, nb_total, stream);
+    e = dispatch_rows<128, 1>(a, nb_total, stream);
   } else if (d->head_dim == 64) {
-    e = dispatch_rows<64, 0, VA_NST_BF16_D64>(a, nb_total, stream);
+    e = dispatch_rows<64, 0>(a, nb_total, stream);
   } else {
-    e = dispatch_rows<128, 0, VA_NST_BF16_D128>(a, nb_total, stream);
+    e = dispatch_rows<128, 0>(a, nb_total, stream);
   }
   return e == hipSuccess ? VA_OK : VA_ERR_HIP;
 }

@@ -473,6 +473,36 @@ def test_deterministic_repeat():
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
 
 
+def test_graph_replay_matches_eager():
+    """Split + combine captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, equals the eager launch bit for bit."""
+    plan, kw, q, k, v, s = linear_case(8003, 8, 6, 6, 1, 128, "causal", first_pos=9000)
+    q, k, v, s = q.to(DEV), k.to(DEV), v.to(DEV), s.to(DEV)
+    ws = va.workspace_for(plan, DEV)
+    out = torch.empty((plan.rows, plan.q_heads, plan.head_dim), dtype=torch.float32, device=DEV)
+    lse = torch.empty((plan.rows, plan.q_heads), dtype=torch.float32, device=DEV)
+    va.verify_attn_split(plan, q, k, v, ws)
+    va.verify_attn_combine(plan, ws, out, lse=lse, sink=s)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        va.verify_attn_split(plan, q, k, v, ws)
+        va.verify_attn_combine(plan, ws, out, lse=lse, sink=s)
+    for rep in range(4):
+        out.fill_(NAN)
+        lse.fill_(NAN)
+        ws.fill_(NAN)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref_o.view(torch.int32)), f"replay {rep}: out differs"
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), f"replay {rep}: lse differs"
+        # eager work between replays
+        o2, l2, _ = run(plan, q, k, v, s)
+        assert torch.equal(o2.view(torch.int32), ref_o.cpu().view(torch.int32))
+
+
 @pytest.mark.parametrize("mask", ["causal", "tree"])
 def test_append_invariance(mask):
     """Changing keys and values a row does not see leaves that row's output
