@@ -631,9 +631,10 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
 // 32 consecutive d of one (row, query head).  Thread t owns four of them
 // (dq = t % 8) and the splits s = sg, sg + 32, sg + 64, ... (sg = t / 8),
 // which it folds into four FP32 chains (one per d) against a running maximum
-// that moves only when a batch brings a larger m.  All loads of a batch (up to
-// kCombBatch splits: their (m, l) and O) are issued together, so S <= 512
-// takes one memory round trip.  The 32 chains of each d are then merged by
+// that moves only when a batch brings a larger m.  All loads of a batch
+// (BATCH splits: their (m, l) and O) are issued together; the launch picks
+// the smallest BATCH in {1, 2, 4, 8, 16} that covers S in one round, so
+// S <= 512 takes one memory round trip and short reads run few instructions.  The 32 chains of each d are then merged by
 // lane exchanges inside each wave and once through LDS across the four waves,
 // with the sink.
 // ---------------------------------------------------------------------------
@@ -642,64 +643,79 @@ constexpr int kCombThreads = 256;
 constexpr int kCombD = 32;                    // d per workgroup
 constexpr int kCombDQ = kCombD / 4;           // threads per split group
 constexpr int kCombNSG = kCombThreads / kCombDQ;  // split groups
-constexpr int kCombBatch = 16;
+constexpr int kCombMaxBatch = 16;
 
-__device__ __forceinline__ float xor_max3(float x) {  // over lanes l ^ 8, 16, 32
-  x = fmaxf(x, __shfl_xor(x, 8, 64));
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+// Lane l ^ 8 by DPP row_ror:8 (a rotation by 8 inside each 16-lane row).
+__device__ __forceinline__ float lane_xor8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+// Reductions over the eight lanes l ^ {0, 8, 16, 24, 32, ...} that share
+// l % 8, all on the VALU.
+__device__ __forceinline__ float xor_max3(float x) {
+  x = fmaxf(x, lane_xor8(x));
+  return wave_max16x4(x);
 }
 __device__ __forceinline__ float xor_sum3(float x) {
-  x += __shfl_xor(x, 8, 64);
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
+  x += lane_xor8(x);
+  return wave_sum16x4(x);
 }
 
+template <int BATCH>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs a) {
   __shared__ f32x4 wacc[kCombThreads / 64][kCombDQ];
   __shared__ float wm[kCombThreads / 64], wden[kCombThreads / 64];
 
+  // every kernel argument loaded in one round trip (see pin())
+  const float *ws_ml = a.ws_ml, *ws_o = a.ws_o, *sinkp = a.sink;
+  float *outb = a.out, *lsep = a.lse;
+  const int32_t live_rows = a.live_rows, group = a.group, mrows = a.mrows, q_heads = a.q_heads;
+  const int32_t kv_heads = a.kv_heads, S = a.splits, D = a.head_dim;
+  pin(ws_ml), pin(ws_o), pin(sinkp), pin(outb), pin(lsep), pin(live_rows), pin(group), pin(mrows);
+  pin(q_heads), pin(kv_heads), pin(S), pin(D);
+
   const int rh = blockIdx.x;
-  const int r = rh / a.q_heads, h = rh % a.q_heads;
-  const int D = a.head_dim;
+  const int r = rh / q_heads, h = rh % q_heads;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int dq = t % kCombDQ, sg = t / kCombDQ;
   const int d0 = kCombD * blockIdx.y + 4 * dq;
-  float *outp = a.out + ((int64_t)r * a.q_heads + h) * D;
+  float *outp = outb + ((int64_t)r * q_heads + h) * D;
 
-  if (r >= a.live_rows) {  // padding row: no read of the workspace
+  if (r >= live_rows) {  // padding row: no read of the workspace
     if (sg == 0) *(f32x4 *)(outp + d0) = (f32x4){0.f, 0.f, 0.f, 0.f};
-    if (a.lse && blockIdx.y == 0 && t == 0) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
+    if (lsep && blockIdx.y == 0 && t == 0) lsep[(int64_t)r * q_heads + h] = -INFINITY;
     return;
   }
-  const int g = h / a.group;
-  const int mrow = r * a.group + (h - g * a.group);
-  const int S = a.splits;
-  const int64_t stride_unit = (int64_t)a.kv_heads * a.mrows;  // units between splits
-  const int64_t unit0 = (int64_t)g * a.mrows + mrow;
-  const f32x2 *ml = (const f32x2 *)a.ws_ml + unit0;
-  const f32x4 *ob = (const f32x4 *)(a.ws_o + unit0 * D + d0);
-  const int64_t ostride = stride_unit * (D / 4);  // f32x4 between splits
+  const int g = h / group;
+  const int mrow = r * group + (h - g * group);
+  const int64_t stride_unit = (int64_t)kv_heads * mrows;  // units between splits
+  const int64_t unit0 = (int64_t)g * mrows + mrow;
+  // split s of this (row, head): (m, l) at mlb + s*ml_step, O at ob + s*o_step
+  const uint8_t *mlb = (const uint8_t *)(ws_ml + unit0 * 2);
+  const uint8_t *ob = (const uint8_t *)(ws_o + unit0 * D + d0);
+  const uint64_t ml_step = (uint64_t)stride_unit * 2 * 4;
+  const uint64_t o_step = (uint64_t)stride_unit * D * 4;
 
   float M = -INFINITY, den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sg; s0 < S; s0 += kCombNSG * kCombBatch) {
-    f32x2 mlv[kCombBatch];
-    f32x4 ov[kCombBatch];
+  for (int s0 = sg; s0 < S; s0 += kCombNSG * BATCH) {
+    f32x2 mlv[BATCH];
+    f32x4 ov[BATCH];
+    // Loads are unconditional, so they issue back to back: a split past S
+    // re-reads split S-1 and gets m + (-inf) = -inf, hence weight 0 (its
+    // finite l and O then add nothing).
 #pragma unroll
-    for (int j = 0; j < kCombBatch; ++j) {
+    for (int j = 0; j < BATCH; ++j) {
       const int s = s0 + kCombNSG * j;
-      mlv[j] = (f32x2){-INFINITY, 0.f};
-      ov[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (s < S) {
-        mlv[j] = ml[(int64_t)s * stride_unit];
-        ov[j] = ob[(int64_t)s * ostride];
-      }
+      const uint32_t se = (uint32_t)(s < S - 1 ? s : S - 1);
+      mlv[j] = *(const f32x2 *)(mlb + se * ml_step);
+      ov[j] = *(const f32x4 *)(ob + se * o_step);
+      mlv[j][0] += s < S ? 0.f : -INFINITY;
     }
+    asm volatile("" ::: "memory");  // keeps every load of the batch above the first use
     float bm = M;
 #pragma unroll
-    for (int j = 0; j < kCombBatch; ++j) bm = fmaxf(bm, mlv[j][0]);
+    for (int j = 0; j < BATCH; ++j) bm = fmaxf(bm, mlv[j][0]);
     if (bm > M) {
       const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - bm);
       den *= alpha;
@@ -708,7 +724,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs
     }
     const float Mu = (M == -INFINITY) ? 0.f : M;
 #pragma unroll
-    for (int j = 0; j < kCombBatch; ++j) {
+    for (int j = 0; j < BATCH; ++j) {
       const float w = __builtin_amdgcn_exp2f(mlv[j][0] - Mu);  // 0 for m = -inf
       den = fmaf(w, mlv[j][1], den);
 #pragma unroll
@@ -732,7 +748,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs
   __syncthreads();
 
   if (t < kCombDQ) {  // wave 0, one lane per dq: merge the waves and the sink
-    const float sink2 = a.sink ? a.sink[h] * LOG2E_F : -INFINITY;
+    const float sink2 = sinkp ? sinkp[h] * LOG2E_F : -INFINITY;
     float Mt = sink2;
 #pragma unroll
     for (int i = 0; i < kCombThreads / 64; ++i) Mt = fmaxf(Mt, wm[i]);
@@ -748,13 +764,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs
       for (int k = 0; k < 4; ++k) tot[k] = fmaf(fi, c[k], tot[k]);
     }
     dt += __builtin_amdgcn_exp2f(sink2 - Mu);  // 0 without a sink
-    const bool lse_lane = a.lse && blockIdx.y == 0 && dq == 0;
+    const bool lse_lane = lsep && blockIdx.y == 0 && dq == 0;
     if (Mt == -INFINITY) {  // nothing visible and no sink
       *(f32x4 *)(outp + d0) = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (lse_lane) a.lse[(int64_t)r * a.q_heads + h] = -INFINITY;
+      if (lse_lane) lsep[(int64_t)r * q_heads + h] = -INFINITY;
     } else {
       *(f32x4 *)(outp + d0) = tot / dt;
-      if (lse_lane) a.lse[(int64_t)r * a.q_heads + h] = (Mu + __log2f(dt)) * LN2_F;
+      if (lse_lane) lsep[(int64_t)r * q_heads + h] = (Mu + __log2f(dt)) * LN2_F;
     }
   }
 }
@@ -919,8 +935,21 @@ extern "C" va_status verify_attn_combine(const va_plan *plan, const void *worksp
   a.kv_heads = d->kv_heads;
   a.splits = d->splits;
   a.head_dim = d->head_dim;
+  // the smallest batch that covers the splits in one round (fewer
+  // instructions for short reads); larger S loops over rounds of 16
   dim3 grid(d->rows * d->q_heads, d->head_dim / kCombD);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombThreads), 0, stream, a);
+  const int per = (d->splits + kCombNSG - 1) / kCombNSG;
+  if (per <= 1) {
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kCombThreads), 0, stream, a);
+  } else if (per <= 2) {
+    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(kCombThreads), 0, stream, a);
+  } else if (per <= 4) {
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(kCombThreads), 0, stream, a);
+  } else if (per <= 8) {
+    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(kCombThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(combine_kernel<kCombMaxBatch>, grid, dim3(kCombThreads), 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
