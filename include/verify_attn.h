@@ -79,7 +79,8 @@ typedef enum { VA_KV_BF16 = 0, VA_KV_K_E4M3_WHT_V_I8 = 1 } va_kv_fmt;
 
 #define VA_MAX_ROWS 16
 #define VA_MAX_MATRIX_ROWS 96   /* rows * (q_heads / kv_heads) */
-#define VA_TILE 64              /* keys per tile; split boundaries are tile aligned */
+#define VA_TILE 64              /* ring slots come in 64-slot tiles                      */
+#define VA_SPLIT_KEYS 32        /* keys per split granule; split boundaries are 32-key aligned */
 
 /* The problem, as plain host data.  Fields marked (w) are read in window mode
  * only, (t) in tree mode only. */
@@ -112,7 +113,7 @@ typedef struct {
   int32_t splits;              /* S                                                        */
   int32_t matrix_rows;         /* rows * G                                                 */
   int64_t lo, hi;              /* union of the live rows' visible keys lies in [lo, hi)    */
-  int64_t tile_lo, tiles;      /* first tile floor(lo/64) and tile count ceil(hi/64)-tile_lo */
+  int64_t chunk_lo, chunks;    /* first granule floor(lo/32), count ceil(hi/32) - chunk_lo */
   int64_t row_lo[VA_MAX_ROWS]; /* row r sees [row_lo, row_hi) (tree: the prefix part)      */
   int64_t row_hi[VA_MAX_ROWS];
   uint32_t anc[VA_MAX_ROWS];   /* tree: bit j set iff node j is node r or its ancestor     */
@@ -133,9 +134,9 @@ va_status verify_attn_plan(const va_problem *p, va_plan *plan, size_t *workspace
 va_status verify_attn_plan_query(const va_plan *plan, va_plan_info *info);
 
 /* Key range [*key_begin, *key_end) that split s covers (empty if begin ==
- * end).  With q = T / S and r = T % S, split s takes q + 1 tiles if s < r
- * and q otherwise, contiguous from tile_lo; keys are clipped to [lo, hi).
- * Host only. */
+ * end).  With C granules of 32 keys, q = C / S and r = C % S, split s takes
+ * q + 1 granules if s < r and q otherwise, contiguous from chunk_lo; keys are
+ * clipped to [lo, hi).  Host only. */
 va_status verify_attn_plan_split_range(const va_plan *plan, int32_t s,
                                        int64_t *key_begin, int64_t *key_end);
 

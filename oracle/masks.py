@@ -20,15 +20,16 @@ Readings where the pages leave a step open:
   prefix [0, prefix_len) plus its ancestors and itself; parent -1 means the
   node hangs off the last committed token, which is already in the prefix.
 * Ring slot of position p is p mod ring_slots.
-* Splits are contiguous runs of 64-key tiles starting at the tile holding the
-  lowest visible key, balanced to within one tile: with q = T // S and
-  r = T % S, split s takes q + 1 tiles if s < r and q tiles otherwise, in
-  order.
+* Splits are contiguous runs of 32-key chunks starting at the chunk holding
+  the lowest visible key, balanced to within one chunk: with q = C // S and
+  r = C % S (C chunks), split s takes q + 1 chunks if s < r and q chunks
+  otherwise, in order.  (The pages fix the 64-slot tile of the read and the
+  ring, not the unit a split boundary falls on.)
 """
 
 import numpy as np
 
-TILE = 64
+SPLIT_KEYS = 32  # keys per split granule
 
 CAUSAL = "causal"
 WINDOW = "window"
@@ -153,19 +154,19 @@ def visible_matrix(p, lo, hi):
 
 
 def split_key_ranges(lo, hi, splits):
-    """Key range [a, b) of each split: contiguous 64-key tiles, balanced."""
+    """Key range [a, b) of each split: contiguous 32-key chunks, balanced."""
     if hi <= lo:
         return [(0, 0)] * splits
-    t_lo = lo // TILE
-    t_hi = -(-hi // TILE)
-    n = t_hi - t_lo
+    c_lo = lo // SPLIT_KEYS
+    c_hi = -(-hi // SPLIT_KEYS)
+    n = c_hi - c_lo
     out = []
     q, r = divmod(n, splits)
     for s in range(splits):
-        a_t = t_lo + s * q + min(s, r)
-        b_t = a_t + q + (1 if s < r else 0)
-        a = max(lo, a_t * TILE)
-        b = min(hi, b_t * TILE)
+        a_c = c_lo + s * q + min(s, r)
+        b_c = a_c + q + (1 if s < r else 0)
+        a = max(lo, a_c * SPLIT_KEYS)
+        b = min(hi, b_c * SPLIT_KEYS)
         out.append((a, b) if b > a else (a, a))
     return out
 

@@ -46,7 +46,7 @@ class va_plan_info(ctypes.Structure):
     _fields_ = [
         ("splits", ctypes.c_int32), ("matrix_rows", ctypes.c_int32),
         ("lo", ctypes.c_int64), ("hi", ctypes.c_int64),
-        ("tile_lo", ctypes.c_int64), ("tiles", ctypes.c_int64),
+        ("chunk_lo", ctypes.c_int64), ("chunks", ctypes.c_int64),
         ("row_lo", ctypes.c_int64 * VA_MAX_ROWS), ("row_hi", ctypes.c_int64 * VA_MAX_ROWS),
         ("anc", ctypes.c_uint32 * VA_MAX_ROWS), ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -145,7 +145,7 @@ def verify_attn_plan_query(plan):
     _check("verify_attn_plan_query", _lib().verify_attn_plan_query(ctypes.byref(plan.plan), ctypes.byref(info)))
     return {
         "splits": info.splits, "matrix_rows": info.matrix_rows, "lo": info.lo, "hi": info.hi,
-        "tile_lo": info.tile_lo, "tiles": info.tiles, "row_lo": list(info.row_lo), "row_hi": list(info.row_hi),
+        "chunk_lo": info.chunk_lo, "chunks": info.chunks, "row_lo": list(info.row_lo), "row_hi": list(info.row_hi),
         "anc": list(info.anc), "workspace_bytes": info.workspace_bytes,
     }
 

@@ -14,21 +14,21 @@
 static inline int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
 static inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Splits: each workgroup streams a contiguous run of tiles, and a workgroup
-// runs its chunks one after another, so the shortest split kernel gives every
-// workgroup as few tiles as possible: one tile per split, up to one
-// workgroup per CU over all KV heads (more than one per CU measured slower:
-// the extra partials cost more than the extra overlap gains).  A capped count
-// of 8 or more is kept a multiple of 8, one share per XCD.
-static const int64_t kMinTilesPerSplit = 1;
+// Splits: each workgroup streams a contiguous run of 32-key granules, one
+// after another, so the shortest split kernel gives every workgroup as few
+// granules as possible: one per split, up to one workgroup per CU over all
+// KV heads (more than one per CU measured slower: the extra partials cost
+// more than the extra overlap gains).  A capped count of 8 or more is kept a
+// multiple of 8, one share per XCD.
+static const int64_t kMinChunksPerSplit = 1;
 static const int64_t kWorkgroupsPerCU = 1;
 
-static int32_t choose_splits(int64_t tiles, int32_t kv_heads, int32_t num_cus) {
-  if (tiles <= 0) return 1;
+static int32_t choose_splits(int64_t chunks, int32_t kv_heads, int32_t num_cus) {
+  if (chunks <= 0) return 1;
   if (num_cus <= 0) num_cus = 256;
   int64_t cap = (kWorkgroupsPerCU * num_cus) / kv_heads;
   if (cap < 1) cap = 1;
-  const int64_t want = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+  const int64_t want = (chunks + kMinChunksPerSplit - 1) / kMinChunksPerSplit;
   if (want <= cap) return (int32_t)want;  // every split gets its minimum
   int64_t s = cap;
   if (s >= 8) s = (s / 8) * 8;  // keep whole rounds over the 8 XCDs
@@ -129,9 +129,9 @@ extern "C" va_status verify_attn_plan(const va_problem *p, va_plan *plan, size_t
   }
   if (d.ring_slots == 0 && p->kv_capacity < 0) return VA_ERR_INVALID;
 
-  d.tile_lo = lo / VA_TILE;
-  d.tiles = (hi > lo) ? (hi + VA_TILE - 1) / VA_TILE - d.tile_lo : 0;
-  d.ring_base_slot = d.ring_slots ? (int32_t)((d.tile_lo * VA_TILE) % d.ring_slots) : 0;
+  d.chunk_lo = lo / VA_SPLIT_KEYS;
+  d.chunks = (hi > lo) ? (hi + VA_SPLIT_KEYS - 1) / VA_SPLIT_KEYS - d.chunk_lo : 0;
+  d.ring_base_slot = d.ring_slots ? (int32_t)((d.chunk_lo * VA_SPLIT_KEYS) % d.ring_slots) : 0;
 
   // Keys seen by every live row, where no per-key mask is needed.
   if (p->live_rows > 0) {
@@ -145,7 +145,7 @@ extern "C" va_status verify_attn_plan(const va_problem *p, va_plan *plan, size_t
     d.full_hi = fhi;
   }
 
-  d.splits = p->splits > 0 ? p->splits : choose_splits(d.tiles, d.kv_heads, p->num_cus);
+  d.splits = p->splits > 0 ? p->splits : choose_splits(d.chunks, d.kv_heads, p->num_cus);
 
   const uint64_t units = (uint64_t)d.splits * d.kv_heads * d.matrix_rows;
   d.ml_bytes = ((units * 2 * sizeof(float)) + 255) / 256 * 256;
@@ -170,8 +170,8 @@ extern "C" va_status verify_attn_plan_query(const va_plan *plan, va_plan_info *i
   info->matrix_rows = d->matrix_rows;
   info->lo = d->lo;
   info->hi = d->hi;
-  info->tile_lo = d->tile_lo;
-  info->tiles = d->tiles;
+  info->chunk_lo = d->chunk_lo;
+  info->chunks = d->chunks;
   for (int r = 0; r < VA_MAX_ROWS; ++r) {
     info->row_lo[r] = d->row_lo[r];
     info->row_hi[r] = d->row_hi[r];
@@ -185,12 +185,12 @@ extern "C" va_status verify_attn_plan_split_range(const va_plan *plan, int32_t s
                                                   int64_t *key_end) {
   const va_plan_data *d = as_data(plan);
   if (!d || !key_begin || !key_end || s < 0 || s >= d->splits) return VA_ERR_INVALID;
-  const int64_t T = d->tiles, S = d->splits;
-  const int64_t q = T / S, r = T % S;
-  const int64_t t0 = d->tile_lo + s * q + (s < r ? s : r);
-  const int64_t t1 = t0 + q + (s < r ? 1 : 0);
-  int64_t a = imax64(d->lo, t0 * VA_TILE);
-  int64_t b = imin64(d->hi, t1 * VA_TILE);
+  const int64_t C = d->chunks, S = d->splits;
+  const int64_t q = C / S, r = C % S;
+  const int64_t c0 = d->chunk_lo + s * q + (s < r ? s : r);
+  const int64_t c1 = c0 + q + (s < r ? 1 : 0);
+  int64_t a = imax64(d->lo, c0 * VA_SPLIT_KEYS);
+  int64_t b = imin64(d->hi, c1 * VA_SPLIT_KEYS);
   if (b < a) b = a;
   *key_begin = a;
   *key_end = b;

@@ -13,10 +13,10 @@ struct va_plan_data {
   int32_t group;        // G = Hq / Hkv
   int32_t matrix_rows;  // rows * G
   int32_t mask, kv_fmt, window, ring_slots, splits;
-  int32_t ring_base_slot;  // (tile_lo * 64) mod ring_slots, 0 for a linear cache
+  int32_t ring_base_slot;  // (chunk_lo * 32) mod ring_slots, 0 for a linear cache
   int64_t first_pos, prefix_len, kv_capacity;
   int64_t lo, hi;          // union extent of the live rows' visible keys
-  int64_t tile_lo, tiles;  // tiles [tile_lo, tile_lo + tiles) cover [lo, hi)
+  int64_t chunk_lo, chunks;  // 32-key granules [chunk_lo, chunk_lo + chunks) cover [lo, hi)
   int64_t full_lo, full_hi;  // keys every live row sees, outside the tree part
   int64_t row_lo[VA_MAX_ROWS], row_hi[VA_MAX_ROWS];
   uint32_t anc[VA_MAX_ROWS];

@@ -49,6 +49,7 @@ typedef float f32x2 __attribute__((__vector_size__(8)));
 namespace va_detail {
 
 constexpr int kChunk = 32;  // keys per step
+static_assert(kChunk == VA_SPLIT_KEYS, "a split is a whole number of chunks");
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
 struct SplitArgs {
@@ -61,10 +62,10 @@ struct SplitArgs {
   int64_t kv_head_stride_b;  // bytes
   int64_t kv_row_stride_b;   // bytes
   int64_t v_scale_head_stride;
-  int64_t base;  // absolute position of relative key 0 (= tile_lo * 64)
+  int64_t base;  // absolute position of relative key 0 (= chunk_lo * 32)
   int32_t rows, live_rows, group, mrows, q_heads, kv_heads;
   float inv_group;           // 1 / group (row of matrix row m: (m + 0.5) * inv_group)
-  int32_t splits, tiles, tiles_q, tiles_r;  // tiles_q = tiles / splits, tiles_r = tiles % splits
+  int32_t splits, chunks_q, chunks_r;  // chunks / splits, chunks % splits
   int32_t rel_lo, rel_hi;    // read extent, relative to base
   int32_t full_lo, full_hi;  // every live row sees these keys (relative)
   int32_t ring_slots, ring_base_slot;
@@ -235,8 +236,8 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
   const int kvh = blockIdx.y;
 
   // ---------------- this split's chunk range ----------------
-  // split s takes q + 1 tiles if s < r, else q (q = T / S, r = T % S)
-  const int32_t tq = a.tiles_q, tr = a.tiles_r, rel_lo = a.rel_lo, rel_hi = a.rel_hi;
+  // split s takes q + 1 chunks if s < r, else q (q = C / S, r = C % S)
+  const int32_t cq = a.chunks_q, cr = a.chunks_r, rel_lo = a.rel_lo, rel_hi = a.rel_hi;
   const int32_t ring_slots = a.ring_slots, ring_base = a.ring_base_slot;
   const int64_t kv_base = a.base, row_stride = a.kv_row_stride_b, head_stride = a.kv_head_stride_b;
   const uint8_t *kptr = a.k, *vptr = a.v;
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
   uint32_t anc[VA_MAX_ROWS];
 #pragma unroll
   for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = a.anc[i];
-  pin(tq), pin(tr), pin(rel_lo), pin(rel_hi), pin(ring_slots), pin(ring_base), pin(kv_base);
+  pin(cq), pin(cr), pin(rel_lo), pin(rel_hi), pin(ring_slots), pin(ring_base), pin(kv_base);
   pin(row_stride), pin(head_stride), pin(kptr), pin(vptr);
   if constexpr (FMT == 1) pin(vsc), pin(vsc_stride);
   pin(inv_group), pin(scale_log2), pin(mrows), pin(live_rows), pin(group), pin(q_heads), pin(tree);
@@ -262,14 +263,10 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
 
   int32_t c_first = 0, nch = 0;
   auto chunk_range = [&]() {
-    const int32_t t0 = split * tq + (split < tr ? split : tr);
-    const int32_t t1 = t0 + tq + (split < tr ? 1 : 0);
-    int32_t c0 = 2 * t0, c1 = 2 * t1;  // in 32-key chunks, relative
-    if (c0 < rel_lo / kChunk) c0 = rel_lo / kChunk;
-    const int32_t c_end_ext = (rel_hi + kChunk - 1) / kChunk;
-    if (c1 > c_end_ext) c1 = c_end_ext;
-    c_first = c0;
-    nch = c1 > c0 ? c1 - c0 : 0;
+    // in chunks relative to base (base is chunk aligned and the chunks cover
+    // [rel_lo, rel_hi) exactly, so no clipping is needed)
+    c_first = split * cq + (split < cr ? split : cr);
+    nch = cq + (split < cr ? 1 : 0);
   };
 
   if (wave >= W) {
@@ -627,22 +624,18 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: grid (rows * Hq, D / 32), 256 threads; a workgroup merges
+// Combine kernel: grid (rows * Hq, D / 32), WAVES wave64s; a workgroup merges
 // 32 consecutive d of one (row, query head).  Thread t owns four of them
-// (dq = t % 8) and the splits s = sg, sg + 32, sg + 64, ... (sg = t / 8),
-// which it folds into four FP32 chains (one per d) against a running maximum
-// that moves only when a batch brings a larger m.  All loads of a batch
-// (BATCH splits: their (m, l) and O) are issued together; the launch picks
-// the smallest BATCH in {1, 2, 4, 8, 16} that covers S in one round, so
-// S <= 512 takes one memory round trip and short reads run few instructions.  The 32 chains of each d are then merged by
-// lane exchanges inside each wave and once through LDS across the four waves,
-// with the sink.
+// (dq = t % 8) and the splits s = sg, sg + NSG, sg + 2*NSG, ... (sg = t / 8,
+// NSG = 8 * WAVES split groups), which it folds into four FP32 chains (one
+// per d) against a running maximum that moves only when a batch brings a
+// larger m.  All loads of a batch (BATCH splits: their (m, l) and O) are
+// issued together.  The chains of each d are then merged by lane exchanges
+// inside each wave and, with four waves, once through LDS; then the sink.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 4096;
-constexpr int kCombThreads = 256;
-constexpr int kCombD = 32;                    // d per workgroup
-constexpr int kCombDQ = kCombD / 4;           // threads per split group
-constexpr int kCombNSG = kCombThreads / kCombDQ;  // split groups
+constexpr int kCombD = 32;           // d per workgroup
+constexpr int kCombDQ = kCombD / 4;  // threads per split group (four d each)
 constexpr int kCombMaxBatch = 16;
 
 // Lane l ^ 8 by DPP row_ror:8 (a rotation by 8 inside each 16-lane row).
@@ -660,10 +653,11 @@ __device__ __forceinline__ float xor_sum3(float x) {
   return wave_sum16x4(x);
 }
 
-template <int BATCH>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs a) {
-  __shared__ f32x4 wacc[kCombThreads / 64][kCombDQ];
-  __shared__ float wm[kCombThreads / 64], wden[kCombThreads / 64];
+template <int BATCH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a) {
+  constexpr int kCombNSG = 8 * WAVES;  // split groups
+  __shared__ f32x4 wacc[WAVES][kCombDQ];
+  __shared__ float wm[WAVES], wden[WAVES];
 
   // every kernel argument loaded in one round trip (see pin())
   const float *ws_ml = a.ws_ml, *ws_o = a.ws_o, *sinkp = a.sink;
@@ -738,28 +732,35 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs
   den = xor_sum3(den * f);
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = xor_sum3(acc[c] * f);
-  if (lane < kCombDQ) {
-    wacc[wave][lane] = acc;
-    if (lane == 0) {
-      wm[wave] = Mw;
-      wden[wave] = den;
+  if constexpr (WAVES > 1) {
+    if (lane < kCombDQ) {
+      wacc[wave][lane] = acc;
+      if (lane == 0) {
+        wm[wave] = Mw;
+        wden[wave] = den;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   if (t < kCombDQ) {  // wave 0, one lane per dq: merge the waves and the sink
     const float sink2 = sinkp ? sinkp[h] * LOG2E_F : -INFINITY;
     float Mt = sink2;
-#pragma unroll
-    for (int i = 0; i < kCombThreads / 64; ++i) Mt = fmaxf(Mt, wm[i]);
-    const float Mu = (Mt == -INFINITY) ? 0.f : Mt;
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
     float dt = 0.f;
+    if constexpr (WAVES > 1) {
 #pragma unroll
-    for (int i = 0; i < kCombThreads / 64; ++i) {
-      const float fi = (wm[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wm[i] - Mu);
-      dt = fmaf(fi, wden[i], dt);
-      const f32x4 c = wacc[i][dq];
+      for (int i = 0; i < WAVES; ++i) Mt = fmaxf(Mt, wm[i]);
+    } else {
+      Mt = fmaxf(Mt, Mw);
+    }
+    const float Mu = (Mt == -INFINITY) ? 0.f : Mt;
+#pragma unroll
+    for (int i = 0; i < WAVES; ++i) {
+      const float wmi = WAVES > 1 ? wm[i] : Mw;
+      const float fi = (wmi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wmi - Mu);
+      dt = fmaf(fi, WAVES > 1 ? wden[i] : den, dt);
+      const f32x4 c = WAVES > 1 ? wacc[i][dq] : acc;
 #pragma unroll
       for (int k = 0; k < 4; ++k) tot[k] = fmaf(fi, c[k], tot[k]);
     }
@@ -773,6 +774,38 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const CombineArgs
       if (lse_lane) lsep[(int64_t)r * q_heads + h] = (Mu + __log2f(dt)) * LN2_F;
     }
   }
+}
+
+// One wave per workgroup while it covers the splits in one batch of at most
+// kComb1WaveBatch (no LDS merge, no barrier); else four waves.  The batch is
+// the smallest power of two that covers S in one round (fewer instructions
+// for short reads); larger S loop over rounds of kCombMaxBatch.
+#ifndef VA_COMB_1WAVE_BATCH
+#define VA_COMB_1WAVE_BATCH 8
+#endif
+constexpr int kComb1WaveBatch = VA_COMB_1WAVE_BATCH;
+
+template <int WAVES>
+hipError_t launch_combine_w(const CombineArgs &a, dim3 grid, int per, hipStream_t stream) {
+  const dim3 block(64 * WAVES);
+  if (per <= 1) {
+    hipLaunchKernelGGL((combine_kernel<1, WAVES>), grid, block, 0, stream, a);
+  } else if (per <= 2) {
+    hipLaunchKernelGGL((combine_kernel<2, WAVES>), grid, block, 0, stream, a);
+  } else if (per <= 4) {
+    hipLaunchKernelGGL((combine_kernel<4, WAVES>), grid, block, 0, stream, a);
+  } else if (per <= 8) {
+    hipLaunchKernelGGL((combine_kernel<8, WAVES>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<kCombMaxBatch, WAVES>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs &a, dim3 grid, int S, hipStream_t stream) {
+  const int per1 = (S + 7) / 8;  // splits per thread with one wave (8 split groups)
+  if (per1 <= kComb1WaveBatch) return launch_combine_w<1>(a, grid, per1, stream);
+  return launch_combine_w<4>(a, grid, (S + 31) / 32, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -872,7 +905,7 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   a.kv_head_stride_b = kv_head_stride * esz;
   a.kv_row_stride_b = kv_row_stride * esz;
   a.v_scale_head_stride = v_scale_head_stride;
-  a.base = d->tile_lo * VA_TILE;
+  a.base = d->chunk_lo * VA_SPLIT_KEYS;
   a.rows = d->rows;
   a.live_rows = d->live_rows;
   a.group = d->group;
@@ -881,9 +914,8 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   a.q_heads = d->q_heads;
   a.kv_heads = d->kv_heads;
   a.splits = d->splits;
-  a.tiles = (int32_t)d->tiles;
-  a.tiles_q = (int32_t)(d->tiles / d->splits);
-  a.tiles_r = (int32_t)(d->tiles % d->splits);
+  a.chunks_q = (int32_t)(d->chunks / d->splits);
+  a.chunks_r = (int32_t)(d->chunks % d->splits);
   a.rel_lo = (int32_t)(d->lo - a.base);
   a.rel_hi = (int32_t)(d->hi - a.base);
   a.full_lo = (int32_t)(d->full_lo - a.base);
@@ -935,22 +967,8 @@ extern "C" va_status verify_attn_combine(const va_plan *plan, const void *worksp
   a.kv_heads = d->kv_heads;
   a.splits = d->splits;
   a.head_dim = d->head_dim;
-  // the smallest batch that covers the splits in one round (fewer
-  // instructions for short reads); larger S loops over rounds of 16
   dim3 grid(d->rows * d->q_heads, d->head_dim / kCombD);
-  const int per = (d->splits + kCombNSG - 1) / kCombNSG;
-  if (per <= 1) {
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kCombThreads), 0, stream, a);
-  } else if (per <= 2) {
-    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(kCombThreads), 0, stream, a);
-  } else if (per <= 4) {
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(kCombThreads), 0, stream, a);
-  } else if (per <= 8) {
-    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(kCombThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(combine_kernel<kCombMaxBatch>, grid, dim3(kCombThreads), 0, stream, a);
-  }
-  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+  return launch_combine(a, grid, d->splits, stream) == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
 extern "C" va_status swa_ring_write(const void *k_new, const void *v_new, int32_t rows, int64_t first_pos,

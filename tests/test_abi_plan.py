@@ -190,11 +190,11 @@ def test_chosen_splits_are_sane():
     for P in (1024, 4096, 16384, 32768, 65536, 131072, 196608):
         plan = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, first_pos=P,
                        kv_capacity=262144, num_cus=256)
-        S, T = plan.splits, plan.info["tiles"]
-        assert 1 <= S <= T and S <= 4096
-        # one tile per split while that fits one workgroup per CU; else a
-        # multiple of 8 workgroups no larger than the CU count
-        if T <= 256:
-            assert S == T
+        S, C = plan.splits, plan.info["chunks"]
+        assert 1 <= S <= C and S <= 4096
+        # one 32-key granule per split while that fits one workgroup per CU;
+        # else a multiple of 8 workgroups no larger than the CU count
+        if C <= 256:
+            assert S == C
         else:
             assert S <= 256 and S % 8 == 0

@@ -135,10 +135,10 @@ def test_config1_tiny_causal():
     """1 KV head, 6 q heads, D 64, 8 rows (5 live) at 1019..1026, read extent
     1,024 keys, capacity 1,032 with the padding rows' slots poisoned, 4 splits."""
     plan, kw, q, k, v, s = linear_case(101, 8, 5, 6, 1, 64, "causal", first_pos=1019, splits=4, extra_cap=5)
-    assert plan.problem.kv_capacity == 1032 and plan.info["hi"] == 1024 and plan.info["tiles"] == 16
+    assert plan.problem.kv_capacity == 1032 and plan.info["hi"] == 1024 and plan.info["chunks"] == 32
     out, lse, ws, ro, rl, p, cache = gpu_and_oracle(plan, kw, q, k, v, s)
     check(out, lse, ro, rl, 5, "config1")
-    # partials against the oracle's split form (same 4 tile-aligned splits)
+    # partials against the oracle's split form (same 4 granule-aligned splits)
     m_g, l_g, O_g = partials(plan, ws)
     m_o, l_o, O_o = oattn.split_partials(p, f64(q), cache, plan.problem.scale, 4)
     live = 5
@@ -548,11 +548,11 @@ def test_single_visible_key_is_exact():
 
 
 @pytest.mark.parametrize("rows,live,Hq,Hkv,D,P,S", [
-    (8, 5, 6, 1, 64, 1019, 64),     # more splits than tiles: empty splits
+    (8, 5, 6, 1, 64, 1019, 64),     # more splits than granules: empty splits
     (16, 16, 2, 2, 64, 777, 0),     # G = 1: 16 matrix rows
     (8, 8, 8, 1, 128, 2500, 0),     # 64 matrix rows: two row groups of two blocks
     (16, 13, 5, 1, 64, 1500, 0),    # 80 matrix rows: third block of the second group empty
-    (16, 16, 6, 1, 128, 63, 0),     # 96 matrix rows, context shorter than a tile
+    (16, 16, 6, 1, 128, 63, 0),     # 96 matrix rows, context shorter than a 64-key tile
     (1, 1, 6, 1, 128, 4095, 0),     # a single row
     (8, 7, 6, 1, 128, 100000, 3),   # few long splits
 ])

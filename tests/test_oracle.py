@@ -152,7 +152,7 @@ def test_split_form_equals_definition(mask, kw):
 
 
 def test_split_form_random_long():
-    """Several tiles and a ragged tail, splits that leave some empty."""
+    """Several 32-key granules and a ragged tail, splits that leave some empty."""
     rng = np.random.default_rng(6)
     p, q, cache = _rand_case(rng, CAUSAL, R=8, live=6, Hkv=1, G=6, D=8, P=1000)
     o, lse = attn.verify_attn_ref(p, q, cache, 0.3, None)
@@ -285,25 +285,28 @@ def test_window_counts():
             assert keys[-1] == t and keys[0] == max(0, t - 4095)
 
 
-@pytest.mark.parametrize("lo,hi", [(0, 1), (0, 64), (0, 1024), (0, 1029), (970, 5100), (5, 6), (63, 65)])
+@pytest.mark.parametrize("lo,hi", [(0, 1), (0, 32), (0, 64), (0, 1024), (0, 1029), (970, 5100), (5, 6),
+                                   (31, 33), (63, 65)])
 def test_split_ranges_partition(lo, hi):
-    T = -(-hi // 64) - lo // 64
-    for S in (1, 2, 3, 4, 8, T, T + 3):
+    C = -(-hi // 32) - lo // 32
+    for S in (1, 2, 3, 4, 8, C, C + 3):
         rr = masks.split_key_ranges(lo, hi, S)
         assert len(rr) == S
         covered = [j for a, b in rr for j in range(a, b)]
         assert covered == list(range(lo, hi))
-        tiles = []
+        chunks = []
         for a, b in rr:
             if b > a:
                 if a != lo:
-                    assert a % 64 == 0
+                    assert a % 32 == 0
                 if b != hi:
-                    assert b % 64 == 0
-                tiles.append(-(-b // 64) - a // 64)
+                    assert b % 32 == 0
+                chunks.append(-(-b // 32) - a // 32)
             else:
-                tiles.append(0)
-        assert max(tiles) - min(tiles) <= 1
+                chunks.append(0)
+        assert max(chunks) - min(chunks) <= 1
+        # the first splits take the extra chunk
+        assert chunks == sorted(chunks, reverse=True)
 
 
 # ---------------------------------------------------------------- ring
