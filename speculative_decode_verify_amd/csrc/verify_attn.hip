@@ -34,6 +34,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "plan_data.h"
 #include "verify_attn.h"
 
@@ -297,58 +299,68 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
     //      spread over all bank groups.  V (INT8) is read bytewise, unswizzled.
     // A chunk's DMA is 2*NDMA instructions: u < NDMA copies K rows
     // [u*RPI, u*RPI + RPI), the rest V; instruction u lands at stage + 1024*u
-    // (the V tile starts NDMA KiB into the stage).  Producer wave pw issues
-    // instructions [pw*U, pw*U + U) of every chunk.
-    const int pw = wave - W;
-    uint32_t off[U];
-    bool isv[U];
+    // (the V tile starts NDMA KiB into the stage).  Producer wave PW issues
+    // instructions [PW*U, PW*U + U) of every chunk; the producer index is a
+    // template constant, so each producer's lane offsets are plain
+    // arithmetic on constants.
+    auto produce = [&](auto pw_const) {
+      constexpr int PW = decltype(pw_const)::value;
+      uint32_t off[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int u = pw * U + i;
-      isv[i] = u >= NDMA;
-      const int t = isv[i] ? u - NDMA : u;
-      const int row = t * RPI + lane / PIECES;
-      const int pos = lane % PIECES;
-      const int f = isv[i] ? (FMT == 0 ? (2 * row) & (PIECES - 2) : 0) : (row & (PIECES - 1));
-      off[i] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ f);
-    }
-    // Chunk n into stage `st` (lane l of instruction u stores 16 bytes at
-    // stage + 1024*u + 16*l), then (quantised values) the chunk's scales.
-    auto issue = [&](int32_t n, int st) {
-      const int32_t c0 = (c_first + n) * kChunk;
-      const int64_t row0 = chunk_row(c0);
-      const uint8_t *kc = kbase + row0 * row_stride;
-      const uint8_t *vc = vbase + row0 * row_stride;
-      uint8_t *stg = smem + st * kStageB + 1024 * pw * U;
-      if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
-#pragma unroll
-        for (int i = 0; i < U; ++i) dma16((isv[i] ? vc : kc) + off[i], stg + 1024 * i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-          const int u = pw * U + i;
-          const int row = (isv[i] ? u - NDMA : u) * RPI + lane / PIECES;
-          const uint32_t x = (uint32_t)clampx(row, c0) * rs;
-          dma16((isv[i] ? vc : kc) + x + (off[i] - (uint32_t)row * rs), stg + 1024 * i);
-        }
+      for (int i = 0; i < U; ++i) {
+        const int u = PW * U + i;
+        const bool isv = u >= NDMA;
+        const int t = isv ? u - NDMA : u;
+        const int row = t * RPI + lane / PIECES;
+        const int pos = lane % PIECES;
+        const int f = isv ? (FMT == 0 ? (2 * row) & (PIECES - 2) : 0) : (row & (PIECES - 1));
+        off[i] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ f);
       }
-      if constexpr (FMT == 1) {
-        const float *sc = vsc + (int64_t)kvh * vsc_stride + row0;
-        dma4(sc + clampx(lane & 31, c0), smem + st * kStageB + 2 * kTileB);
+      // Chunk n into stage `st` (lane l of instruction u stores 16 bytes at
+      // stage + 1024*u + 16*l), then (quantised values) the chunk's scales.
+      auto issue = [&](int32_t n, int st) {
+        const int32_t c0 = (c_first + n) * kChunk;
+        const int64_t row0 = chunk_row(c0);
+        const uint8_t *kc = kbase + row0 * row_stride;
+        const uint8_t *vc = vbase + row0 * row_stride;
+        uint8_t *stg = smem + st * kStageB + 1024 * PW * U;
+        if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
+#pragma unroll
+          for (int i = 0; i < U; ++i) dma16((PW * U + i >= NDMA ? vc : kc) + off[i], stg + 1024 * i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < U; ++i) {
+            const int u = PW * U + i;
+            const int row = (u >= NDMA ? u - NDMA : u) * RPI + lane / PIECES;
+            const uint32_t x = (uint32_t)clampx(row, c0) * rs;
+            dma16((u >= NDMA ? vc : kc) + x + (off[i] - (uint32_t)row * rs), stg + 1024 * i);
+          }
+        }
+        if constexpr (FMT == 1) {
+          const float *sc = vsc + (int64_t)kvh * vsc_stride + row0;
+          dma4(sc + clampx(lane & 31, c0), smem + st * kStageB + 2 * kTileB);
+        }
+      };
+#pragma unroll
+      for (int j = 0; j < NST - 1; ++j)
+        if (j < nch) issue(j, j);
+      int st_prev = NST - 1;  // stage of chunk n - 1
+      for (int32_t n = 0; n < nch; ++n) {
+        // chunks issued after n: n+1 .. min(n + NST - 2, nch - 1); DMA groups
+        // complete in issue order, so this wait leaves exactly those in flight.
+        const int32_t later = nch - 1 - n;
+        wait_chunks<kVmP, NST - 2>(later < NST - 2 ? later : NST - 2);
+        wg_barrier();
+        if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
+        st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
       }
     };
-#pragma unroll
-    for (int j = 0; j < NST - 1; ++j)
-      if (j < nch) issue(j, j);
-    int st_prev = NST - 1;  // stage of chunk n - 1
-    for (int32_t n = 0; n < nch; ++n) {
-      // chunks issued after n: n+1 .. min(n + NST - 2, nch - 1); DMA groups
-      // complete in issue order, so this wait leaves exactly those in flight.
-      const int32_t later = nch - 1 - n;
-      wait_chunks<kVmP, NST - 2>(later < NST - 2 ? later : NST - 2);
-      wg_barrier();
-      if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
-      st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
+    static_assert(NPW == 1 || NPW == 2, "one or two producers");
+    if constexpr (NPW == 1) {
+      produce(std::integral_constant<int, 0>{});
+    } else {
+      if (wave == W) produce(std::integral_constant<int, 0>{});
+      else produce(std::integral_constant<int, 1>{});
     }
     return;
   }
