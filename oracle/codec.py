@@ -15,6 +15,9 @@ silent:
 * Values: one FP32 scale per (token, KV head), s = max|v| / 127; codes are
   round-half-even of v / s clamped to [-127, 127]; s = 0 gives all-zero codes.
   Dequantisation is code * s.
+* Where a code is decided from a rotated key, the rotation is taken in FP32
+  (`wht_f32`, the precision a GPU encoder works in) so that both sides round
+  the same value.
 """
 
 import numpy as np
@@ -71,6 +74,38 @@ def wht(x):
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-1]
     return x @ hadamard(n).T / np.sqrt(n)
+
+
+def wht_f32(x):
+    """The normalised rotation as a GPU computes it in FP32: the fast
+    Walsh-Hadamard transform in natural order, one butterfly stage per bit of
+    the index from the lowest (width 1, 2, 4, ..., n/2), each stage replacing
+    the pair (a, b) at indices (i, i + width) by (a + b, a - b) in float32,
+    then a float32 multiply by float32(1/sqrt(n)).
+
+    Rounding the rotated key to FP8 is decided on this FP32 value, so an
+    encoder in FP32 and this function must agree bit for bit; the float64
+    `wht` is the definition it approximates (to FP32 rounding).
+    """
+    y = np.array(x, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    if n & (n - 1):
+        raise ValueError("length must be a power of two")
+    width = 1
+    while width < n:
+        z = y.reshape(y.shape[:-1] + (n // (2 * width), 2, width))
+        a = z[..., 0, :].copy()
+        b = z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(y.shape)
+        width *= 2
+    return y * np.float32(1.0 / np.sqrt(n))
+
+
+def encode_keys_f32(k):
+    """E4M3FN codes of the FP32-rotated keys: e4m3_encode(wht_f32(k))."""
+    return e4m3_encode(wht_f32(k).astype(np.float64))
 
 
 def i8_encode(v):

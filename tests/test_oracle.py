@@ -384,6 +384,45 @@ def test_e4m3_encode_saturates_and_midpoints():
     assert codec.e4m3_encode(np.array([np.nan])).tolist() == [0x7F]
 
 
+def test_wht_f32_exact_on_integers():
+    """Small integer inputs keep every butterfly exact in FP32, so the FP32
+    rotation is exactly float32(H x) * float32(1/sqrt(128)) with H the
+    Sylvester matrix from scipy -- any wrong pairing or sign fails."""
+    rng = np.random.default_rng(21)
+    x = rng.integers(-50, 51, size=(40, 128)).astype(np.float64)
+    exact = (x @ scipy.linalg.hadamard(128).T).astype(np.float32)
+    want = exact * np.float32(1.0 / math.sqrt(128))
+    got = codec.wht_f32(x.astype(np.float32))
+    assert got.dtype == np.float32
+    assert np.array_equal(got.view(np.int32), want.view(np.int32))
+
+
+def test_wht_f32_within_fp32_rounding_of_definition():
+    """Seven FP32 butterfly stages and one multiply: each output is within
+    8 * 2^-24 * sum|x| / sqrt(128) + 2^-24 |y| of the float64 rotation."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((64, 128)) * rng.choice([1e-3, 1.0, 40.0], size=(64, 1))).astype(np.float32)
+    y = codec.wht(x.astype(np.float64))
+    got = codec.wht_f32(x).astype(np.float64)
+    bound = 8 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True) / math.sqrt(128) \
+        + 2.0 ** -24 * np.abs(y)
+    assert np.all(np.abs(got - y) <= bound)
+    assert np.abs(got - y).max() > 0  # FP32, not a float64 computation in disguise
+
+
+def test_encode_keys_f32_is_the_rotation_then_e4m3():
+    rng = np.random.default_rng(23)
+    x = rng.integers(-3, 4, size=(16, 128)).astype(np.float32)  # FP32-exact rotation
+    assert np.array_equal(codec.encode_keys_f32(x), codec.e4m3_encode(codec.wht(x.astype(np.float64))))
+    # a one-hot key rotates to +-c/sqrt(128) everywhere: one code magnitude, signs from H's column
+    k = np.zeros((1, 128), np.float32)
+    k[0, 5] = 2.0
+    codes = codec.encode_keys_f32(k)[0]
+    mag = codec.e4m3_encode(np.array([2.0 / math.sqrt(128)]))[0]
+    signs = scipy.linalg.hadamard(128)[:, 5] < 0
+    assert np.array_equal(codes, np.where(signs, mag | 0x80, mag).astype(np.uint8))
+
+
 def test_wht_vs_scipy_and_orthonormal():
     H = codec.hadamard(128)
     assert np.array_equal(H, scipy.linalg.hadamard(128))
