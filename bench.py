@@ -157,6 +157,90 @@ def summarize_profiles(d):
     open(name, "w").write("\n".join(out) + "\n")
     print(f"wrote {name} and {TRAFFIC_FILE}")
 
+    kt = os.path.join(d, "trace_kvw", "kvw_kernel_trace.csv")
+    if os.path.exists(kt):
+        rows = [r for r in csv.DictReader(open(kt)) if "kv_write_kernel" in r["Kernel_Name"]]
+        by = collections.defaultdict(list)
+        for r in rows:
+            n = r["Kernel_Name"]
+            by[n[n.index("kv_write_kernel"):n.index(">") + 1].replace(" ", "")].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        kl = None
+        for line in open(os.path.join(d, "kvw.log")):
+            if line.startswith("{") and "verify_kv_write" in line:
+                kl = json.loads(line)
+        if kl is None or kl["kernel_hash"] != kernel_hash():
+            raise SystemExit("kv-write profile missing or of another kernel source")
+        o = ["# kv_write_kernel, the rows' KV written before the read (window ring bf16; tree cache E4M3 + INT8)", "",
+             f"kernel source sha256[:16]: {kernel_hash()}", "",
+             f"command: rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace_kvw -o kvw -- {py} --kv-write", "",
+             "| kernel | launches | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for k, v in sorted(by.items()):
+            o.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        o += ["", "bench line of the same command (graph replay, events; slowed by the trace):", ""]
+        for c in kl["cases"]:
+            o.append(f"- {c['case']}: {c['rows']} rows x {c['kv_heads']} KV heads x D {c['head_dim']}: "
+                     f"{c['us_per_call']} us per call, {c['bytes_per_call']} bytes moved")
+        plain = os.path.join(d, "kvw_plain.log")
+        if os.path.exists(plain):
+            for line in open(plain):
+                if line.startswith("{") and "verify_kv_write" in line:
+                    pl = json.loads(line)
+                    o += ["", f"the same without the profiler ({py} --kv-write):", ""]
+                    for c in pl["cases"]:
+                        o.append(f"- {c['case']}: {c['us_per_call']} us per call")
+        kname = os.path.join(ROOT, "profiles", "kv_write_kernel_ring_and_tree_cache.md")
+        open(kname, "w").write("\n".join(o) + "\n")
+        print(f"wrote {kname}")
+
+
+def bench_kv_write(torch, va, synth, dev, reps=200):
+    """Time verify_kv_write at the configurations that write rows before the
+    read: the window ring (bf16, 8 rows, 1 KV head, D 64, 4160 slots) and the
+    quantised tree cache (16 rows, 4 KV heads, D 128, at a 64K prefix), from a
+    graph of back-to-back launches.  Prints one JSON line (not the sweep's)."""
+    cases = []
+    g = synth.gen(9100)
+    for name, rows, hkv, d, quant, first_pos, ring in (
+            ("window ring, bf16", 8, 1, 64, False, 194560, 4160),
+            ("tree cache, E4M3 keys + INT8 values", 16, 4, 128, True, 65536, 0)):
+        k_new = synth.normal_bf16((rows, hkv, d), g).to(dev)
+        v_new = synth.normal_bf16((rows, hkv, d), g).to(dev)
+        slots = ring if ring else first_pos + rows + 64
+        if quant:
+            kc = torch.zeros((hkv, slots, d), dtype=torch.uint8, device=dev)
+            vc = torch.zeros((hkv, slots, d), dtype=torch.int8, device=dev)
+            vs = torch.zeros((hkv, slots), dtype=torch.float32, device=dev)
+            moved = rows * hkv * (2 * d * 2 + 2 * d + 4)   # bf16 rows in, codes + scale out
+        else:
+            kc = torch.zeros((hkv, slots, d), dtype=torch.bfloat16, device=dev)
+            vc = torch.zeros((hkv, slots, d), dtype=torch.bfloat16, device=dev)
+            vs = None
+            moved = rows * hkv * 2 * d * 2 * 2             # bf16 rows in and out
+        cases.append((name, rows, hkv, d, first_pos, ring, k_new, v_new, kc, vc, vs, moved))
+    out = []
+    for name, rows, hkv, d, first_pos, ring, k_new, v_new, kc, vc, vs, moved in cases:
+        def launches():
+            for _ in range(reps):
+                va.verify_kv_write(k_new, v_new, first_pos, kc, vc, v_scale=vs, ring_slots=ring,
+                                   stream=torch.cuda.current_stream())
+        launches()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            launches()
+        gr.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        out.append({"case": name, "rows": rows, "kv_heads": hkv, "head_dim": d, "us_per_call": round(us, 3),
+                    "bytes_per_call": moved, "gb_s": round(moved / (us * 1e-6) / 1e9, 2)})
+    print(json.dumps({"metric": "verify_kv_write us/call", "unit": "us", "higher_is_better": False,
+                      "launch": "HIP graph replay, back to back", "cases": out,
+                      "kernel_hash": kernel_hash()}), flush=True)
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -171,6 +255,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time to spend on the CPU baseline")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from one profiling session's outputs (no GPU)")
+    ap.add_argument("--kv-write", action="store_true",
+                    help="only time verify_kv_write (the rows' KV written into the cache before the read)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -199,6 +285,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.kv_write:
+        bench_kv_write(torch, va, synth, dev)
         return
     contexts = args.ctx or CONTEXTS
     stream = torch.cuda.current_stream()

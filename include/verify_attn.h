@@ -27,7 +27,8 @@
  *   VA_MASK_WINDOW  row r at t sees max(0, t-window+1)..t.  The keys live in
  *                   a ring of ring_slots slots (position p in slot
  *                   p mod ring_slots) or, with ring_slots = 0, in a linear
- *                   cache.  swa_ring_write stores the rows' own K/V first.
+ *                   cache.  swa_ring_write (bf16) or verify_kv_write (any
+ *                   format) stores the rows' own K/V first.
  *   VA_MASK_TREE    node i's key sits at position prefix_len + i; row i sees
  *                   0..prefix_len-1, its tree ancestors and itself.
  *   Rows live_rows..rows-1 are padding: they see nothing, never widen the
@@ -193,6 +194,42 @@ va_status swa_ring_write(const void *k_new, const void *v_new, int32_t rows, int
                          int32_t kv_heads, int32_t head_dim, void *k_ring, void *v_ring,
                          int32_t ring_slots, int64_t kv_head_stride, int64_t kv_row_stride,
                          hipStream_t stream);
+
+/* Write the verification rows' own K/V into a KV cache before the read, in
+ * the cache's storage format (4090 post, "A cheaper cache and state": keys in
+ * FP8 after a Hadamard rotation, values in INT8 with one scale per token and
+ * KV head; IQuestRT report, "Read only the KV tiles needed by the current
+ * positions": the rows are written before the read).  Row r of KV head g
+ * goes to slot first_pos + r of a linear cache (ring_slots = 0) or to slot
+ * (first_pos + r) mod ring_slots of a ring.  All `rows` rows are written,
+ * padding included.
+ *   k_new, v_new  [rows, kv_heads, head_dim] bf16, contiguous.
+ *   kv_fmt        VA_KV_BF16: the rows are copied.
+ *                 VA_KV_K_E4M3_WHT_V_I8 (head_dim 128): k' = H k / sqrt(128)
+ *                 is formed in FP32 by the fast transform (butterflies of
+ *                 width 1, 2, ..., 64, each (a, b) -> (a + b, a - b), then a
+ *                 multiply by FP32 1/sqrt(128)) and stored as the nearest
+ *                 E4M3FN code (ties to even, saturating at 448, sign kept);
+ *                 s = max|v| / 127 in FP32 goes to v_scale and each value is
+ *                 stored as the round-half-even of v / s (taken in FP64)
+ *                 clamped to [-127, 127] (all codes 0 when s = 0).
+ *   k_cache, v_cache  [kv_heads, slots, head_dim]: bf16, or uint8 (keys) and
+ *                 int8 (values) codes, element strides kv_head_stride and
+ *                 kv_row_stride, 16-byte aligned rows.
+ *   v_scale       [kv_heads, slots] FP32 with head stride v_scale_head_stride
+ *                 (quantised format), else ignored.
+ *   kv_capacity   linear cache: slots per KV head; must hold first_pos + rows.
+ * Errors: VA_ERR_INVALID (rows outside 0..4096, kv_heads < 1, head_dim not
+ * 64/128, unknown kv_fmt, negative first_pos, ring_slots < rows or not a
+ * multiple of 64, NULL or misaligned pointers, bad strides),
+ * VA_ERR_UNSUPPORTED (quantised format with head_dim != 128),
+ * VA_ERR_CAPACITY (linear cache smaller than first_pos + rows), VA_ERR_HIP.
+ * rows == 0 is a no-op. */
+va_status verify_kv_write(const void *k_new, const void *v_new, int32_t rows, int64_t first_pos,
+                          int32_t kv_heads, int32_t head_dim, int32_t kv_fmt, void *k_cache,
+                          void *v_cache, float *v_scale, int64_t v_scale_head_stride,
+                          int64_t kv_capacity, int32_t ring_slots, int64_t kv_head_stride,
+                          int64_t kv_row_stride, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *va_status_string(va_status s);

@@ -75,10 +75,11 @@ def load_library():
     lib.verify_attn_split.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, I64, I64, I64, V, SZ, V]
     lib.verify_attn_combine.argtypes = [ctypes.POINTER(va_plan), V, SZ, V, V, V, V]
     lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
+    lib.verify_kv_write.argtypes = [V, V, I32, I64, I32, I32, I32, V, V, V, I64, I64, I32, I64, I64, V]
     lib.va_status_string.argtypes = [ctypes.c_int]
     lib.va_status_string.restype = ctypes.c_char_p
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
-               "verify_attn_split", "verify_attn_combine", "swa_ring_write"):
+               "verify_attn_split", "verify_attn_combine", "swa_ring_write", "verify_kv_write"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -249,6 +250,38 @@ def swa_ring_write(k_new, v_new, first_pos, k_ring, v_ring, stream=None):
     _check("swa_ring_write", _lib().swa_ring_write(
         _ptr(k_new), _ptr(v_new), rows, first_pos, hkv, d, _ptr(k_ring), _ptr(v_ring), k_ring.shape[1],
         k_ring.stride(0), k_ring.stride(1), _stream(stream)))
+
+
+def verify_kv_write(k_new, v_new, first_pos, k_cache, v_cache, v_scale=None, ring_slots=0, stream=None):
+    """k_new, v_new [rows, Hkv, D] bf16 contiguous.  k_cache, v_cache
+    [Hkv, slots, D]: bf16 (copied), or uint8 keys / int8 values (encoded,
+    with v_scale [Hkv, slots] float32).  ring_slots = 0 writes slot
+    first_pos + r of a linear cache, else (first_pos + r) mod ring_slots."""
+    import torch
+    _require(k_new, "k_new", (torch.bfloat16,))
+    _require(v_new, "v_new", (torch.bfloat16,))
+    if not (k_new.is_contiguous() and v_new.is_contiguous()) or k_new.shape != v_new.shape or k_new.dim() != 3:
+        raise ValueError("k_new/v_new must be contiguous [rows, Hkv, D]")
+    if k_cache.dtype == torch.bfloat16:
+        fmt = 0
+        _require(v_cache, "v_cache", (torch.bfloat16,))
+    else:
+        fmt = 1
+        _require(k_cache, "k_cache", (torch.uint8,))
+        _require(v_cache, "v_cache", (torch.int8,))
+        _require(v_scale, "v_scale", (torch.float32,))
+        if v_scale.dim() != 2 or v_scale.stride(1) != 1 or v_scale.shape[1] < k_cache.shape[1]:
+            raise ValueError("v_scale must be [Hkv, slots] with contiguous rows")
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride() or k_cache.dim() != 3 \
+            or k_cache.stride(2) != 1:
+        raise ValueError("k_cache/v_cache must share shape and strides, rows contiguous")
+    rows, hkv, d = k_new.shape
+    if k_cache.shape[0] != hkv or k_cache.shape[2] != d:
+        raise ValueError("cache shape does not match the new rows")
+    _check("verify_kv_write", _lib().verify_kv_write(
+        _ptr(k_new), _ptr(v_new), rows, first_pos, hkv, d, fmt, _ptr(k_cache), _ptr(v_cache), _ptr(v_scale),
+        v_scale.stride(0) if v_scale is not None else 0, k_cache.shape[1], ring_slots,
+        k_cache.stride(0), k_cache.stride(1), _stream(stream)))
 
 
 def verify_attn(plan, q, k, v, sink=None, v_scale=None, workspace=None, out=None, lse=None, stream=None):

@@ -842,6 +842,84 @@ __global__ __launch_bounds__(256) void ring_write_kernel(const uint8_t *k_new, c
 }
 
 // ---------------------------------------------------------------------------
+// KV write with the cache's codec: one wave per (row, KV head).
+// ---------------------------------------------------------------------------
+// E4M3FN code of y: nearest finite value, ties to the even code, saturating
+// at 448, sign copied from y.  Integer-exact: the mantissa is rounded as
+// rint(|y| * 2^(3 - e)) in [8, 16] for |y| >= 2^-6 (e = floor(log2 |y|); a
+// carry to 16 moves to the next binade), and as rint(|y| * 2^9) for the
+// subnormal step 2^-9 below; both scalings are exact powers of two.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 31) << 7;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);  // 0..8; 8 is the smallest normal 2^-6
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a is a normal FP32 here
+    uint32_t r = (uint32_t)rintf(a * __uint_as_float((uint32_t)(127 + 3 - e) << 23));
+    if (r == 16u) {
+      r = 8u;
+      e += 1;
+    }
+    code = ((uint32_t)(e + 7) << 3) | (r - 8u);
+  }
+  return sign | code;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64) void kv_write_kernel(const uint16_t *k_new, const uint16_t *v_new, int kv_heads,
+                                                      int head_dim, uint8_t *k_cache, uint8_t *v_cache, float *v_scale,
+                                                      int64_t v_scale_head_stride, int64_t first_pos, int ring_slots,
+                                                      int64_t head_stride_b, int64_t row_stride_b) {
+  const int r = blockIdx.x / kv_heads, g = blockIdx.x % kv_heads;
+  const int lane = threadIdx.x;
+  const int64_t pos = first_pos + r;
+  const int64_t slot = ring_slots ? pos % ring_slots : pos;
+  const int64_t src = ((int64_t)r * kv_heads + g) * head_dim;  // elements
+  const int64_t dst = (int64_t)g * head_stride_b + slot * row_stride_b;  // bytes
+  if constexpr (FMT == 0) {
+    const int pieces = head_dim / 8;  // 16-byte pieces per row
+    if (lane < pieces) {
+      *(u32x4 *)(k_cache + dst + 16 * lane) = *(const u32x4 *)(k_new + src + 8 * lane);
+      *(u32x4 *)(v_cache + dst + 16 * lane) = *(const u32x4 *)(v_new + src + 8 * lane);
+    }
+  } else {
+    // head_dim 128: lane l holds elements 2l and 2l + 1.
+    const uint32_t kw = *(const uint32_t *)(k_new + src + 2 * lane);
+    const uint32_t vw = *(const uint32_t *)(v_new + src + 2 * lane);
+    float x0 = __uint_as_float(kw << 16), x1 = __uint_as_float(kw & 0xffff0000u);
+    // width 1 inside the lane, then widths 2..64 pair lane l with l ^ (width/2)
+    float y0 = x0 + x1, y1 = x0 - x1;
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+      const float p0 = __shfl_xor(y0, h, 64), p1 = __shfl_xor(y1, h, 64);
+      const bool upper = (lane & h) != 0;
+      y0 = upper ? p0 - y0 : y0 + p0;
+      y1 = upper ? p1 - y1 : y1 + p1;
+    }
+    const float inv = 0.08838834764831845f;  // 1/sqrt(128)
+    const uint32_t kc = e4m3_code(y0 * inv) | (e4m3_code(y1 * inv) << 8);
+    *(uint16_t *)(k_cache + dst + 2 * lane) = (uint16_t)kc;
+
+    const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) amax = fmaxf(amax, __shfl_xor(amax, h, 64));
+    const float sc = amax / 127.f;  // IEEE division, correctly rounded
+    int c0 = 0, c1 = 0;
+    if (sc != 0.f) {
+      c0 = (int)rint((double)v0 / (double)sc);
+      c1 = (int)rint((double)v1 / (double)sc);
+      c0 = c0 < -127 ? -127 : (c0 > 127 ? 127 : c0);
+      c1 = c1 < -127 ? -127 : (c1 > 127 ? 127 : c1);
+    }
+    *(uint16_t *)(v_cache + dst + 2 * lane) = (uint16_t)((uint32_t)(c0 & 0xff) | ((uint32_t)(c1 & 0xff) << 8));
+    if (lane == 0) v_scale[(int64_t)g * v_scale_head_stride + slot] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 const va_plan_data *plan_of(const va_plan *plan) {
@@ -1001,5 +1079,39 @@ extern "C" va_status swa_ring_write(const void *k_new, const void *v_new, int32_
                      (const uint8_t *)k_new, (const uint8_t *)v_new, rows, kv_heads, head_dim,
                      (uint8_t *)k_ring, (uint8_t *)v_ring, ring_slots, slot0, kv_head_stride * 2,
                      kv_row_stride * 2);
+  return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+extern "C" va_status verify_kv_write(const void *k_new, const void *v_new, int32_t rows, int64_t first_pos,
+                                     int32_t kv_heads, int32_t head_dim, int32_t kv_fmt, void *k_cache,
+                                     void *v_cache, float *v_scale, int64_t v_scale_head_stride,
+                                     int64_t kv_capacity, int32_t ring_slots, int64_t kv_head_stride,
+                                     int64_t kv_row_stride, hipStream_t stream) {
+  if (rows < 0 || rows > 4096) return VA_ERR_INVALID;
+  if (kv_heads < 1 || first_pos < 0) return VA_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return VA_ERR_INVALID;
+  if (kv_fmt != VA_KV_BF16 && kv_fmt != VA_KV_K_E4M3_WHT_V_I8) return VA_ERR_INVALID;
+  const bool quant = kv_fmt == VA_KV_K_E4M3_WHT_V_I8;
+  if (quant && head_dim != 128) return VA_ERR_UNSUPPORTED;
+  if (ring_slots < 0 || (ring_slots > 0 && (ring_slots < rows || ring_slots % VA_TILE != 0))) return VA_ERR_INVALID;
+  if (rows == 0) return VA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache) return VA_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return VA_ERR_INVALID;
+  const int64_t esz = quant ? 1 : 2;
+  if (kv_head_stride < 0 || kv_row_stride < head_dim) return VA_ERR_INVALID;
+  if (((kv_head_stride * esz) & 15) || ((kv_row_stride * esz) & 15)) return VA_ERR_INVALID;
+  if (quant && (!v_scale || v_scale_head_stride < 0)) return VA_ERR_INVALID;
+  if (ring_slots == 0 && kv_capacity < first_pos + rows) return VA_ERR_CAPACITY;
+  const dim3 grid((unsigned)rows * (unsigned)kv_heads);
+  if (quant) {
+    hipLaunchKernelGGL(kv_write_kernel<1>, grid, dim3(64), 0, stream, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, kv_heads, head_dim, (uint8_t *)k_cache, (uint8_t *)v_cache,
+                       v_scale, v_scale_head_stride, first_pos, ring_slots, kv_head_stride, kv_row_stride);
+  } else {
+    hipLaunchKernelGGL(kv_write_kernel<0>, grid, dim3(64), 0, stream, (const uint16_t *)k_new,
+                       (const uint16_t *)v_new, kv_heads, head_dim, (uint8_t *)k_cache, (uint8_t *)v_cache,
+                       v_scale, v_scale_head_stride, first_pos, ring_slots, kv_head_stride * 2,
+                       kv_row_stride * 2);
+  }
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
