@@ -432,7 +432,7 @@ def main():
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "split_kernel<D=128,W=3,bf16,NST=4,NPW=2>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
+                "kernel": "split_kernel<D=128,W=3,bf16,NST=4,NPW=2,STATE=false>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
                 "avg_launch_us": round(split_ms / launches * 1e3, 2), "launches": launches}
 
     # ---------------- CPU baseline (oracle) + full-size parity ----------------

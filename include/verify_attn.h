@@ -179,6 +179,46 @@ va_status verify_attn_split(const va_plan *plan, const void *q, const void *k, c
 va_status verify_attn_combine(const va_plan *plan, const void *workspace, size_t workspace_bytes,
                               const float *sink, float *out, float *lse, hipStream_t stream);
 
+/* Per-call state in device memory, for calls whose positions and row count
+ * are produced on the device (IQuestRT report, "IQuestRT execution": lengths
+ * stay on the device and the step is launched from graphs).  A plan built for
+ * a bucket -- the largest extent the state may describe -- fixes the grid and
+ * the workspace; each call then reads this record, and the kernels derive the
+ * row intervals, the read extent, the split table and the tree's ancestor
+ * bits from it on the device.  Fields have the meaning of the va_problem
+ * fields of the same name; the rest of the problem comes from the plan. */
+typedef struct {
+  int64_t first_pos;             /* causal/window: position of row 0                       */
+  int64_t prefix_len;            /* tree: committed keys 0..P-1                              */
+  int32_t live_rows;             /* 0..rows                                                  */
+  int32_t reserved;              /* 0                                                        */
+  int32_t parent[VA_MAX_ROWS];   /* tree: -1, or an index below the node's own               */
+} va_state;
+
+/* verify_attn_split and verify_attn_combine with the per-call state read from
+ * device memory (`state`, 8-byte aligned, written before the call on the same
+ * stream).  The plan's problem gives the bucket: the keys a state reads,
+ * [lo, hi) as va_plan_info defines them for the state's own problem, must end
+ * at or below the plan's hi (the plan has checked that key range against
+ * kv_capacity, or against the ring, whose size covers any window state of at
+ * most `rows` rows).  With C the state's 32-key granules, the split count is
+ * min(S, C) for the plan's S (at least 1); the workgroups above it exit
+ * without reading, so a short state in a long bucket reads only its own keys.
+ * The launch configuration depends on the plan alone, so both calls can be
+ * captured in a graph once and replayed for every state of the bucket.
+ * A state outside the bucket, or with live_rows outside [0, rows], a
+ * position outside [0, 2^61], reserved != 0 or (tree) a parent out of range,
+ * reads no key: the combine writes NaN to every output element and lse.
+ * Errors (returned): as verify_attn_split / verify_attn_combine, plus
+ * VA_ERR_INVALID for a NULL or misaligned state. */
+va_status verify_attn_split_state(const va_plan *plan, const va_state *state, const void *q, const void *k,
+                                  const void *v, const float *v_scale, int64_t v_scale_head_stride,
+                                  int64_t kv_head_stride, int64_t kv_row_stride, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+va_status verify_attn_combine_state(const va_plan *plan, const va_state *state, const void *workspace,
+                                    size_t workspace_bytes, const float *sink, float *out, float *lse,
+                                    hipStream_t stream);
+
 /* Store the verification rows' own K/V into the sliding-window ring before
  * the read (IQuestRT report, "Read only the KV tiles needed by the current
  * positions"; "Let correctness checks change the design"): row r's K/V, for

@@ -38,6 +38,14 @@ class va_problem(ctypes.Structure):
     ]
 
 
+class va_state(ctypes.Structure):
+    _fields_ = [
+        ("first_pos", ctypes.c_int64), ("prefix_len", ctypes.c_int64),
+        ("live_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("parent", ctypes.c_int32 * VA_MAX_ROWS),
+    ]
+
+
 class va_plan(ctypes.Structure):
     _fields_ = [("words", ctypes.c_uint64 * 256)]
 
@@ -74,12 +82,15 @@ def load_library():
                                                  ctypes.POINTER(I64)]
     lib.verify_attn_split.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, I64, I64, I64, V, SZ, V]
     lib.verify_attn_combine.argtypes = [ctypes.POINTER(va_plan), V, SZ, V, V, V, V]
+    lib.verify_attn_split_state.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, I64, V, SZ, V]
+    lib.verify_attn_combine_state.argtypes = [ctypes.POINTER(va_plan), V, V, SZ, V, V, V, V]
     lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
     lib.verify_kv_write.argtypes = [V, V, I32, I64, I32, I32, I32, V, V, V, I64, I64, I32, I64, I64, V]
     lib.va_status_string.argtypes = [ctypes.c_int]
     lib.va_status_string.restype = ctypes.c_char_p
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
-               "verify_attn_split", "verify_attn_combine", "swa_ring_write", "verify_kv_write"):
+               "verify_attn_split", "verify_attn_combine", "verify_attn_split_state",
+               "verify_attn_combine_state", "swa_ring_write", "verify_kv_write"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -185,7 +196,30 @@ def workspace_for(plan, device=None):
     return torch.empty(max(n, 1), dtype=torch.float32, device=device or "cuda")
 
 
-def verify_attn_split(plan, q, k, v, workspace, v_scale=None, stream=None):
+def pack_state(first_pos=0, prefix_len=0, live_rows=0, parent=None):
+    """The 88-byte va_state record as a CPU int64 tensor of 11 words (copy it
+    into a device tensor of the same shape between graph replays)."""
+    import torch
+    st = va_state()
+    st.first_pos, st.prefix_len, st.live_rows, st.reserved = first_pos, prefix_len, live_rows, 0
+    par = list(parent) if parent is not None else []
+    if len(par) > VA_MAX_ROWS:
+        raise ValueError("at most 16 tree nodes")
+    for i in range(VA_MAX_ROWS):
+        st.parent[i] = par[i] if i < len(par) else -1
+    t = torch.empty(ctypes.sizeof(va_state) // 8, dtype=torch.int64)
+    ctypes.memmove(t.data_ptr(), ctypes.byref(st), ctypes.sizeof(va_state))
+    return t
+
+
+def _require_state(state):
+    import torch
+    _require(state, "state", (torch.int64,))
+    if not state.is_contiguous() or state.numel() * 8 != ctypes.sizeof(va_state):
+        raise ValueError("state must be a contiguous int64 tensor of 11 words (a packed va_state)")
+
+
+def _split_args(plan, q, k, v, workspace, v_scale):
     """q [rows, Hq, D] bf16 contiguous; k, v [Hkv, slots, D] (bf16, or uint8/int8
     for the quantised format) with the last dimension contiguous; v_scale
     [Hkv, slots] float32 for the quantised format."""
@@ -207,14 +241,25 @@ def verify_attn_split(plan, q, k, v, workspace, v_scale=None, stream=None):
     if k.dim() != 3 or k.shape[0] != plan.kv_heads or k.shape[2] != plan.head_dim or k.stride(2) != 1:
         raise ValueError(f"k/v must be [{plan.kv_heads}, slots, {plan.head_dim}] with contiguous rows")
     _require(workspace, "workspace", (torch.float32,))
-    ws_bytes = workspace.numel() * 4
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(v_scale), v_scale.stride(0) if v_scale is not None else 0,
+            k.stride(0), k.stride(1), _ptr(workspace), workspace.numel() * 4)
+
+
+def verify_attn_split(plan, q, k, v, workspace, v_scale=None, stream=None):
+    """Partial attention of every split (shapes as in _split_args)."""
     _check("verify_attn_split", _lib().verify_attn_split(
-        ctypes.byref(plan.plan), _ptr(q), _ptr(k), _ptr(v), _ptr(v_scale),
-        v_scale.stride(0) if v_scale is not None else 0, k.stride(0), k.stride(1),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+        ctypes.byref(plan.plan), *_split_args(plan, q, k, v, workspace, v_scale), _stream(stream)))
 
 
-def verify_attn_combine(plan, workspace, out, lse=None, sink=None, stream=None):
+def verify_attn_split_state(plan, state, q, k, v, workspace, v_scale=None, stream=None):
+    """verify_attn_split with positions, live rows and tree read on the device
+    from `state` (a device copy of pack_state(...)) when the kernel runs."""
+    _require_state(state)
+    _check("verify_attn_split_state", _lib().verify_attn_split_state(
+        ctypes.byref(plan.plan), _ptr(state), *_split_args(plan, q, k, v, workspace, v_scale), _stream(stream)))
+
+
+def _combine_args(plan, workspace, out, lse, sink):
     """out [rows, Hq, D] float32 contiguous; lse [rows, Hq] float32 or None;
     sink [Hq] float32 or None."""
     import torch
@@ -230,9 +275,20 @@ def verify_attn_combine(plan, workspace, out, lse=None, sink=None, stream=None):
         _require(sink, "sink", (torch.float32,))
         if not sink.is_contiguous() or sink.numel() != plan.q_heads:
             raise ValueError("sink must be contiguous [Hq] float32")
+    return _ptr(workspace), workspace.numel() * 4, _ptr(sink), _ptr(out), _ptr(lse)
+
+
+def verify_attn_combine(plan, workspace, out, lse=None, sink=None, stream=None):
+    """Merge the splits' partials into out (and lse); shapes as in _combine_args."""
     _check("verify_attn_combine", _lib().verify_attn_combine(
-        ctypes.byref(plan.plan), _ptr(workspace), workspace.numel() * 4, _ptr(sink), _ptr(out), _ptr(lse),
-        _stream(stream)))
+        ctypes.byref(plan.plan), *_combine_args(plan, workspace, out, lse, sink), _stream(stream)))
+
+
+def verify_attn_combine_state(plan, state, workspace, out, lse=None, sink=None, stream=None):
+    """verify_attn_combine for a verify_attn_split_state call with the same state."""
+    _require_state(state)
+    _check("verify_attn_combine_state", _lib().verify_attn_combine_state(
+        ctypes.byref(plan.plan), _ptr(state), *_combine_args(plan, workspace, out, lse, sink), _stream(stream)))
 
 
 def swa_ring_write(k_new, v_new, first_pos, k_ring, v_ring, stream=None):
@@ -284,8 +340,10 @@ def verify_kv_write(k_new, v_new, first_pos, k_cache, v_cache, v_scale=None, rin
         k_cache.stride(0), k_cache.stride(1), _stream(stream)))
 
 
-def verify_attn(plan, q, k, v, sink=None, v_scale=None, workspace=None, out=None, lse=None, stream=None):
-    """Split then combine on one stream; allocates what is not passed in."""
+def verify_attn(plan, q, k, v, sink=None, v_scale=None, workspace=None, out=None, lse=None, stream=None,
+                state=None):
+    """Split then combine on one stream; allocates what is not passed in.
+    With `state` (device int64 [11]) the state entry points run instead."""
     import torch
     dev = q.device
     if workspace is None:
@@ -294,6 +352,10 @@ def verify_attn(plan, q, k, v, sink=None, v_scale=None, workspace=None, out=None
         out = torch.empty((plan.rows, plan.q_heads, plan.head_dim), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((plan.rows, plan.q_heads), dtype=torch.float32, device=dev)
-    verify_attn_split(plan, q, k, v, workspace, v_scale=v_scale, stream=stream)
-    verify_attn_combine(plan, workspace, out, lse=lse, sink=sink, stream=stream)
+    if state is None:
+        verify_attn_split(plan, q, k, v, workspace, v_scale=v_scale, stream=stream)
+        verify_attn_combine(plan, workspace, out, lse=lse, sink=sink, stream=stream)
+    else:
+        verify_attn_split_state(plan, state, q, k, v, workspace, v_scale=v_scale, stream=stream)
+        verify_attn_combine_state(plan, state, workspace, out, lse=lse, sink=sink, stream=stream)
     return out, lse

@@ -79,6 +79,10 @@ struct SplitArgs {
   // bits are set in anc[r].
   int32_t t0_rel, window;
   uint32_t anc[VA_MAX_ROWS];
+  // Per-call state in device memory (the state entry points): the fields
+  // above that depend on positions or rows are then derived from it.
+  const va_state *state;
+  int64_t bucket_hi;  // the plan's extent end: no state may read beyond it
 };
 
 struct CombineArgs {
@@ -88,7 +92,87 @@ struct CombineArgs {
   float *out;
   float *lse;
   int32_t rows, live_rows, group, mrows, q_heads, kv_heads, splits, head_dim;
+  const va_state *state;  // as in SplitArgs
+  int32_t tree, window, ring_slots;
+  int64_t bucket_hi;
 };
+
+// Per-call geometry derived from a va_state on the device, with the same
+// rules as the host plan (row intervals, read extent, 32-key split table,
+// ancestor bits) and the split kernel's relative coordinates.
+struct StateGeo {
+  int64_t base;
+  int32_t rel_lo, rel_hi, full_lo, full_hi, cq, cr, splits, live_rows, ring_base, t0_rel, tree_lo;
+  uint32_t anc[VA_MAX_ROWS];
+  bool valid;
+};
+
+__device__ __forceinline__ StateGeo geo_from_state(const va_state *stp, int32_t rows, int32_t tree, int32_t window,
+                                                   int32_t ring_slots, int32_t splits_plan, int64_t bucket_hi) {
+  const va_state st = *stp;
+  StateGeo g;
+  const int32_t live = st.live_rows;
+  const int64_t fp = st.first_pos, P = st.prefix_len;
+  const int64_t kMaxPos = (int64_t)1 << 61;
+  bool valid = st.reserved == 0 && live >= 0 && live <= rows;
+  int64_t lo = 0, hi = 0, flo = 0, fhi = 0;
+  uint32_t anc[VA_MAX_ROWS];
+#pragma unroll
+  for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = 0u;
+  if (tree) {
+    valid = valid && P >= 0 && P <= kMaxPos;
+#pragma unroll
+    for (int i = 0; i < VA_MAX_ROWS; ++i) {
+      const int32_t pa = st.parent[i];
+      if (i < rows) valid = valid && pa >= -1 && pa < i;
+      // parents precede their children, so anc[pa] is final here
+      uint32_t bits = 1u << i;
+#pragma unroll
+      for (int j = 0; j < i; ++j) bits |= (pa == j) ? anc[j] : 0u;
+      anc[i] = bits;
+    }
+#pragma unroll
+    for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = i < live ? anc[i] : 0u;
+    lo = 0;
+    hi = P + live;
+    flo = 0;
+    fhi = P;
+  } else {
+    valid = valid && fp >= 0 && fp <= kMaxPos;
+    lo = window ? fp - window + 1 : 0;
+    if (lo < 0) lo = 0;
+    hi = fp + live;
+    flo = window ? fp + live - 1 - window + 1 : 0;
+    if (flo < 0) flo = 0;
+    fhi = fp + 1;
+  }
+  if (live == 0) lo = hi = flo = fhi = 0;
+  valid = valid && hi <= bucket_hi;
+  const int64_t chunk_lo = lo >> 5;
+  const int64_t chunks = live > 0 ? ((hi + 31) >> 5) - chunk_lo : 0;
+  const int32_t S = (int32_t)(chunks < splits_plan ? (chunks > 0 ? chunks : 1) : splits_plan);
+  g.base = chunk_lo << 5;
+  g.splits = S;
+  g.cq = (int32_t)(chunks / S);
+  g.cr = (int32_t)(chunks % S);
+  g.rel_lo = (int32_t)(lo - g.base);
+  g.rel_hi = (int32_t)(hi - g.base);
+  int32_t rflo = (int32_t)(flo - g.base), rfhi = (int32_t)(fhi - g.base);
+  if (flo - g.base < g.rel_lo) rflo = g.rel_lo;
+  if (fhi - g.base > g.rel_hi) rfhi = g.rel_hi;
+  if (rfhi < rflo) rfhi = rflo;
+  g.full_lo = rflo;
+  g.full_hi = rfhi;
+  g.ring_base = ring_slots ? (int32_t)(g.base % ring_slots) : 0;
+  g.t0_rel = tree ? 0 : (int32_t)(fp - g.base);
+  // tree: base is 0 and P < hi <= the bucket's hi < 2^31; unused otherwise
+  g.tree_lo = tree ? (int32_t)P : 0;
+  g.live_rows = live;
+#pragma unroll
+  for (int i = 0; i < VA_MAX_ROWS; ++i) g.anc[i] = anc[i];
+  g.valid = valid;
+  return g;
+}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -214,7 +298,7 @@ __device__ __forceinline__ void pin(int64_t x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
 
-template <int D, int W, int FMT, int NST, int NPW>
+template <int D, int W, int FMT, int NST, int NPW, bool STATE>
 __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a) {
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
@@ -239,21 +323,36 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
 
   // ---------------- this split's chunk range ----------------
   // split s takes q + 1 chunks if s < r, else q (q = C / S, r = C % S)
-  const int32_t cq = a.chunks_q, cr = a.chunks_r, rel_lo = a.rel_lo, rel_hi = a.rel_hi;
-  const int32_t ring_slots = a.ring_slots, ring_base = a.ring_base_slot;
-  const int64_t kv_base = a.base, row_stride = a.kv_row_stride_b, head_stride = a.kv_head_stride_b;
+  int32_t cq = a.chunks_q, cr = a.chunks_r, rel_lo = a.rel_lo, rel_hi = a.rel_hi;
+  const int32_t ring_slots = a.ring_slots;
+  int32_t ring_base = a.ring_base_slot;
+  int64_t kv_base = a.base;
+  const int64_t row_stride = a.kv_row_stride_b, head_stride = a.kv_head_stride_b;
   const uint8_t *kptr = a.k, *vptr = a.v;
   const float *vsc = a.v_scale;
   const int64_t vsc_stride = a.v_scale_head_stride;
   const float inv_group = a.inv_group, scale_log2 = a.scale_log2;
-  const int32_t mrows = a.mrows, live_rows = a.live_rows, group = a.group, q_heads = a.q_heads;
-  const int32_t tree = a.tree, tree_lo = a.tree_lo, t0_rel = a.t0_rel, window = a.window;
-  const int32_t full_lo = a.full_lo, full_hi = a.full_hi, kv_heads = a.kv_heads;
+  const int32_t mrows = a.mrows, group = a.group, q_heads = a.q_heads;
+  int32_t live_rows = a.live_rows;
+  const int32_t tree = a.tree, window = a.window;
+  int32_t tree_lo = a.tree_lo, t0_rel = a.t0_rel;
+  int32_t full_lo = a.full_lo, full_hi = a.full_hi;
+  const int32_t kv_heads = a.kv_heads;
   const uint8_t *qptr = a.q;
   float *ws_ml = a.ws_ml, *ws_o = a.ws_o;
   uint32_t anc[VA_MAX_ROWS];
 #pragma unroll
   for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = a.anc[i];
+  if constexpr (STATE) {
+    const StateGeo g = geo_from_state(a.state, a.rows, tree, window, ring_slots, a.splits, a.bucket_hi);
+    // workgroups above the state's split count, or any for a state outside
+    // the bucket, read nothing (uniform over the workgroup, before any barrier)
+    if (!g.valid || split >= g.splits) return;
+    cq = g.cq, cr = g.cr, rel_lo = g.rel_lo, rel_hi = g.rel_hi, ring_base = g.ring_base, kv_base = g.base;
+    live_rows = g.live_rows, tree_lo = g.tree_lo, t0_rel = g.t0_rel, full_lo = g.full_lo, full_hi = g.full_hi;
+#pragma unroll
+    for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = g.anc[i];
+  }
   pin(cq), pin(cr), pin(rel_lo), pin(rel_hi), pin(ring_slots), pin(ring_base), pin(kv_base);
   pin(row_stride), pin(head_stride), pin(kptr), pin(vptr);
   if constexpr (FMT == 1) pin(vsc), pin(vsc_stride);
@@ -665,7 +764,7 @@ __device__ __forceinline__ float xor_sum3(float x) {
   return wave_sum16x4(x);
 }
 
-template <int BATCH, int WAVES>
+template <int BATCH, int WAVES, bool STATE>
 __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a) {
   constexpr int kCombNSG = 8 * WAVES;  // split groups
   __shared__ f32x4 wacc[WAVES][kCombDQ];
@@ -674,10 +773,25 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
   // every kernel argument loaded in one round trip (see pin())
   const float *ws_ml = a.ws_ml, *ws_o = a.ws_o, *sinkp = a.sink;
   float *outb = a.out, *lsep = a.lse;
-  const int32_t live_rows = a.live_rows, group = a.group, mrows = a.mrows, q_heads = a.q_heads;
-  const int32_t kv_heads = a.kv_heads, S = a.splits, D = a.head_dim;
+  int32_t live_rows = a.live_rows, S = a.splits;
+  const int32_t group = a.group, mrows = a.mrows, q_heads = a.q_heads;
+  const int32_t kv_heads = a.kv_heads, D = a.head_dim;
   pin(ws_ml), pin(ws_o), pin(sinkp), pin(outb), pin(lsep), pin(live_rows), pin(group), pin(mrows);
   pin(q_heads), pin(kv_heads), pin(S), pin(D);
+  if constexpr (STATE) {
+    const StateGeo g = geo_from_state(a.state, a.rows, a.tree, a.window, a.ring_slots, a.splits, a.bucket_hi);
+    if (!g.valid) {  // a state outside the bucket: every output is NaN
+      const int t = threadIdx.x;
+      if (t < kCombDQ) {
+        const int rh = blockIdx.x;
+        *(f32x4 *)(outb + (int64_t)rh * D + kCombD * blockIdx.y + 4 * t) = (f32x4){NAN, NAN, NAN, NAN};
+        if (lsep && blockIdx.y == 0 && t == 0) lsep[rh] = NAN;
+      }
+      return;
+    }
+    live_rows = g.live_rows;
+    S = g.splits;
+  }
 
   const int rh = blockIdx.x;
   const int r = rh / q_heads, h = rh % q_heads;
@@ -797,27 +911,30 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
 #endif
 constexpr int kComb1WaveBatch = VA_COMB_1WAVE_BATCH;
 
-template <int WAVES>
+template <int WAVES, bool STATE>
 hipError_t launch_combine_w(const CombineArgs &a, dim3 grid, int per, hipStream_t stream) {
   const dim3 block(64 * WAVES);
   if (per <= 1) {
-    hipLaunchKernelGGL((combine_kernel<1, WAVES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<1, WAVES, STATE>), grid, block, 0, stream, a);
   } else if (per <= 2) {
-    hipLaunchKernelGGL((combine_kernel<2, WAVES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<2, WAVES, STATE>), grid, block, 0, stream, a);
   } else if (per <= 4) {
-    hipLaunchKernelGGL((combine_kernel<4, WAVES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<4, WAVES, STATE>), grid, block, 0, stream, a);
   } else if (per <= 8) {
-    hipLaunchKernelGGL((combine_kernel<8, WAVES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<8, WAVES, STATE>), grid, block, 0, stream, a);
   } else {
-    hipLaunchKernelGGL((combine_kernel<kCombMaxBatch, WAVES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<kCombMaxBatch, WAVES, STATE>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
+// S is the plan's split count: with a per-call state the kernel runs with at
+// most that many, so the configuration covers every state of the bucket.
+template <bool STATE>
 hipError_t launch_combine(const CombineArgs &a, dim3 grid, int S, hipStream_t stream) {
   const int per1 = (S + 7) / 8;  // splits per thread with one wave (8 split groups)
-  if (per1 <= kComb1WaveBatch) return launch_combine_w<1>(a, grid, per1, stream);
-  return launch_combine_w<4>(a, grid, (S + 31) / 32, stream);
+  if (per1 <= kComb1WaveBatch) return launch_combine_w<1, STATE>(a, grid, per1, stream);
+  return launch_combine_w<4, STATE>(a, grid, (S + 31) / 32, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -939,35 +1056,38 @@ constexpr int producers_for() { return FMT == 1 ? 1 : 2; }
 template <int D, int FMT>
 constexpr int stages_for() { return FMT == 1 ? 8 : (D == 64 ? 8 : 4); }
 
-template <int D, int W, int FMT>
+template <int D, int W, int FMT, bool STATE>
 hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
   dim3 grid(a.splits, a.kv_heads);
-  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW>), grid, dim3(64 * (W + NPW)), 0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE>), grid, dim3(64 * (W + NPW)), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int FMT>
+template <int D, int FMT, bool STATE>
 hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
   switch (nb_total) {
-    case 1: return launch_split<D, 1, FMT>(a, stream);
-    case 2: return launch_split<D, 2, FMT>(a, stream);
-    case 3: return launch_split<D, 3, FMT>(a, stream);
-    case 4: return launch_split<D, 4, FMT>(a, stream);
-    case 5: return launch_split<D, 5, FMT>(a, stream);
-    case 6: return launch_split<D, 6, FMT>(a, stream);
+    case 1: return launch_split<D, 1, FMT, STATE>(a, stream);
+    case 2: return launch_split<D, 2, FMT, STATE>(a, stream);
+    case 3: return launch_split<D, 3, FMT, STATE>(a, stream);
+    case 4: return launch_split<D, 4, FMT, STATE>(a, stream);
+    case 5: return launch_split<D, 5, FMT, STATE>(a, stream);
+    case 6: return launch_split<D, 6, FMT, STATE>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
-}  // namespace va_detail
-using namespace va_detail;
+template <bool STATE>
+hipError_t dispatch_split(const SplitArgs &a, int nb_total, bool quant, int head_dim, hipStream_t stream) {
+  if (quant) return dispatch_rows<128, 1, STATE>(a, nb_total, stream);
+  if (head_dim == 64) return dispatch_rows<64, 0, STATE>(a, nb_total, stream);
+  return dispatch_rows<128, 0, STATE>(a, nb_total, stream);
+}
 
-extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const void *k, const void *v,
-                                       const float *v_scale, int64_t v_scale_head_stride,
-                                       int64_t kv_head_stride, int64_t kv_row_stride, void *workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
+va_status split_impl(const va_plan *plan, const va_state *state, const void *q, const void *k, const void *v,
+                     const float *v_scale, int64_t v_scale_head_stride, int64_t kv_head_stride,
+                     int64_t kv_row_stride, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   const va_plan_data *d = plan_of(plan);
   if (!d) return VA_ERR_INVALID;
   if (!workspace || workspace_bytes < d->workspace_bytes) return VA_ERR_WORKSPACE;
@@ -975,7 +1095,9 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   if (d->splits > kMaxSplits) return VA_ERR_UNSUPPORTED;
   const bool quant = d->kv_fmt == VA_KV_K_E4M3_WHT_V_I8;
   const int64_t esz = quant ? 1 : 2;
-  if (d->hi > d->lo) {
+  // a per-call state may read anywhere in the bucket, so its pointers are
+  // checked even when the plan's own extent is empty
+  if (state || d->hi > d->lo) {
     if (!q || !k || !v) return VA_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return VA_ERR_INVALID;
     if (kv_head_stride < 0 || kv_row_stride < d->head_dim) return VA_ERR_INVALID;
@@ -1016,29 +1138,23 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
   a.ring_slots = d->ring_slots;
   a.ring_base_slot = d->ring_base_slot;
   a.tree = d->mask == VA_MASK_TREE;
-  {
-    // tree keys relative to base; clamp far-away values into int32
-    int64_t tl = d->prefix_len - a.base;
-    a.tree_lo = (int32_t)(tl > (int64_t)1 << 30 ? (int64_t)1 << 30 : tl);
-  }
+  // tree mode: base is 0 (the extent starts at key 0) and the plan keeps
+  // prefix_len + live_rows below 2^31; chain modes never read it
+  a.tree_lo = a.tree ? (int32_t)d->prefix_len : 0;
   a.scale_log2 = d->scale * LOG2E_F;
   a.t0_rel = (d->mask == VA_MASK_TREE) ? 0 : (int32_t)(d->first_pos - a.base);
   a.window = (d->mask == VA_MASK_WINDOW) ? d->window : 0;
   for (int r = 0; r < VA_MAX_ROWS; ++r) a.anc[r] = d->anc[r];
+  a.state = state;
+  a.bucket_hi = d->hi;
   const int nb_total = (d->matrix_rows + 15) / 16;
-  hipError_t e;
-  if (quant) {
-    e = dispatch_rows<128, 1>(a, nb_total, stream);
-  } else if (d->head_dim == 64) {
-    e = dispatch_rows<64, 0>(a, nb_total, stream);
-  } else {
-    e = dispatch_rows<128, 0>(a, nb_total, stream);
-  }
+  const hipError_t e = state ? dispatch_split<true>(a, nb_total, quant, d->head_dim, stream)
+                             : dispatch_split<false>(a, nb_total, quant, d->head_dim, stream);
   return e == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
-extern "C" va_status verify_attn_combine(const va_plan *plan, const void *workspace, size_t workspace_bytes,
-                                         const float *sink, float *out, float *lse, hipStream_t stream) {
+va_status combine_impl(const va_plan *plan, const va_state *state, const void *workspace, size_t workspace_bytes,
+                       const float *sink, float *out, float *lse, hipStream_t stream) {
   const va_plan_data *d = plan_of(plan);
   if (!d || !out) return VA_ERR_INVALID;
   if (!workspace || workspace_bytes < d->workspace_bytes) return VA_ERR_WORKSPACE;
@@ -1057,8 +1173,50 @@ extern "C" va_status verify_attn_combine(const va_plan *plan, const void *worksp
   a.kv_heads = d->kv_heads;
   a.splits = d->splits;
   a.head_dim = d->head_dim;
+  a.state = state;
+  a.tree = d->mask == VA_MASK_TREE;
+  a.window = (d->mask == VA_MASK_WINDOW) ? d->window : 0;
+  a.ring_slots = d->ring_slots;
+  a.bucket_hi = d->hi;
   dim3 grid(d->rows * d->q_heads, d->head_dim / kCombD);
-  return launch_combine(a, grid, d->splits, stream) == hipSuccess ? VA_OK : VA_ERR_HIP;
+  const hipError_t e = state ? launch_combine<true>(a, grid, d->splits, stream)
+                             : launch_combine<false>(a, grid, d->splits, stream);
+  return e == hipSuccess ? VA_OK : VA_ERR_HIP;
+}
+
+inline bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
+
+}  // namespace va_detail
+using namespace va_detail;
+
+extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const void *k, const void *v,
+                                       const float *v_scale, int64_t v_scale_head_stride,
+                                       int64_t kv_head_stride, int64_t kv_row_stride, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  return split_impl(plan, nullptr, q, k, v, v_scale, v_scale_head_stride, kv_head_stride, kv_row_stride,
+                    workspace, workspace_bytes, stream);
+}
+
+extern "C" va_status verify_attn_combine(const va_plan *plan, const void *workspace, size_t workspace_bytes,
+                                         const float *sink, float *out, float *lse, hipStream_t stream) {
+  return combine_impl(plan, nullptr, workspace, workspace_bytes, sink, out, lse, stream);
+}
+
+extern "C" va_status verify_attn_split_state(const va_plan *plan, const va_state *state, const void *q,
+                                             const void *k, const void *v, const float *v_scale,
+                                             int64_t v_scale_head_stride, int64_t kv_head_stride,
+                                             int64_t kv_row_stride, void *workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  if (!state || !aligned8(state)) return VA_ERR_INVALID;
+  return split_impl(plan, state, q, k, v, v_scale, v_scale_head_stride, kv_head_stride, kv_row_stride,
+                    workspace, workspace_bytes, stream);
+}
+
+extern "C" va_status verify_attn_combine_state(const va_plan *plan, const va_state *state, const void *workspace,
+                                               size_t workspace_bytes, const float *sink, float *out, float *lse,
+                                               hipStream_t stream) {
+  if (!state || !aligned8(state)) return VA_ERR_INVALID;
+  return combine_impl(plan, state, workspace, workspace_bytes, sink, out, lse, stream);
 }
 
 extern "C" va_status swa_ring_write(const void *k_new, const void *v_new, int32_t rows, int64_t first_pos,

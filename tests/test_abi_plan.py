@@ -27,6 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = va.load_library()
     names = declared_functions()
     assert set(names) >= {"verify_attn_plan", "verify_attn_split", "verify_attn_combine", "swa_ring_write", "verify_kv_write",
+                          "verify_attn_split_state", "verify_attn_combine_state",
                           "verify_attn_plan_query", "verify_attn_plan_split_range", "va_status_string"}
     for n in names:
         assert hasattr(lib, n), n
