@@ -86,8 +86,11 @@ def summarize_profiles(d):
     cw = [v for n, g, v in counters("pmc_copy_write", "copy_counter_collection.csv") if "copyBuffer" in n]
     f_scale = copy_bytes / (sum(cf) / len(cf) * 1024)
     w_scale = copy_bytes / (sum(cw) / len(cw) * 1024)
-    fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if "split_kernel" in n]
-    wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if "split_kernel" in n]
+    def static_split(n):  # the static-plan split kernel (the device-state instances are timed apart)
+        return "split_kernel" in n and "true>" not in n.replace(" ", "")
+
+    fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if static_split(n)]
+    wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if static_split(n)]
     if len(fe) != len(wr):
         raise SystemExit("fetch and write runs saw different split launches")
     per_launch = [f * f_scale * 1024 + w * w_scale * 1024 for (_, f), (_, w) in zip(fe, wr)]
@@ -125,9 +128,11 @@ def summarize_profiles(d):
         tot[kind] += v
         out.append(f"| {kind} | {wgs} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     for kind in ("split_kernel", "combine_kernel"):
-        v = [x for k, x in tot.items() if k.startswith(kind) for x in x]
-        if v:
-            out.append(f"| {kind} (all) | all | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        for flag, label in (("false>", "static plan"), ("true>", "device state")):
+            v = [x for k, x in tot.items() if k.startswith(kind) and k.endswith(flag) for x in x]
+            if v:
+                out.append(f"| {kind} ({label}, all) | all | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} "
+                           f"| {max(v):.2f} |")
     out.append("")
     out.append("bench line of the same command (events; the trace itself slows the launches): "
                f"roofline avg_launch_us {bl['roofline']['avg_launch_us']}, value {bl['value']} GB/s")
@@ -421,6 +426,52 @@ def main():
     achieved = split_bytes / (split_ms * 1e-3) / 1e9
     launches = len(cases) * args.kernel_reps
 
+    # ---------------- pass C: the device-state entry points ----------------
+    # One plan for a bucket covering the whole sweep (8 rows at the largest
+    # context) fixes the grid; each context's positions and live rows come
+    # from a state record in device memory.  Timed like pass B; the outputs
+    # must match the static call's (same partials; the combine may order its
+    # FP32 sum differently).
+    bucket = va.Plan(rows=ROWS, live_rows=ROWS, q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
+                     first_pos=max(contexts), kv_capacity=CAP, scale=1 / math.sqrt(D))
+    bws = va.workspace_for(bucket, dev)
+    bout = torch.empty((ROWS, HQ, D), dtype=torch.float32, device=dev)
+    blse = torch.empty((ROWS, HQ), dtype=torch.float32, device=dev)
+    for c, entry in zip(cases, sweep):
+        st = va.pack_state(first_pos=c["ctx"], live_rows=c["live"]).to(dev)
+
+        def ssplits(c=c, st=st):
+            for i in range(args.kernel_reps):
+                k, v = c["kvs"][i % args.replicas]
+                va.verify_attn_split_state(bucket, st, c["q"], k, v, bws, stream=torch.cuda.current_stream())
+
+        def scombines(c=c, st=st):
+            for i in range(args.kernel_reps):
+                va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"],
+                                             stream=torch.cuda.current_stream())
+        gs, gc = capture(ssplits), capture(scombines)
+        gs.replay()
+        gc.replay()
+        a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        gs.replay()
+        b.record(stream)
+        gc.replay()
+        d.record(stream)
+        torch.cuda.synchronize()
+        del gs, gc
+        call(c, 0)
+        k, v = c["kvs"][0]
+        va.verify_attn_split_state(bucket, st, c["q"], k, v, bws, stream=stream)
+        va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"], stream=stream)
+        torch.cuda.synchronize()
+        L = c["live"]
+        if not (torch.allclose(bout[:L], c["out"][:L], rtol=1e-5, atol=1e-6) and
+                torch.allclose(blse[:L], c["lse"][:L], rtol=1e-6, atol=1e-5)):
+            raise SystemExit(f"state path differs from the static call at ctx {c['ctx']}")
+        entry["state_split_us"] = round(a.elapsed_time(b) / args.kernel_reps * 1e3, 2)
+        entry["state_combine_us"] = round(b.elapsed_time(d) / args.kernel_reps * 1e3, 2)
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -490,7 +541,8 @@ def main():
         "config": {"workload": "full-attention verify sweep: Hkv 1, Hq 6, D 128, 8 rows (4-8 live), "
                                "causal, sink on, capacity 262144, ctx 1K-192K, cold KV",
                    "contexts": contexts, "replicas": args.replicas, "splits": "plan" if not args.splits else args.splits,
-                   "launch": "HIP graph replay"},
+                   "launch": "HIP graph replay",
+                   "state_bucket": f"{ROWS} rows at {max(contexts)}, {bucket.splits} splits"},
         "eager_launch_ms_per_step": round(eager_ms_per_step, 4),
         "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "sweep": sweep,
         "wall_s_timed": round(t_wall, 4), "kernel_hash": kernel_hash(),
