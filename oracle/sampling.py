@@ -116,7 +116,9 @@ def sample_row(z, k, top_p, temperature, u):
     probs = np.zeros(ids.size)
     probs[:m] = p[:m] / p[:m].sum()
     j, dm = draw(e[:m], u)
-    tm = float(np.min(np.abs(excl[1:] - top_p))) if ids.size > 1 else np.inf
+    # the cut compares excl with top_p only where p_i > 0 (p_i = 0 is never kept)
+    pos = np.nonzero(p[1:] > 0)[0] + 1
+    tm = float(np.min(np.abs(excl[pos] - top_p))) if pos.size else np.inf
     return dict(ids=ids, probs=probs, kept=m, token=int(ids[j]), topp_margin=tm, draw_margin=dm)
 
 

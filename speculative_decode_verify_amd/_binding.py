@@ -46,6 +46,15 @@ class va_state(ctypes.Structure):
     ]
 
 
+class va_sample_params(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("top_k", ctypes.c_int32), ("vocab", ctypes.c_int64),
+        ("row_stride", ctypes.c_int64), ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+        ("seed", ctypes.c_uint64), ("first_position", ctypes.c_int64), ("purpose", ctypes.c_uint32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class va_plan(ctypes.Structure):
     _fields_ = [("words", ctypes.c_uint64 * 256)]
 
@@ -86,11 +95,18 @@ def load_library():
     lib.verify_attn_combine_state.argtypes = [ctypes.POINTER(va_plan), V, V, SZ, V, V, V, V]
     lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
     lib.verify_kv_write.argtypes = [V, V, I32, I64, I32, I32, I32, V, V, V, I64, I64, I32, I64, I64, V]
+    SP = ctypes.POINTER(va_sample_params)
+    lib.va_sample_workspace_bytes.argtypes = [SP]
+    lib.va_sample_workspace_bytes.restype = SZ
+    lib.va_sample.argtypes = [SP, V, V, V, V, V, V, SZ, V]
+    lib.va_accept.argtypes = [V, V, V, V, I32, V, V, V, I32, V, I32, ctypes.c_uint64, I64, V, V, V]
+    lib.va_sample_accept.argtypes = [SP, V, V, V, V, I32, V, V, V, V, V, V, V, V, SZ, V]
     lib.va_status_string.argtypes = [ctypes.c_int]
     lib.va_status_string.restype = ctypes.c_char_p
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
                "verify_attn_split", "verify_attn_combine", "verify_attn_split_state",
-               "verify_attn_combine_state", "swa_ring_write", "verify_kv_write"):
+               "verify_attn_combine_state", "swa_ring_write", "verify_kv_write", "va_sample", "va_accept",
+               "va_sample_accept"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -359,3 +375,100 @@ def verify_attn(plan, q, k, v, sink=None, v_scale=None, workspace=None, out=None
         verify_attn_split_state(plan, state, q, k, v, workspace, v_scale=v_scale, stream=stream)
         verify_attn_combine_state(plan, state, workspace, out, lse=lse, sink=sink, stream=stream)
     return out, lse
+
+
+# ----------------------------------------------------------------------------- sampling and acceptance
+
+PURPOSE_TARGET, PURPOSE_ACCEPT, PURPOSE_RESIDUAL = 0, 1, 2
+
+
+def sample_params(rows, vocab, top_k=20, top_p=0.95, temperature=1.0, seed=0, first_position=0, purpose=0,
+                  row_stride=None):
+    p = va_sample_params()
+    p.rows, p.top_k, p.vocab = rows, top_k, vocab
+    p.row_stride = vocab if row_stride is None else row_stride
+    p.temperature, p.top_p, p.seed = temperature, top_p, seed
+    p.first_position, p.purpose, p.reserved = first_position, purpose, 0
+    return p
+
+
+def sample_workspace_bytes(params):
+    return _lib().va_sample_workspace_bytes(ctypes.byref(params))
+
+
+def _sample_call_args(logits, top_k, top_p, temperature, seed, first_position, purpose, workspace, out):
+    import torch
+    _require(logits, "logits", (torch.float32,))
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, vocab] with contiguous rows")
+    rows, vocab = logits.shape
+    p = sample_params(rows, vocab, top_k, top_p, temperature, seed, first_position, purpose, logits.stride(0))
+    need = sample_workspace_bytes(p)
+    if need == 0:
+        raise VAError("va_sample_workspace_bytes", 1)
+    dev = logits.device
+    if workspace is None:
+        workspace = torch.empty((need + 7) // 8, dtype=torch.int64, device=dev)
+    if out is None:
+        out = dict(ids=torch.empty((rows, top_k), dtype=torch.int32, device=dev),
+                   probs=torch.empty((rows, top_k), dtype=torch.float32, device=dev),
+                   kept=torch.empty(rows, dtype=torch.int32, device=dev),
+                   tokens=torch.empty(rows, dtype=torch.int32, device=dev))
+    return p, workspace, out
+
+
+def va_sample(logits, top_k=20, top_p=0.95, temperature=1.0, seed=0, first_position=0, purpose=PURPOSE_TARGET,
+              workspace=None, out=None, stream=None):
+    """Top-k / top-p sampling of every row of FP32 logits [rows, vocab].
+    Returns dict(ids [rows, top_k], probs [rows, top_k], kept [rows], tokens [rows])."""
+    p, ws, out = _sample_call_args(logits, top_k, top_p, temperature, seed, first_position, purpose, workspace, out)
+    _check("va_sample", _lib().va_sample(
+        ctypes.byref(p), _ptr(logits), _ptr(out["ids"]), _ptr(out["probs"]), _ptr(out["kept"]), _ptr(out["tokens"]),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def _q_args(q_ids, q_probs, q_kept, drafts):
+    if q_ids is None:
+        return None, None, None, 1, None
+    if q_ids.dim() != 2 or not q_ids.is_contiguous() or q_probs.shape != q_ids.shape or not q_probs.is_contiguous():
+        raise ValueError("q_ids / q_probs must be contiguous [n - 1, q_stride]")
+    return _ptr(q_ids), _ptr(q_probs), _ptr(q_kept), q_ids.shape[1], _ptr(drafts)
+
+
+def va_accept(p_ids, p_probs, p_kept, p_tokens, q_ids, q_probs, q_kept, drafts, seed, first_position,
+              accepted=None, out_tokens=None, stream=None):
+    """Rejection acceptance of n - 1 drafts against n target rows (int32 / FP32
+    device tensors as va_sample writes them).  Returns (accepted [1], out_tokens [n])."""
+    import torch
+    n = p_ids.shape[0]
+    dev = p_ids.device
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(n, dtype=torch.int32, device=dev)
+    qi, qp, qk, qs, dr = _q_args(q_ids, q_probs, q_kept, drafts)
+    _check("va_accept", _lib().va_accept(
+        _ptr(p_ids), _ptr(p_probs), _ptr(p_kept), _ptr(p_tokens), p_ids.shape[1], qi, qp, qk, qs, dr, n,
+        seed, first_position, _ptr(accepted), _ptr(out_tokens), _stream(stream)))
+    return accepted, out_tokens
+
+
+def va_sample_accept(logits, q_ids, q_probs, q_kept, drafts, top_k=20, top_p=0.95, temperature=1.0, seed=0,
+                     first_position=0, purpose=PURPOSE_TARGET, workspace=None, out=None, accepted=None,
+                     out_tokens=None, stream=None):
+    """va_sample of the n verification rows, then the acceptance, in two launches.
+    Returns (dict as va_sample, accepted [1], out_tokens [n])."""
+    import torch
+    p, ws, out = _sample_call_args(logits, top_k, top_p, temperature, seed, first_position, purpose, workspace, out)
+    dev = logits.device
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(p.rows, dtype=torch.int32, device=dev)
+    qi, qp, qk, qs, dr = _q_args(q_ids, q_probs, q_kept, drafts)
+    _check("va_sample_accept", _lib().va_sample_accept(
+        ctypes.byref(p), _ptr(logits), qi, qp, qk, qs, dr, _ptr(out["ids"]), _ptr(out["probs"]), _ptr(out["kept"]),
+        _ptr(out["tokens"]), _ptr(accepted), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+    return out, accepted, out_tokens

@@ -53,3 +53,40 @@ def normal_bf16_device(shape, seed, device):
     (for benchmark-sized caches that would be slow to draw on the CPU)."""
     g = torch.Generator(device=device).manual_seed(int(seed))
     return torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+
+
+LOGIT_KINDS = ("lm", "flat", "bf16", "masked", "few", "equal", "spike")
+
+
+def logits_f32(rows, vocab, g, kind="lm"):
+    """FP32 logits [rows, vocab] of a few shapes a language-model head gives:
+      lm      N(0, 2^2) plus 32 tokens per row raised by U(4, 12) (a peaked head);
+      flat    N(0, 0.5^2) (a wide top-p set);
+      bf16    lm rounded to bf16 (many equal logits);
+      masked  -inf except 100 tokens drawn N(0, 1) (a constrained vocabulary);
+      few     -inf except 5 tokens (fewer finite logits than a top-k of 20);
+      equal   all zero (every logit tied);
+      spike   N(0, 1) with one token at +60 (one token holds the mass)."""
+    if kind == "equal":
+        return torch.zeros((rows, vocab), dtype=torch.float32)
+    if kind in ("lm", "bf16"):
+        z = torch.randn((rows, vocab), generator=g) * 2.0
+        n = min(32, vocab)
+        for r in range(rows):
+            idx = torch.randperm(vocab, generator=g)[:n]
+            z[r, idx] += 4.0 + 8.0 * torch.rand(n, generator=g)
+        return z.to(torch.bfloat16).float() if kind == "bf16" else z
+    if kind == "flat":
+        return torch.randn((rows, vocab), generator=g) * 0.5
+    if kind in ("masked", "few"):
+        n = min(100 if kind == "masked" else 5, vocab)
+        z = torch.full((rows, vocab), float("-inf"))
+        for r in range(rows):
+            idx = torch.randperm(vocab, generator=g)[:n]
+            z[r, idx] = torch.randn(n, generator=g)
+        return z
+    if kind == "spike":
+        z = torch.randn((rows, vocab), generator=g)
+        z[torch.arange(rows), torch.randint(0, vocab, (rows,), generator=g)] = 60.0
+        return z
+    raise ValueError(kind)

@@ -14,11 +14,12 @@ from oracle import masks
 from oracle.masks import Problem
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "verify_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)) - {"sizeof"})
 
@@ -28,6 +29,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"verify_attn_plan", "verify_attn_split", "verify_attn_combine", "swa_ring_write", "verify_kv_write",
                           "verify_attn_split_state", "verify_attn_combine_state",
+                          "va_sample", "va_accept", "va_sample_accept", "va_sample_workspace_bytes",
                           "verify_attn_plan_query", "verify_attn_plan_split_range", "va_status_string"}
     for n in names:
         assert hasattr(lib, n), n
