@@ -45,6 +45,7 @@ METRIC = "verify-attn µs/call and KV-read GB/s (% HBM peak), 8 rows×6 heads, 1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep_traffic.json")
 COPY_PROBE_MIB = 1024
 KERNEL_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "verify_attn.hip")
+SAMPLE_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "sample.hip")
 
 
 def kv_bytes(hi):
@@ -54,6 +55,11 @@ def kv_bytes(hi):
 
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def sample_hash():
+    with open(SAMPLE_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -162,6 +168,53 @@ def summarize_profiles(d):
     open(name, "w").write("\n".join(out) + "\n")
     print(f"wrote {name} and {TRAFFIC_FILE}")
 
+    st = os.path.join(d, "trace_sampler", "sampler_kernel_trace.csv")
+    if os.path.exists(st):
+        rows = [r for r in csv.DictReader(open(st)) if "sample_kernel" in r["Kernel_Name"] or
+                "accept_kernel" in r["Kernel_Name"]]
+        by = collections.defaultdict(list)
+        for r in rows:
+            n = r["Kernel_Name"]
+            name = n[n.index("sample_detail::") + len("sample_detail::"):n.index("(")].replace(" ", "")
+            wgs = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_X"])
+            by[(name, wgs)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+
+        def sampler_line(log):
+            for line in open(os.path.join(d, log)):
+                if line.startswith("{") and "va_sample_accept" in line:
+                    return json.loads(line)
+            raise SystemExit(f"no sampler line in {log}")
+        sl = sampler_line("sampler_trace.log")
+        if sl["kernel_hash"] != sample_hash():
+            raise SystemExit("sampler profile of another kernel source")
+        o = ["# sample_kernel, sampling of 8 verification rows and acceptance of 7 drafts "
+             "(top-k 20, top-p 0.95, FP32 logits)", "",
+             f"kernel source sha256[:16]: {sample_hash()}", "",
+             f"command: rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace_sampler -o sampler -- {py} --sampler "
+             "--no-cpu-baseline", "",
+             "workgroups = tiles x rows: 160 for the 160,000-token vocabulary, 24 for the 20,000-token share; "
+             "<true> runs the acceptance in the last row.", "",
+             "| kernel | workgroups | launches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+        for (name, wgs), v in sorted(by.items()):
+            if len(v) < 10:
+                continue  # the single eager calls before capture
+            o.append(f"| {name} | {wgs} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        o += ["", "bench line of the same command (graph replay, events):", ""]
+        for c in sl["cases"]:
+            o.append(f"- {c['case']} (V = {c['vocab']}): sample + accept {c['us_per_call']} us, sample only "
+                     f"{c['sample_only_us']} us per call; logits {c['logit_bytes']} bytes")
+        plain = os.path.join(d, "sampler.log")
+        if os.path.exists(plain):
+            pl = sampler_line("sampler.log")
+            o += ["", f"the same without the profiler ({py} --sampler):", ""]
+            for c in pl["cases"]:
+                cb = c.get("cpu_baseline")
+                o.append(f"- {c['case']}: {c['us_per_call']} us per call (sample only {c['sample_only_us']} us)"
+                         + (f"; oracle {cb['value']} us per call on one host thread" if cb else ""))
+        sname = os.path.join(ROOT, "profiles", "sample_kernel_sampling_acceptance.md")
+        open(sname, "w").write("\n".join(o) + "\n")
+        print(f"wrote {sname}")
+
     kt = os.path.join(d, "trace_kvw", "kvw_kernel_trace.csv")
     if os.path.exists(kt):
         rows = [r for r in csv.DictReader(open(kt)) if "kv_write_kernel" in r["Kernel_Name"]]
@@ -247,6 +300,96 @@ def bench_kv_write(torch, va, synth, dev, reps=200):
                       "kernel_hash": kernel_hash()}), flush=True)
 
 
+def bench_sampler(torch, va, synth, dev, reps=100, replicas=4, cpu_seconds=5.0, cpu=True):
+    """Sampling of 8 verification rows (top-k 20, top-p 0.95, temperature 1)
+    plus acceptance of their 7 drafts, over the full 160,000-token vocabulary
+    and over a 20,000-token share, with FP32 logits resident in HBM
+    (`replicas` copies read in turn).  The draft's lists come from va_sample
+    on perturbed logits (untimed).  Timed from graphs of back-to-back calls;
+    the full-size outputs of replica 0 are checked against the oracle.
+    Prints one JSON line (not the sweep's)."""
+    import numpy as np
+    from oracle import sampling as osamp
+    n, k, top_p, seed, pos0 = 8, 20, 0.95, 20260, 123456
+    out = []
+    for name, V in (("full vocabulary", 160000), ("one GPU's share of eight", 20000)):
+        g = synth.gen(9300 + V)
+        zs = [synth.logits_f32(n, V, g, "lm") for _ in range(replicas)]
+        zd = zs[0][: n - 1] + 0.5 * torch.randn((n - 1, V), generator=g)
+        zg = [z.to(dev) for z in zs]
+        dr = va.va_sample(zd.to(dev), seed=seed, first_position=pos0, purpose=3)
+        q = (dr["ids"][: n - 1].contiguous(), dr["probs"][: n - 1].contiguous(), dr["kept"][: n - 1].contiguous(),
+             dr["tokens"][: n - 1].contiguous())
+        p = va.sample_params(n, V, top_k=k, top_p=top_p, seed=seed, first_position=pos0)
+        ws = va.sample_workspace_for(p, dev)
+        o = dict(ids=torch.empty((n, k), dtype=torch.int32, device=dev),
+                 probs=torch.empty((n, k), dtype=torch.float32, device=dev),
+                 kept=torch.empty(n, dtype=torch.int32, device=dev),
+                 tokens=torch.empty(n, dtype=torch.int32, device=dev))
+        acc = torch.empty(1, dtype=torch.int32, device=dev)
+        toks = torch.empty(n, dtype=torch.int32, device=dev)
+
+        def fused(i):
+            va.va_sample_accept(zg[i % replicas], *q, top_k=k, top_p=top_p, seed=seed, first_position=pos0,
+                                workspace=ws, out=o, accepted=acc, out_tokens=toks,
+                                stream=torch.cuda.current_stream())
+
+        def sample_only(i):
+            va.va_sample(zg[i % replicas], top_k=k, top_p=top_p, seed=seed, first_position=pos0, workspace=ws,
+                         out=o, stream=torch.cuda.current_stream())
+        # full-size check of replica 0 against the oracle (decisions away from their margins)
+        fused(0)
+        torch.cuda.synchronize()
+        res = {kk: v.cpu().numpy() for kk, v in o.items()}
+        t0 = time.perf_counter()
+        ref = osamp.sample(zs[0].double().numpy(), k, float(np.float32(top_p)), 1.0, seed, pos0, 0)
+        qn = [x.cpu().numpy() for x in q]
+        a_ref, t_ref, margin = osamp.accept(res["ids"], res["probs"], res["kept"], res["tokens"], *qn, n, seed,
+                                            pos0)
+        t_oracle = time.perf_counter() - t0
+        ok = all(np.array_equal(res["ids"][r], ref[r]["ids"]) for r in range(n))
+        ok = ok and all(int(res["tokens"][r]) == ref[r]["token"] for r in range(n)
+                        if ref[r]["topp_margin"] > 1e-5 and ref[r]["draw_margin"] > 1e-5)
+        ok = ok and (margin <= 1e-6 or (int(acc.item()) == a_ref and list(toks.cpu().numpy()[: a_ref + 1]) == t_ref))
+        times = {}
+        for label, fn in (("sample_accept", fused), ("sample", sample_only)):
+            def launches(fn=fn):
+                for i in range(reps):
+                    fn(i)
+            launches()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                launches()
+            gr.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times[label] = a.elapsed_time(b) * 1e3 / reps
+            del gr
+        nbytes = n * V * 4
+        case = {"case": name, "rows": n, "vocab": V, "top_k": k, "top_p": top_p, "drafts": n - 1,
+                "us_per_call": round(times["sample_accept"], 3), "sample_only_us": round(times["sample"], 3),
+                "logit_bytes": nbytes, "logit_gb_s": round(nbytes / (times["sample_accept"] * 1e-6) / 1e9, 1),
+                "pct_hbm_peak": round(100 * nbytes / (times["sample_accept"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                "parity": {"pass": bool(ok), "accepted": int(acc.item())}}
+        if cpu:
+            passes, t_cpu = 1, t_oracle
+            while t_cpu < cpu_seconds and passes < 50:
+                t0 = time.perf_counter()
+                osamp.sample(zs[passes % replicas].double().numpy(), k, float(np.float32(top_p)), 1.0, seed, pos0, 0)
+                osamp.accept(res["ids"], res["probs"], res["kept"], res["tokens"], *qn, n, seed, pos0)
+                t_cpu += time.perf_counter() - t0
+                passes += 1
+            case["cpu_baseline"] = {"value": round(t_cpu / passes * 1e6, 1), "unit": "us/call", "cores": 1,
+                                    "kind": "oracle", "sample": f"{passes} calls, float64 numpy"}
+        out.append(case)
+    print(json.dumps({"metric": "va_sample_accept us/call (8 rows, 7 drafts, top-k 20, top-p 0.95)", "unit": "us",
+                      "higher_is_better": False, "launch": "HIP graph replay, back to back", "cases": out,
+                      "kernel_hash": sample_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +405,8 @@ def main():
                     help="write the profiles/ summaries from one profiling session's outputs (no GPU)")
     ap.add_argument("--kv-write", action="store_true",
                     help="only time verify_kv_write (the rows' KV written into the cache before the read)")
+    ap.add_argument("--sampler", action="store_true",
+                    help="time va_sample_accept (sampling + acceptance) instead of the attention sweep")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -293,6 +438,9 @@ def main():
         return
     if args.kv_write:
         bench_kv_write(torch, va, synth, dev)
+        return
+    if args.sampler:
+        bench_sampler(torch, va, synth, dev, cpu=not args.no_cpu_baseline)
         return
     contexts = args.ctx or CONTEXTS
     stream = torch.cuda.current_stream()

@@ -85,8 +85,11 @@ typedef struct {
 } va_sample_params;
 
 /* Workspace bytes for va_sample / va_sample_accept with these parameters
- * (one sorted candidate list per (row, tile) plus a counter), or 0 if the
- * parameters are invalid. */
+ * (one sorted candidate list per (row, tile) after a 256-byte block of
+ * counters), or 0 if the parameters are invalid.  The counters must be zero
+ * before a workspace's first use (zero-fill it once); every call leaves them
+ * zero again, so a workspace is reused without clearing.  Two calls in flight
+ * at once must not share a workspace. */
 size_t va_sample_workspace_bytes(const va_sample_params *params);
 
 /* Sample every row (IQuestRT report, "Include sampling and acceptance in the
@@ -99,8 +102,11 @@ size_t va_sample_workspace_bytes(const va_sample_params *params);
  *   probs      [rows][top_k] FP32: renormalised kept probabilities, 0 past kept.
  *   kept       [rows] int32: number of kept candidates (>= 1).
  *   tokens     [rows] int32: the drawn token.
- *   workspace  >= va_sample_workspace_bytes, 16-byte aligned; scratch.
- * Two launches: the tile scan (grid tiles x rows) and the per-row merge.
+ *   workspace  >= va_sample_workspace_bytes, 16-byte aligned, counters
+ *              zero (see above).
+ * One launch, grid tiles x rows: each workgroup scans one tile; the last
+ * workgroup of a row to finish merges the row's tile lists and draws (a
+ * device-scope counter per row in the workspace hands over).
  * Errors: VA_ERR_INVALID (a parameter outside its range, a NULL or misaligned
  * pointer), VA_ERR_WORKSPACE, VA_ERR_HIP. */
 va_status va_sample(const va_sample_params *params, const float *logits, int32_t *ids, float *probs,
@@ -122,9 +128,9 @@ va_status va_accept(const int32_t *p_ids, const float *p_probs, const int32_t *p
                     int32_t *accepted, int32_t *out_tokens, hipStream_t stream);
 
 /* va_sample of the n = rows verification rows (purpose as given, normally
- * VA_PURPOSE_TARGET) followed by va_accept, in two launches: the last row to
- * finish its merge runs the acceptance (a counter in the workspace, zeroed
- * by the tile scan of the same call).  Outputs as the two calls'. */
+ * VA_PURPOSE_TARGET) followed by va_accept, in the one launch of va_sample:
+ * the last row to finish its merge runs the acceptance (a second counter in
+ * the workspace).  Outputs as the two calls'. */
 va_status va_sample_accept(const va_sample_params *params, const float *logits, const int32_t *q_ids,
                            const float *q_probs, const int32_t *q_kept, int32_t q_stride, const int32_t *drafts,
                            int32_t *ids, float *probs, int32_t *kept, int32_t *tokens, int32_t *accepted,

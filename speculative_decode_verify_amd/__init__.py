@@ -9,6 +9,6 @@ from ._binding import (  # noqa: F401
     verify_attn_split, verify_attn_combine, verify_attn_split_state, verify_attn_combine_state, pack_state,
     swa_ring_write, verify_kv_write, verify_attn, workspace_for,
     library_path, load_library, MASKS, KV_FORMATS,
-    sample_params, sample_workspace_bytes, va_sample, va_accept, va_sample_accept,
+    sample_params, sample_workspace_bytes, sample_workspace_for, va_sample, va_accept, va_sample_accept,
     PURPOSE_TARGET, PURPOSE_ACCEPT, PURPOSE_RESIDUAL,
 )

@@ -396,6 +396,13 @@ def sample_workspace_bytes(params):
     return _lib().va_sample_workspace_bytes(ctypes.byref(params))
 
 
+def sample_workspace_for(params, device=None):
+    """A zero-filled workspace (its counters must start at zero; every call
+    leaves them zero, so it can be reused)."""
+    import torch
+    return torch.zeros((sample_workspace_bytes(params) + 7) // 8, dtype=torch.int64, device=device or "cuda")
+
+
 def _sample_call_args(logits, top_k, top_p, temperature, seed, first_position, purpose, workspace, out):
     import torch
     _require(logits, "logits", (torch.float32,))
@@ -408,7 +415,7 @@ def _sample_call_args(logits, top_k, top_p, temperature, seed, first_position, p
         raise VAError("va_sample_workspace_bytes", 1)
     dev = logits.device
     if workspace is None:
-        workspace = torch.empty((need + 7) // 8, dtype=torch.int64, device=dev)
+        workspace = torch.zeros((need + 7) // 8, dtype=torch.int64, device=dev)
     if out is None:
         out = dict(ids=torch.empty((rows, top_k), dtype=torch.int32, device=dev),
                    probs=torch.empty((rows, top_k), dtype=torch.float32, device=dev),

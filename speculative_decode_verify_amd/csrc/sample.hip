@@ -63,42 +63,148 @@ __device__ __forceinline__ u64 composite(float f, uint32_t id) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
 
-__device__ __forceinline__ int bits_below(u64 mask) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 __device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
 
-// The k-th largest of the 64 lanes' values (1 <= k <= 64), or 0 when fewer
-// than k lanes hold a value >= 1.  The count of lanes reaching c falls as c
-// grows, so the largest c reached by k lanes -- the answer -- is built bit by
-// bit from the top.
-__device__ __forceinline__ u64 wave_kth_largest(u64 v, int k) {
-  u64 t = 0;
-#pragma unroll 8
-  for (int b = 63; b >= 0; --b) {
-    const u64 c = t | (1ull << b);
-    if (__popcll(__ballot(v >= c)) >= k) t = c;
-  }
-  return t;
+// Lane-to-lane moves on the DPP and permute paths (no LDS round trip).  They
+// read other lanes' registers, so every lane of the wave must execute them.
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ u64 readlane64(u64 v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((u64)hi << 32) | lo;
 }
 
-// Butterfly sum: every lane gets the same value in the same order.
+// Device-scope (agent) relaxed loads and stores: they bypass the per-XCD L2's
+// non-coherent state (the sc1 bit), so data handed from a workgroup on one XCD
+// to a workgroup on another needs no cache-wide write-back or invalidate --
+// only the writer's wait for its stores before the hand-off counter moves.
+template <typename T>
+__device__ __forceinline__ void store_agent(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_agent(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Zero entries kept after the candidates of an LDS list: every rank loop
+// below reads up to 8 steps of G past the end, and zeros rank below any entry.
+constexpr int kRankPad = 128;
+
+// The k-th largest of the wave's 64 values (1 <= k <= 64; values distinct
+// unless 0), or 0 when fewer than k lanes hold a value above 0.  buf holds the
+// 64 values in LDS (written by the caller, then a barrier); each lane counts
+// the values above its own with broadcast reads.
+__device__ __forceinline__ u64 wave_kth_largest(const u64 *buf, u64 v, int k) {
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 16) {
+    u64 w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = buf[j + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r += w[q] > v ? 1 : 0;
+  }
+  const u64 hit = __ballot(v != 0 && r == k - 1);
+  return hit ? readlane64(v, __builtin_ctzll(hit)) : 0ull;
+}
+
+// Integer sum over groups of G consecutive lanes (G = 1, 2, 4, 8 or 16,
+// uniform), every lane of a group getting the group's total.
+__device__ __forceinline__ int group_sum(int x, int G) {
+  if (G > 1) x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+  if (G > 2) x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+  if (G > 4) {                                                                // lane ^ 4
+    const int y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);   // 7 - i within 8
+    x += __builtin_amdgcn_update_dpp(0, y, 0x1B, 0xF, 0xF, false);            // then i ^ 3 within 4
+  }
+  if (G > 8) x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);  // lane ^ 8
+  return x;
+}
+
+// out[r] = c[i] for every entry i of c[0, C) whose rank r (number of larger
+// entries) is below k.  NT threads (index t) share the work: G threads per
+// entry, each counting over every G-th entry, then summing within the group.
+// c needs kRankPad zeros after its C entries.
+template <int NT, bool AGENT>
+__device__ __forceinline__ void rank_and_place(const u64 *c, int C, int k, u64 *out, int t) {
+  int G = 1;
+  while (G < 16 && C * G * 2 <= NT) G <<= 1;
+  const int lg = __builtin_ctz(G);
+  for (int base = 0; base < C * G; base += NT) {
+    const int slot = base + t, i = slot >> lg, q = slot & (G - 1);
+    const bool ok = i < C;
+    const u64 v = ok ? c[ok ? i : 0] : ~0ull;
+    int r = 0;
+    for (int j = q; j < C; j += 8 * G) {
+      u64 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = c[j + u * G];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += w[u] > v ? 1 : 0;
+    }
+    r = group_sum(r, G);
+    if (ok && q == 0 && r < k) {
+      if constexpr (AGENT) store_agent(out + r, v);
+      else out[r] = v;
+    }
+  }
+}
+
+// Inclusive prefix sum of integers over lanes (as wave_inclusive_scan).
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = lane_id() >> 4;
+  if (row >= 1) x += r0;
+  if (row >= 2) x += r1;
+  if (row >= 3) x += r2;
+  return x;
+}
+
+// Sum over the wave, the same value in every lane (lane 0's): rotations by
+// 8, 4, 2, 1 inside each row of 16, then the row partners 16 and 32 apart.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Inclusive prefix sum over lanes: shifts by 1, 2, 4, 8 inside each row of
+// 16 (lanes shifted in from outside the row add 0), then each row adds the
+// totals of the rows before it.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const int row = lane_id() >> 4;
+  if (row >= 1) x += r0;
+  if (row >= 2) x += r1;
+  if (row >= 3) x += r2;
   return x;
 }
 
-// Inclusive prefix sum over lanes (Hillis-Steele).
-__device__ __forceinline__ float wave_inclusive_scan(float x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
+// The value of lane i - 1 (0 in lane 0).
+__device__ __forceinline__ float wave_shift_up1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x138, 0xF, 0xF, true));
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
@@ -126,96 +232,174 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t pos, uin
 }
 
 // ---------------------------------------------------------------------------
-// Tile scan.
+// The sampling kernel: tile scan, then (last tile of a row) merge and draw,
+// then (last row, with ACCEPT) the acceptance.
 // ---------------------------------------------------------------------------
-struct TileArgs {
+struct SampleArgs {
   const float *logits;
-  u64 *lists;         // [rows][tiles][k]
-  uint32_t *counter;  // zeroed here when the call accepts, else NULL
+  u64 *lists;           // [rows][tiles][k] sorted tile lists
+  uint32_t *row_count;  // [rows] tiles finished; zero between calls
+  uint32_t *done;       // rows finished; zero between calls
   int64_t row_stride, vocab;
-  int32_t k, tiles;
+  int32_t k, tiles, rows;
   int32_t vec;  // rows start 16-byte aligned: 16-byte loads
+  int32_t *ids;
+  float *probs;
+  int32_t *kept, *tokens;
+  float inv_temp, top_p;
+  uint64_t seed;
+  int64_t pos0;
+  uint32_t purpose;
 };
 
-// One workgroup per (tile, row).  Thread t holds logits 1024 j + 4 t + c
-// (j < 8, c < 4): eight coalesced 16-byte loads (4-byte loads when rows do
-// not start on 16 bytes).  The tile's top-k is found
-// without sorting the tile:
+struct SampleShared {
+  u64 cand[kTile + kRankPad];  // lane maxima, then candidates
+  u64 top[kMaxK];
+  u64 wbound[kTileThreads / 64];
+  uint32_t ncand, flag;
+};
+
+// The exact top-k of x (kPerThread composites per thread, 0 = empty) over the
+// workgroup, written in order to out[0, k) (zeros past the number of
+// entries).  No sort of the whole set:
 //   1. each wave takes B_w, the k-th largest of its 64 lanes' maxima: at
-//      least k of the wave's elements reach B_w, so the tile's k-th largest
+//      least k of the wave's entries reach B_w, so the k-th largest overall
 //      does too, and so does B = max_w B_w;
-//   2. the elements >= B (typically a few more than k) are gathered in LDS;
-//   3. each candidate's rank is the number of larger candidates; ranks below
+//   2. the entries >= B (typically a few more than k) are gathered in LDS;
+//   3. each gathered entry's rank is the number of larger ones; ranks below
 //      k are written in order.
-__global__ __launch_bounds__(kTileThreads) void topk_tile_kernel(const TileArgs a) {
-  __shared__ u64 cand[kTile];
-  __shared__ u64 wbound[kTileThreads / 64];
-  __shared__ uint32_t ncand;
-  const int tile = blockIdx.x, row = blockIdx.y;
+template <int E, bool AGENT>
+__device__ __forceinline__ void block_topk(const u64 (&x)[E], int k, SampleShared &sh, u64 *out) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int k = a.k;
-  if (t == 0) {
-    ncand = 0u;
-    if (a.counter && tile == 0 && row == 0) *a.counter = 0u;
+  u64 m = x[0];
+#pragma unroll
+  for (int e = 1; e < E; ++e) m = umax64(m, x[e]);
+  if (t == 0) sh.ncand = 0u;
+  sh.cand[t] = m;
+  __syncthreads();
+  const u64 bw = wave_kth_largest(sh.cand + 64 * wave, m, k);
+  if (lane == 0) sh.wbound[wave] = bw;
+  __syncthreads();
+  u64 B = sh.wbound[0];
+#pragma unroll
+  for (int w = 1; w < kTileThreads / 64; ++w) B = umax64(B, sh.wbound[w]);
+  // B = 0: no wave has k nonempty lanes; every entry is then a candidate
+  const u64 lo = B > 0 ? B : 1ull;
+
+  // each wave reserves room for its candidates (one LDS atomic), each lane
+  // writes its own at its prefix offset
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt += x[e] >= lo ? 1u : 0u;
+  const uint32_t incl = wave_inclusive_scan_u32(cnt);
+  const uint32_t wtotal = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  uint32_t wbase = 0u;
+  if (lane == 0 && wtotal) wbase = atomicAdd(&sh.ncand, wtotal);
+  uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase) + incl - cnt;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (x[e] >= lo) sh.cand[pos++] = x[e];
+  __syncthreads();
+
+  const int C = (int)sh.ncand;
+  if (t < kRankPad) sh.cand[C + t] = 0ull;
+  __syncthreads();
+  rank_and_place<kTileThreads, AGENT>(sh.cand, C, k, out, t);
+  for (int i = C + t; i < k; i += kTileThreads) {
+    if constexpr (AGENT) store_agent(out + i, 0ull);
+    else out[i] = 0ull;
   }
+}
+
+// Tile `tile` of row `row`: thread t holds logits 1024 j + 4 t + c (j < 8,
+// c < 4).  Every load is issued before the first use: eight 16-byte loads
+// for a full, aligned tile; otherwise 4-byte loads at indices clamped into
+// the tile (always in bounds), the out-of-range ones masked after.
+__device__ __forceinline__ void load_tile(const SampleArgs &a, int tile, int row, u64 (&x)[kPerThread]) {
+  const int t = threadIdx.x;
   const int64_t first = (int64_t)tile * kTile;
   const int64_t left = a.vocab - first;
   const int nvalid = left < kTile ? (int)left : kTile;
   const float *src = a.logits + (int64_t)row * a.row_stride + first;
-
-  u64 x[kPerThread];
+  if (a.vec && nvalid == kTile) {
+    float4 v[kPerThread / 4];
 #pragma unroll
-  for (int j = 0; j < kPerThread / 4; ++j) {
-    const int base = 1024 * j + 4 * t;
-    float f[4];
-    if (a.vec && base + 4 <= nvalid) {
-      const float4 v = *(const float4 *)(src + base);
-      f[0] = v.x, f[1] = v.y, f[2] = v.z, f[3] = v.w;
-    } else {
+    for (int j = 0; j < kPerThread / 4; ++j) v[j] = *(const float4 *)(src + 1024 * j + 4 * t);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) f[c] = base + c < nvalid ? src[base + c] : 0.f;
+    for (int j = 0; j < kPerThread / 4; ++j) {
+      const uint32_t id = (uint32_t)(first + 1024 * j + 4 * t);
+      x[4 * j + 0] = composite(v[j].x, id + 0);
+      x[4 * j + 1] = composite(v[j].y, id + 1);
+      x[4 * j + 2] = composite(v[j].z, id + 2);
+      x[4 * j + 3] = composite(v[j].w, id + 3);
+    }
+  } else {
+    float f[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = 1024 * (e >> 2) + 4 * t + (e & 3);
+      f[e] = src[i < nvalid ? i : nvalid - 1];
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      x[4 * j + c] = base + c < nvalid ? composite(f[c], (uint32_t)(first + base + c)) : 0ull;
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = 1024 * (e >> 2) + 4 * t + (e & 3);
+      x[e] = i < nvalid ? composite(f[e], (uint32_t)(first + i)) : 0ull;
+    }
   }
+}
 
-  u64 m = x[0];
+// Row `row`'s merge (all tiles' lists, read with device-scope loads) and, in
+// wave 0, the probabilities, the top-p cut and the draw.
+__device__ __forceinline__ void merge_and_draw(const SampleArgs &a, int row, SampleShared &sh) {
+  const int t = threadIdx.x, k = a.k, nl = a.tiles * k;
+  const u64 *src = a.lists + (int64_t)row * nl;
+  constexpr int E = kMaxList / kTileThreads;  // 8
+  u64 x[E];
 #pragma unroll
-  for (int e = 1; e < kPerThread; ++e) m = umax64(m, x[e]);
-  const u64 bw = wave_kth_largest(m, k);
-  if (lane == 0) wbound[wave] = bw;
+  for (int e = 0; e < E; ++e) {
+    const int i = t + kTileThreads * e;
+    x[e] = load_agent(src + (i < nl ? i : nl - 1));
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = t + kTileThreads * e < nl ? x[e] : 0ull;
+  block_topk<E, false>(x, k, sh, sh.top);
   __syncthreads();
-  u64 B = wbound[0];
-#pragma unroll
-  for (int w = 1; w < kTileThreads / 64; ++w) B = umax64(B, wbound[w]);
-  // B = 0: no wave has k valid lanes; every valid element is then a candidate
-  const u64 lo = B > 0 ? B : 1ull;
+  if (t >= 64) return;
 
-  int cnt = 0;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) cnt += __popcll(__ballot(x[e] >= lo));
-  uint32_t base = 0;
-  if (lane == 0 && cnt) base = atomicAdd(&ncand, (uint32_t)cnt);
-  base = __shfl(base, 0);
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const bool in = x[e] >= lo;
-    const u64 msk = __ballot(in);
-    if (in) cand[base + bits_below(msk)] = x[e];
-    base += (uint32_t)__popcll(msk);
-  }
-  __syncthreads();
+  const int lane = t;
+  const int kc = (int)(k < a.vocab ? k : a.vocab);  // candidates: min(k, V)
+  const bool valid = lane < kc;
+  const u64 v = valid ? sh.top[lane] : 0ull;
+  const int id = (int)(~(uint32_t)v);
+  const float z = key_value((uint32_t)(v >> 32));
+  const float z0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(z)));
+  const float e = valid ? expf((z - z0) * a.inv_temp) : 0.f;
+  const float S = wave_sum(e);
+  const float p = e / S;
+  const float incl_p = wave_inclusive_scan(p);
+  const float excl = wave_shift_up1(incl_p);
+  const u64 km = __ballot(valid && p > 0.f && excl < a.top_p);
+  const int mk = ~km ? __builtin_ctzll(~km) : 64;  // leading run of kept candidates
+  const bool in = lane < mk;
+  const float ek = in ? e : 0.f;
+  const float Sm = wave_sum(ek);
+  const float pk = in ? ek / Sm : 0.f;
+  const float u = philox_uniform(a.seed, (uint64_t)(a.pos0 + row), a.purpose);
+  const float target = u * Sm;
+  const float incl_e = wave_inclusive_scan(ek);
+  const u64 hit = __ballot(in && target < incl_e);
+  const int token = __builtin_amdgcn_readlane(id, hit ? __builtin_ctzll(hit) : mk - 1);
 
-  const int C = (int)ncand;
-  u64 *out = a.lists + ((int64_t)row * a.tiles + tile) * k;
-  for (int i = t; i < C; i += kTileThreads) {
-    const u64 v = cand[i];
-    int r = 0;
-    for (int j = 0; j < C; ++j) r += cand[j] > v ? 1 : 0;
-    if (r < k) out[r] = v;
+  // agent-scope stores: the acceptance may read them from another XCD
+  const int64_t o = (int64_t)row * k;
+  if (lane < k) {
+    store_agent(a.ids + o + lane, valid ? id : -1);
+    store_agent(a.probs + o + lane, pk);
   }
-  for (int i = C + t; i < k; i += kTileThreads) out[i] = 0ull;  // a tile with fewer than k logits
+  if (lane == 0) {
+    store_agent(a.kept + row, mk);
+    store_agent(a.tokens + row, token);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -242,145 +426,75 @@ __device__ void accept_wave(const AcceptArgs &a) {
   int acc = n - 1, tok = -1;
   for (int i = 0; i < n - 1; ++i) {
     const int d = a.drafts[i];
-    const int pk = clampi(a.p_kept[i], 0, a.p_stride), qk = clampi(a.q_kept[i], 0, a.q_stride);
-    const int pid = lane < pk ? a.p_ids[(int64_t)i * a.p_stride + lane] : -1;
-    const float pp = lane < pk ? a.p_probs[(int64_t)i * a.p_stride + lane] : 0.f;
-    const int qid = lane < qk ? a.q_ids[(int64_t)i * a.q_stride + lane] : -1;
-    const float qp = lane < qk ? a.q_probs[(int64_t)i * a.q_stride + lane] : 0.f;
-    const u64 ph = __ballot(lane < pk && pid == d), qh = __ballot(lane < qk && qid == d);
-    const float pd = ph ? __shfl(pp, __builtin_ctzll(ph)) : 0.f;
-    const float qd = qh ? __shfl(qp, __builtin_ctzll(qh)) : 0.f;
+    const int pk = clampi(load_agent(a.p_kept + i), 0, a.p_stride), qk = clampi(a.q_kept[i], 0, a.q_stride);
+    const bool pin = lane < pk, qin = lane < qk;
+    const int pid = pin ? load_agent(a.p_ids + (int64_t)i * a.p_stride + lane) : -1;
+    const float pp = pin ? load_agent(a.p_probs + (int64_t)i * a.p_stride + lane) : 0.f;
+    const int qid = qin ? a.q_ids[(int64_t)i * a.q_stride + lane] : -1;
+    const float qp = qin ? a.q_probs[(int64_t)i * a.q_stride + lane] : 0.f;
+    const u64 ph = __ballot(pin && pid == d), qh = __ballot(qin && qid == d);
+    const float pd = ph ? readlane_f(pp, __builtin_ctzll(ph)) : 0.f;
+    const float qd = qh ? readlane_f(qp, __builtin_ctzll(qh)) : 0.f;
     const float u = philox_uniform(a.seed, (uint64_t)(a.pos0 + i), VA_PURPOSE_ACCEPT);
     if (u * qd < pd) continue;
     // rejected at row i: replacement from max(0, p - q) over the row's kept tokens
     float qt = 0.f;
     bool found = false;
     for (int j = 0; j < qk; ++j) {
-      const int id2 = __shfl(qid, j);
-      const float pr2 = __shfl(qp, j);
+      const int id2 = __builtin_amdgcn_readlane(qid, j);
+      const float pr2 = readlane_f(qp, j);
       if (!found && pid == id2) qt = pr2, found = true;
     }
-    const float r = lane < pk ? fmaxf(0.f, pp - qt) : 0.f;
+    const float r = pin ? fmaxf(0.f, pp - qt) : 0.f;
     const float R = wave_sum(r);
     if (R > 0.f) {
       const float u2 = philox_uniform(a.seed, (uint64_t)(a.pos0 + i), VA_PURPOSE_RESIDUAL);
       const float incl = wave_inclusive_scan(r);
-      const u64 h = __ballot(lane < pk && u2 * R < incl);
-      tok = __shfl(pid, h ? __builtin_ctzll(h) : pk - 1);
+      const u64 h = __ballot(pin && u2 * R < incl);
+      tok = __builtin_amdgcn_readlane(pid, h ? __builtin_ctzll(h) : pk - 1);
     } else {
-      tok = a.p_tokens[i];
+      tok = load_agent(a.p_tokens + i);
     }
     acc = i;
     break;
   }
-  if (acc == n - 1) tok = a.p_tokens[n - 1];
+  if (acc == n - 1) tok = load_agent(a.p_tokens + (n - 1));
   for (int i = lane; i < n; i += 64) a.out_tokens[i] = i < acc ? a.drafts[i] : (i == acc ? tok : -1);
   if (lane == 0) *a.accepted = acc;
 }
 
 __global__ __launch_bounds__(64) void accept_kernel(const AcceptArgs a) { accept_wave(a); }
 
-// ---------------------------------------------------------------------------
-// Per-row merge, probabilities, top-p and the draw.
-// ---------------------------------------------------------------------------
-struct FinishArgs {
-  const u64 *lists;
-  uint32_t *counter;
-  int32_t *ids;
-  float *probs;
-  int32_t *kept, *tokens;
-  float inv_temp, top_p;
-  uint64_t seed;
-  int64_t pos0;
-  uint32_t purpose;
-  int32_t rows, k, tiles;
-  AcceptArgs acc;  // ACCEPT only
-};
-
-// One wave per row.  The row's tile lists (tiles x k composites, each list
-// sorted) are merged like a tile: B = the k-th largest of the lanes' maxima
-// bounds the k-th largest overall, the entries >= B are ranked by counting.
+// One workgroup per (tile, row).  The last workgroup of a row to finish its
+// tile merges the row; with ACCEPT the last row to be merged runs the
+// acceptance.  Each hand-off: the writers store with device-scope stores and
+// wait for them before a device-scope counter increment; the workgroup that
+// sees the final count reads with device-scope loads and resets the counter
+// for the next call.
 template <bool ACCEPT>
-__global__ __launch_bounds__(64) void sample_finish_kernel(const FinishArgs a) {
-  __shared__ u64 cand[kMaxList];
-  __shared__ u64 top[kMaxK];
-  const int row = blockIdx.x, lane = threadIdx.x;
-  const int k = a.k, nl = a.tiles * k;
-  const u64 *src = a.lists + (int64_t)row * nl;
+__global__ __launch_bounds__(kTileThreads) void sample_kernel(const SampleArgs a, const AcceptArgs acc) {
+  __shared__ SampleShared sh;
+  const int tile = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
+  u64 x[kPerThread];
+  load_tile(a, tile, row, x);
+  block_topk<kPerThread, true>(x, a.k, sh, a.lists + ((int64_t)row * a.tiles + tile) * a.k);
 
-  u64 x[kListPerLane];
-#pragma unroll
-  for (int e = 0; e < kListPerLane; ++e) {
-    const int i = lane + 64 * e;
-    x[e] = i < nl ? src[i] : 0ull;
-  }
-  u64 m = x[0];
-#pragma unroll
-  for (int e = 1; e < kListPerLane; ++e) m = umax64(m, x[e]);
-  const u64 B = wave_kth_largest(m, k);
-  const u64 lo = B > 0 ? B : 1ull;
-  int C = 0;
-#pragma unroll
-  for (int e = 0; e < kListPerLane; ++e) {
-    const bool in = x[e] >= lo;
-    const u64 msk = __ballot(in);
-    if (in) cand[C + bits_below(msk)] = x[e];
-    C += __popcll(msk);
-  }
+  wait_stores();
   __syncthreads();
-  for (int i = lane; i < C; i += 64) {
-    const u64 v = cand[i];
-    int r = 0;
-    for (int j = 0; j < C; ++j) r += cand[j] > v ? 1 : 0;
-    if (r < k) top[r] = v;
-  }
+  if (t == 0) sh.flag = atomicAdd(&a.row_count[row], 1u);
   __syncthreads();
-
-  const int kc = C < k ? C : k;  // min(k, V) candidates
-  const bool valid = lane < kc;
-  const u64 v = valid ? top[lane] : 0ull;
-  const int id = (int)(~(uint32_t)v);
-  const float z = key_value((uint32_t)(v >> 32));
-  const float z0 = __shfl(z, 0);
-  const float e = valid ? expf((z - z0) * a.inv_temp) : 0.f;
-  const float S = wave_sum(e);
-  const float p = e / S;
-  const float incl_p = wave_inclusive_scan(p);
-  float excl = __shfl_up(incl_p, 1);
-  excl = lane == 0 ? 0.f : excl;
-  const u64 km = __ballot(valid && p > 0.f && excl < a.top_p);
-  const int mk = ~km ? __builtin_ctzll(~km) : 64;  // leading run of kept candidates
-  const bool in = lane < mk;
-  const float ek = in ? e : 0.f;
-  const float Sm = wave_sum(ek);
-  const float pk = in ? ek / Sm : 0.f;
-  const float u = philox_uniform(a.seed, (uint64_t)(a.pos0 + row), a.purpose);
-  const float target = u * Sm;
-  const float incl_e = wave_inclusive_scan(ek);
-  const u64 hit = __ballot(in && target < incl_e);
-  const int token = __shfl(id, hit ? __builtin_ctzll(hit) : mk - 1);
-
-  const int64_t o = (int64_t)row * k;
-  if (lane < k) {
-    a.ids[o + lane] = valid ? id : -1;
-    a.probs[o + lane] = pk;
-  }
-  if (lane == 0) {
-    a.kept[row] = mk;
-    a.tokens[row] = token;
-  }
+  if (sh.flag != (uint32_t)(a.tiles - 1)) return;
+  merge_and_draw(a, row, sh);
+  if (t == 0) store_agent(a.row_count + row, 0u);
 
   if constexpr (ACCEPT) {
-    // The last row to get here runs the acceptance over every row's outputs:
-    // release this row's stores before counting, acquire the others' after.
-    __threadfence();
-    uint32_t prev = 0u;
-    if (lane == 0) prev = atomicAdd(a.counter, 1u);
-    prev = __shfl(prev, 0);
-    if (prev != (uint32_t)(a.rows - 1)) return;
-    __threadfence();
-    accept_wave(a.acc);
-    if (lane == 0) *a.counter = 0u;
+    wait_stores();
+    __syncthreads();
+    if (t == 0) sh.flag = atomicAdd(a.done, 1u);
+    __syncthreads();
+    if (sh.flag != (uint32_t)(a.rows - 1)) return;
+    if (t < 64) accept_wave(acc);
+    if (t == 0) store_agent(a.done, 0u);
   }
 }
 
@@ -408,6 +522,8 @@ size_t workspace_of(const va_sample_params *p) {
   return kListOffset + (size_t)p->rows * tiles_of(p) * p->top_k * sizeof(u64);
 }
 
+// Workspace layout: [0, 64) one arrival counter per row, [64, 68) the rows
+// counter, lists from byte 256.  The counters are zero between calls.
 va_status launch_sample(const va_sample_params *p, const float *logits, int32_t *ids, float *probs, int32_t *kept,
                         int32_t *tokens, void *workspace, size_t workspace_bytes, const AcceptArgs *acc,
                         hipStream_t stream) {
@@ -418,42 +534,34 @@ va_status launch_sample(const va_sample_params *p, const float *logits, int32_t 
   if (!workspace || !aligned(workspace, 16)) return VA_ERR_INVALID;
   if (workspace_bytes < workspace_of(p)) return VA_ERR_WORKSPACE;
   const int tiles = tiles_of(p);
-  uint32_t *counter = (uint32_t *)workspace;
-  u64 *lists = (u64 *)((uint8_t *)workspace + kListOffset);
-
-  TileArgs ta;
-  ta.logits = logits;
-  ta.lists = lists;
-  ta.counter = acc ? counter : nullptr;
-  ta.row_stride = p->row_stride;
-  ta.vocab = p->vocab;
-  ta.k = p->top_k;
-  ta.tiles = tiles;
-  ta.vec = aligned(logits, 16) && (p->row_stride & 3) == 0;
-  hipLaunchKernelGGL(topk_tile_kernel, dim3(tiles, p->rows), dim3(kTileThreads), 0, stream, ta);
-  if (hipGetLastError() != hipSuccess) return VA_ERR_HIP;
-
-  FinishArgs fa;
-  memset(&fa, 0, sizeof(fa));
-  fa.lists = lists;
-  fa.counter = counter;
-  fa.ids = ids;
-  fa.probs = probs;
-  fa.kept = kept;
-  fa.tokens = tokens;
-  fa.inv_temp = 1.0f / p->temperature;
-  fa.top_p = p->top_p;
-  fa.seed = p->seed;
-  fa.pos0 = p->first_position;
-  fa.purpose = p->purpose;
-  fa.rows = p->rows;
-  fa.k = p->top_k;
-  fa.tiles = tiles;
+  SampleArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.logits = logits;
+  sa.lists = (u64 *)((uint8_t *)workspace + kListOffset);
+  sa.row_count = (uint32_t *)workspace;
+  sa.done = (uint32_t *)((uint8_t *)workspace + 64);
+  sa.row_stride = p->row_stride;
+  sa.vocab = p->vocab;
+  sa.k = p->top_k;
+  sa.tiles = tiles;
+  sa.rows = p->rows;
+  sa.vec = aligned(logits, 16) && (p->row_stride & 3) == 0;
+  sa.ids = ids;
+  sa.probs = probs;
+  sa.kept = kept;
+  sa.tokens = tokens;
+  sa.inv_temp = 1.0f / p->temperature;
+  sa.top_p = p->top_p;
+  sa.seed = p->seed;
+  sa.pos0 = p->first_position;
+  sa.purpose = p->purpose;
+  const dim3 grid(tiles, p->rows), block(kTileThreads);
   if (acc) {
-    fa.acc = *acc;
-    hipLaunchKernelGGL((sample_finish_kernel<true>), dim3(p->rows), dim3(64), 0, stream, fa);
+    hipLaunchKernelGGL((sample_kernel<true>), grid, block, 0, stream, sa, *acc);
   } else {
-    hipLaunchKernelGGL((sample_finish_kernel<false>), dim3(p->rows), dim3(64), 0, stream, fa);
+    AcceptArgs none;
+    memset(&none, 0, sizeof(none));
+    hipLaunchKernelGGL((sample_kernel<false>), grid, block, 0, stream, sa, none);
   }
   return hipGetLastError() == hipSuccess ? VA_OK : VA_ERR_HIP;
 }

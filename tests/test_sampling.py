@@ -147,6 +147,29 @@ def test_sample_strided_rows_and_many_positions():
 
 
 @pytest.mark.gpu
+def test_workspace_reused_across_shapes():
+    """One zero-filled workspace serves calls of other shapes in a row (its
+    counters return to zero after every call), with and without acceptance."""
+    big = va.sample_params(16, 160000, top_k=64)
+    ws = va.sample_workspace_for(big, DEV)
+    g = synth.gen(31)
+    for rows, V, k in ((16, 160000, 64), (3, 20000, 20), (8, 8193, 7), (16, 160000, 64), (1, 5, 20)):
+        z = synth.logits_f32(rows, V, g, "lm")
+        a = to_np(va.va_sample(z.to(DEV), top_k=k, seed=rows, first_position=V, workspace=ws))
+        near = compare_sample(a, z, k, 0.95, 1.0, rows, V, 0, f"reuse rows={rows} V={V}")
+        assert near <= max(1, rows // 4)
+        out, acc, toks = va.va_sample_accept(z.to(DEV), *([None] * 4 if rows == 1 else [
+            torch.from_numpy(a["ids"][: rows - 1]).to(DEV), torch.from_numpy(a["probs"][: rows - 1]).to(DEV),
+            torch.from_numpy(a["kept"][: rows - 1]).to(DEV), torch.from_numpy(a["tokens"][: rows - 1]).to(DEV)]),
+            top_k=k, seed=rows, first_position=V, workspace=ws)
+        b = to_np(out)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), key
+        # drafts equal to the target's own draws with q = p are all accepted
+        assert int(acc.item()) == rows - 1
+
+
+@pytest.mark.gpu
 def test_sample_deterministic_and_seeded():
     g = synth.gen(5)
     z = synth.logits_f32(8, 20000, g, "flat").to(DEV)
@@ -266,7 +289,7 @@ def test_fused_equals_separate_and_graph_replay(n):
     zt = zt.to(DEV)
     q = [None if x is None else torch.from_numpy(x).to(DEV) for x in res["q"]]
     p = va.sample_params(n, 160000, seed=seed, first_position=pos0)
-    ws = torch.empty((va.sample_workspace_bytes(p) + 7) // 8, dtype=torch.int64, device=DEV)
+    ws = va.sample_workspace_for(p, DEV)
     o = dict(ids=torch.empty((n, 20), dtype=torch.int32, device=DEV),
              probs=torch.empty((n, 20), dtype=torch.float32, device=DEV),
              kept=torch.empty(n, dtype=torch.int32, device=DEV), tokens=torch.empty(n, dtype=torch.int32, device=DEV))
