@@ -102,7 +102,9 @@ def summarize_profiles(d):
     per_launch = [f * f_scale * 1024 + w * w_scale * 1024 for (_, f), (_, w) in zip(fe, wr)]
     traffic = sum(per_launch) / len(per_launch)
     contexts = bench_line("fetch.log")["config"]["contexts"]
-    json.dump({"kernel_hash": kernel_hash(), "contexts": contexts, "hbm_bytes_per_launch": round(traffic),
+    splits = [e["splits"] for e in bench_line("fetch.log")["sweep"]]
+    json.dump({"kernel_hash": kernel_hash(), "contexts": contexts, "splits": splits,
+               "hbm_bytes_per_launch": round(traffic),
                "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "launches": len(per_launch)},
               open(TRAFFIC_FILE, "w"), indent=1)
 
@@ -624,7 +626,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             tr = json.load(open(TRAFFIC_FILE))
-            if tr.get("kernel_hash") == kernel_hash() and sorted(tr.get("contexts", [])) == sorted(contexts):
+            if (tr.get("kernel_hash") == kernel_hash() and tr.get("contexts") == contexts
+                    and tr.get("splits") == [c["plan"].splits for c in cases]):
                 traffic = tr.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
