@@ -92,8 +92,8 @@ def summarize_profiles(d):
     cw = [v for n, g, v in counters("pmc_copy_write", "copy_counter_collection.csv") if "copyBuffer" in n]
     f_scale = copy_bytes / (sum(cf) / len(cf) * 1024)
     w_scale = copy_bytes / (sum(cw) / len(cw) * 1024)
-    def static_split(n):  # the static-plan split kernel (the device-state instances are timed apart)
-        return "split_kernel" in n and "true>" not in n.replace(" ", "")
+    def static_split(n):  # the sweep's kernel: static plan, D 128, 3 consumer waves, bf16
+        return "split_kernel<128,3,0,4,2,false>" in n.replace(" ", "")
 
     fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if static_split(n)]
     wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if static_split(n)]
@@ -392,6 +392,88 @@ def bench_sampler(torch, va, synth, dev, reps=100, replicas=4, cpu_seconds=5.0, 
                       "kernel_hash": sample_hash()}), flush=True)
 
 
+def bench_other_configs(torch, va, synth, dev, reps=20, replicas=4):
+    """The other configurations of the verification call, each timed as one
+    call (ring write where the rows' K/V go to the ring first, split,
+    combine) from a graph of `reps` back-to-back calls over `replicas` cold
+    caches:
+      window  Hkv 1, Hq 6, D 64, 8 rows (5 live), window 4,096 over a
+              4,160-slot ring, rows at 5,120 / 51,200 / 194,560, sink on;
+      tree    Hkv 4, Hq 24, D 128, a 16-node random tree over a 2K / 8K /
+              32K prefix, no sink;
+      tree-q  the same tree over a 64K prefix, keys E4M3 after the rotation,
+              values INT8 with an FP32 scale per (token, head).
+    KV bytes are the algorithmic read (visible keys once per KV head)."""
+    out = []
+    g = synth.gen(9500)
+    cases = []
+    for t0 in (5120, 51200, 194560):
+        cases.append(("window", dict(rows=8, live_rows=5, q_heads=6, kv_heads=1, head_dim=64, mask="window",
+                                     first_pos=t0, window=4096, ring_slots=4160), t0))
+    for P in (2048, 8192, 32768):
+        cases.append(("tree", dict(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree",
+                                   prefix_len=P, parent=synth.random_tree(16, g), kv_capacity=P + 16 + 64), P))
+    cases.append(("tree-q", dict(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree",
+                                 kv_fmt="e4m3_wht_i8", prefix_len=65536, parent=synth.random_tree(16, g),
+                                 kv_capacity=65536 + 16 + 64), 65536))
+    cur = torch.cuda.current_stream
+    for kind, kw, pos in cases:
+        plan = va.Plan(**kw)
+        hkv, d, rows, hq = kw["kv_heads"], kw["head_dim"], kw["rows"], kw["q_heads"]
+        slots = kw.get("ring_slots") or kw["kv_capacity"]
+        quant = kind == "tree-q"
+        lo, hi = plan.info["lo"], plan.info["hi"]
+        kv_bytes = hkv * (hi - lo) * ((2 * d + 4) if quant else 4 * d)
+        q = synth.normal_bf16((rows, hq, d), g).to(dev)
+        sink = synth.normal_f32((hq,), g).to(dev) if kind == "window" else None
+        reps_kv = []
+        for r in range(replicas):
+            if quant:
+                k = torch.randint(0, 126, (hkv, slots, d), dtype=torch.uint8, device=dev)
+                v = torch.randint(-127, 128, (hkv, slots, d), dtype=torch.int8, device=dev)
+                vs = torch.rand((hkv, slots), device=dev) * 0.02
+            else:
+                k = synth.normal_bf16_device((hkv, slots, d), 7000 + 10 * r + pos % 997, dev)
+                v = synth.normal_bf16_device((hkv, slots, d), 7001 + 10 * r + pos % 997, dev)
+                vs = None
+            reps_kv.append((k, v, vs))
+        k_new = synth.normal_bf16((rows, hkv, d), g).to(dev)
+        v_new = synth.normal_bf16((rows, hkv, d), g).to(dev)
+        ws = va.workspace_for(plan, dev)
+        o = torch.empty((rows, hq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
+
+        def one(i, split_only=False):
+            k, v, vs = reps_kv[i % replicas]
+            if kind == "window" and not split_only:
+                va.swa_ring_write(k_new, v_new, pos, k, v, stream=cur())
+            va.verify_attn_split(plan, q, k, v, ws, v_scale=vs, stream=cur())
+            if not split_only:
+                va.verify_attn_combine(plan, ws, o, lse=lse, sink=sink, stream=cur())
+        times = {}
+        for label, so in (("call", False), ("split", True)):
+            for i in range(2):
+                one(i, so)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(reps):
+                    one(i, so)
+            gr.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times[label] = a.elapsed_time(b) * 1e3 / reps
+            del gr
+        out.append({"config": kind, "position": pos, "splits": plan.splits, "kv_bytes": kv_bytes,
+                    "us_per_call": round(times["call"], 2), "split_us": round(times["split"], 2),
+                    "kv_gbs_split": round(kv_bytes / (times["split"] * 1e-6) / 1e9, 1),
+                    "pct_hbm_peak_split": round(100 * kv_bytes / (times["split"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
+        del reps_kv
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -637,6 +719,9 @@ def main():
                 "kernel": "split_kernel<D=128,W=3,bf16,NST=4,NPW=2,STATE=false>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
                 "avg_launch_us": round(split_ms / launches * 1e3, 2), "launches": launches}
 
+    # ---------------- pass D: the other configurations ----------------
+    other = bench_other_configs(torch, va, synth, dev)
+
     # ---------------- CPU baseline (oracle) + full-size parity ----------------
     cpu = None
     parity = None
@@ -695,7 +780,7 @@ def main():
                    "launch": "HIP graph replay",
                    "state_bucket": f"{ROWS} rows at {max(contexts)}, {bucket.splits} splits"},
         "eager_launch_ms_per_step": round(eager_ms_per_step, 4),
-        "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "sweep": sweep,
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "sweep": sweep, "other_configs": other,
         "wall_s_timed": round(t_wall, 4), "kernel_hash": kernel_hash(),
     }
     print(json.dumps(line), flush=True)

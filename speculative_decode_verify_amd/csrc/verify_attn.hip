@@ -215,6 +215,13 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
   out[3] = b[1];
 }
 
+// Two E4M3FN codes (bytes 0-1, or 2-3 with hi) -> two bf16, exact (the gfx950
+// scaled converter with scale 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // LDS DMA: lane l copies `bytes` from its global address to lds + bytes*l
 // (the LDS base is wave-uniform).  Kept out of the kernel templates: the
 // builtin exists only for the device.
@@ -311,7 +318,14 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
   static_assert(FMT == 0 || NPW == 1, "the scale DMA belongs to a single producer");
   static_assert((2 * NDMA) % NPW == 0, "producers share a chunk's DMA evenly");
   static_assert((NST - 2) * kVmP <= 63, "vmcnt counts at most 63 loads");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * kStageB];
+  static_assert(FMT == 0 || NST >= 3, "the quantised pipeline stages one chunk ahead of the decode");
+  // Quantised formats: the consumers decode every chunk once, together, into
+  // bf16 tiles (two buffers, [K | V]); each then reads bf16 operands as for
+  // bf16 caches instead of converting the whole chunk in every wave.
+  constexpr int kDecRow = 2 * D;                         // bf16 bytes per key row
+  constexpr int kDecTile = kChunk * kDecRow;             // one decoded K or V tile
+  constexpr int kDecB = FMT == 1 ? 2 * 2 * kDecTile : 0;  // two buffers of K and V
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * kStageB + kDecB];
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps chunk indices and mask decisions in scalar registers
@@ -443,12 +457,26 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
 #pragma unroll
       for (int j = 0; j < NST - 1; ++j)
         if (j < nch) issue(j, j);
+      if constexpr (FMT == 1) {
+        // the consumers decode chunk n + 1 right after barrier n, so chunk 0
+        // must have landed before an extra first barrier, and chunk n + 1
+        // before barrier n
+        const int32_t ahead = nch - 1;
+        wait_chunks<kVmP, NST - 2>(ahead < NST - 2 ? (ahead > 0 ? ahead : 0) : NST - 2);
+        wg_barrier();
+      }
       int st_prev = NST - 1;  // stage of chunk n - 1
       for (int32_t n = 0; n < nch; ++n) {
         // chunks issued after n: n+1 .. min(n + NST - 2, nch - 1); DMA groups
-        // complete in issue order, so this wait leaves exactly those in flight.
+        // complete in issue order, so this wait leaves exactly those in flight
+        // (for the quantised formats, those after n + 1).
         const int32_t later = nch - 1 - n;
-        wait_chunks<kVmP, NST - 2>(later < NST - 2 ? later : NST - 2);
+        if constexpr (FMT == 0) {
+          wait_chunks<kVmP, NST - 2>(later < NST - 2 ? later : NST - 2);
+        } else {
+          const int32_t after = later - 1;
+          wait_chunks<kVmP, NST - 3>(after < NST - 3 ? (after > 0 ? after : 0) : NST - 3);
+        }
         wg_barrier();
         if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
         st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
@@ -574,9 +602,77 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
   auto fk = [](int row) { return row & (PIECES - 1); };
   auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
 
+  // Decoded tiles (quantised formats): buffer b holds K at dec + b*2*kDecTile
+  // and V after it.  V is bf16 in the bf16 layout (piece P of a row at
+  // 16*(P ^ fv0(row)), fv0 = 2*(row % 8)); K keeps each staged 16-code piece
+  // in its staged slot q, expanded to two bf16 halves at 16-byte positions
+  // (2q + half) ^ (row % 16), so that the 16 lanes reading one operand hit
+  // 16 different positions.
+  uint8_t *const dec = smem + NST * kStageB;
+  auto fv0 = [](int row) { return (2 * row) & 14; };
+  // A consumer lane's decode units: 16 * kChunk units of 16 codes per chunk
+  // (V first, then K), unit u on lane u % (64 * W) -- 64 consecutive units
+  // per wave, so every wave converts one kind at a time.  The codes are read
+  // before the step of the previous chunk and converted after it, so their
+  // LDS latency hides behind the step.
+  constexpr int kUnits = 16 * kChunk;
+  constexpr int NU = (kUnits + 64 * W - 1) / (64 * W);
+  u32x4 codes[FMT == 1 ? NU : 1];
+  auto decode_load = [&](int32_t n) {
+    if constexpr (FMT == 1) {
+      const uint8_t *qs = smem + (n % NST) * kStageB;
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        const int u = 64 * wave + lane + 64 * W * i;
+        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
+        if (u < kUnits) codes[i] = *(const u32x4 *)(qs + (u < 8 * kChunk ? kTileB : 0) + row * KROW + 16 * pc);
+      }
+    }
+  };
+  auto decode_store = [&](int32_t n) {
+    if constexpr (FMT == 1) {
+      uint8_t *dk = dec + (n & 1) * 2 * kDecTile;
+      uint8_t *dv = dk + kDecTile;
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        const int u = 64 * wave + lane + 64 * W * i;
+        if (u >= kUnits) continue;
+        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
+        const u32x4 c = codes[i];
+        if (u < 8 * kChunk) {  // INT8 values: exact in bf16 (|code| <= 127)
+          u32x4 h[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = c[e];
+            const float f0 = (float)((int32_t)(w << 24) >> 24), f1 = (float)((int32_t)(w << 16) >> 24);
+            const float f2 = (float)((int32_t)(w << 8) >> 24), f3 = (float)((int32_t)w >> 24);
+            h[e >> 1][2 * (e & 1)] = pack_bf16x2(f0, f1);
+            h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
+          }
+          uint8_t *dst = dv + row * kDecRow + 16 * ((2 * pc) ^ fv0(row));
+          *(u32x4 *)dst = h[0];
+          *(u32x4 *)(dst + 16) = h[1];
+        } else {  // E4M3 keys: exact in bf16
+          u32x4 h[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e >> 1][2 * (e & 1)] = e4m3x2_to_bf16x2<false>(c[e]);
+            h[e >> 1][2 * (e & 1) + 1] = e4m3x2_to_bf16x2<true>(c[e]);
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            *(u32x4 *)(dk + row * kDecRow + 16 * ((2 * pc + half) ^ (row & 15))) = h[half];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is whole at the next barrier
+    }
+  };
+
   auto step = [&](int32_t n, const uint8_t *kt) {
     const uint8_t *vt = kt + kTileB;
     const int32_t c0 = (c_first + n) * kChunk;
+    const uint8_t *dk = dec + (n & 1) * 2 * kDecTile;  // decoded tiles (quantised formats)
+    const uint8_t *dv = dk + kDecTile;
 
     // ---- K operands: A operand of block mb is keys 16*mb + i16 ----
     bf16x8 kop[2][KS];
@@ -590,17 +686,11 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
       } else {
 #pragma unroll
         for (int kp2 = 0; kp2 < KS / 2; ++kp2) {
-          // 16 E4M3 codes: first 8 -> step 2*kp2, last 8 -> step 2*kp2+1
-          const u32x4 w = *(const u32x4 *)(kt + row * KROW + 16 * ((4 * kp2 + g4) ^ fk(row)));
+          // staged piece (16 codes): first 8 -> step 2*kp2, last 8 -> step 2*kp2+1
+          const int q = (4 * kp2 + g4) ^ fk(row);
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            float f[8];
-            e4m3x4_to_f32(w[2 * half], f);
-            e4m3x4_to_f32(w[2 * half + 1], f + 4);
-            u32x4 o4 = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                        pack_bf16x2(f[6], f[7])};
-            kop[mb][2 * kp2 + half] = __builtin_bit_cast(bf16x8, o4);
-          }
+          for (int half = 0; half < 2; ++half)
+            kop[mb][2 * kp2 + half] = *(const bf16x8 *)(dk + row * kDecRow + 16 * ((2 * q + half) ^ (row & 15)));
         }
       }
     }
@@ -624,15 +714,17 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
         vop[md] = __builtin_bit_cast(bf16x8, w);
       }
     } else {
+      // the decoded bf16 tile, read as for bf16 caches
+      const int rowA = 4 * g4 + (i16 >> 2);
+      const int F = fv0(rowA) >> 1;
+      const uint8_t *vb = dv + rowA * kDecRow + 8 * (i16 & 3);
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const int d = 16 * md + i16;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int row = t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4);
-          const int8_t c = *(const int8_t *)(vt + row * KROW + d);
-          vop[md][t] = (__bf16)(float)c;  // exact
-        }
+        const uint8_t *pa = vb + 32 * (md ^ F);
+        const u32x2 lo = lds_read_tr16(pa);
+        const u32x2 hi = lds_read_tr16(pa + 16 * kDecRow);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        vop[md] = __builtin_bit_cast(bf16x8, w);
       }
       const float *sct = (const float *)(vt + kTileB);
 #pragma unroll
@@ -710,10 +802,20 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
     for (int md = 0; md < MD; ++md) o[md] = mfma16(vop[md], pb, o[md]);
   };
 
+  if constexpr (FMT == 1) {
+    wg_barrier();  // chunk 0 is staged
+    if (nch > 0) {
+      decode_load(0);
+      decode_store(0);
+    }
+  }
   int st = 0;  // stage of chunk n
   for (int32_t n = 0; n < nch; ++n) {
-    wg_barrier();  // chunk n is in LDS; every consumer has left chunk n - 1
+    wg_barrier();  // chunk n is in LDS (decoded); every consumer has left chunk n - 1
+    const bool next = n + 1 < nch;
+    if (next) decode_load(n + 1);  // quantised formats: all consumers, active or not
     if (active) step(n, smem + st * kStageB);
+    if (next) decode_store(n + 1);
     st = st + 1 == NST ? 0 : st + 1;
   }
 
