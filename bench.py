@@ -43,6 +43,9 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 REPLICAS = 6
 METRIC = "verify-attn µs/call and KV-read GB/s (% HBM peak), 8 rows×6 heads, 1K–192K ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep_traffic.json")
+UTIL_FILE = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep_util.json")
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT "
+                 "SQ_LDS_IDX_ACTIVE")
 COPY_PROBE_MIB = 1024
 KERNEL_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "verify_attn.hip")
 SAMPLE_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "sample.hip")
@@ -112,7 +115,8 @@ def summarize_profiles(d):
     dur = collections.defaultdict(list)
     for r in trace:
         n = r["Kernel_Name"]
-        kind = "split_kernel" if "split_kernel" in n else "combine_kernel" if "combine_kernel" in n else None
+        kind = ("split_kernel" if "split_kernel" in n else "combine_kernel" if "combine_kernel" in n
+                else "read_probe_kernel" if "read_probe_kernel" in n else None)
         if kind and "<" in n:
             kind += n[n.index("<"):n.index(">") + 1].replace(" ", "")
         if kind:
@@ -141,6 +145,10 @@ def summarize_profiles(d):
             if v:
                 out.append(f"| {kind} ({label}, all) | all | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} "
                            f"| {max(v):.2f} |")
+    v = tot.get("read_probe_kernel")
+    if v:
+        out.append(f"| read_probe_kernel (plain read of the same bytes, all) | all | {len(v)} | "
+                   f"{sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     out.append("")
     out.append("bench line of the same command (events; the trace itself slows the launches): "
                f"roofline avg_launch_us {bl['roofline']['avg_launch_us']}, value {bl['value']} GB/s")
@@ -166,6 +174,68 @@ def summarize_profiles(d):
     out.append("")
     out.append(f"mean HBM bytes per split launch over the sweep: {traffic:.0f}"
                f" (algorithmic KV bytes per launch: {bl['roofline']['algorithmic_bytes_per_launch']})")
+
+    up = os.path.join(d, "pmc_util", "bench_counter_collection.csv")
+    if os.path.exists(up):
+        if bench_line("util.log")["kernel_hash"] != kernel_hash():
+            raise SystemExit("utilisation counters of another kernel source")
+        # Counter values are whole-GPU totals per dispatch (SQ_INSTS_MFMA of
+        # the 33-workgroup launch is exactly 33 x 3 waves x 16).  Busy
+        # fractions divide by the kernel-trace duration of the same kernel
+        # and grid at the 2.4 GHz peak clock (a lower bound if the clock ran
+        # lower); GRBM_GUI_ACTIVE is not used, since under --pmc it also
+        # counts the serialised launch around each dispatch.
+        kinds = [("split_kernel<128,3,0,4,2,false>", "split: sweep (D 128, 3 consumers, bf16)"),
+                 ("split_kernel<64,3,0,8,2,false>", "split: window ring (D 64, 3 consumers)"),
+                 ("split_kernel<128,6,0,4,2,false>", "split: tree (D 128, 6 consumers, bf16)"),
+                 ("split_kernel<128,6,1,8,1,false>", "split: quantised tree (6 consumers, 1 decoder)")]
+        tdur = collections.defaultdict(list)
+        for (kind, n, wgs), v in dur.items():
+            tdur[(kind, wgs)] += v
+        vals = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(up)):
+            n = r["Kernel_Name"].replace(" ", "")
+            wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+            for key, _ in kinds:
+                if key in n:
+                    vals[(key, wgs)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        out += ["", "## MFMA and LDS activity of split_kernel (rocprofv3 --pmc, one run)", "",
+                f"command: rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d <dir>/pmc_util -o bench -- {py} --steps 2 "
+                "--warmup 0 --kernel-reps 4 --no-cpu-baseline", "",
+                "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x trace duration x 2.4 GHz); MFMA TFLOP/s = "
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / trace duration; LDS conflict = SQ_LDS_BANK_CONFLICT / "
+                "(SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT).", "",
+                "| kernel | workgroups | dispatches | MFMA per dispatch | trace us | MFMA busy % | MFMA TFLOP/s | "
+                "LDS conflict |", "|---|---|---|---|---|---|---|---|"]
+        summary = {}
+        tot_busy = tot_us = 0.0
+        for key, label in kinds:
+            for (k2, wgs) in sorted(x for x in vals if x[0] == key):
+                v = vals[(k2, wgs)]
+                t = tdur.get((key, wgs))
+                if not t or not v.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                    continue
+                us = sum(t) / len(t)
+                busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(v["SQ_VALU_MFMA_BUSY_CYCLES"])
+                mops = sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) / len(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+                ninst = sum(v["SQ_INSTS_MFMA"]) / len(v["SQ_INSTS_MFMA"])
+                conf = sum(v["SQ_LDS_BANK_CONFLICT"])
+                act = sum(v["SQ_LDS_IDX_ACTIVE"])
+                pct = 100 * busy / (1024 * us * 1e-6 * 2.4e9)
+                tf = mops * 512 / (us * 1e-6) / 1e12
+                lc = conf / (act - conf) if act > conf else 0.0
+                out.append(f"| {label} | {wgs} | {len(v['SQ_VALU_MFMA_BUSY_CYCLES'])} | {ninst:.0f} | {us:.2f} | "
+                           f"{pct:.1f} | {tf:.1f} | {lc:.3f} |")
+                summary[f"{key}@{wgs}"] = {"mfma_busy_pct": round(pct, 2), "mfma_tflops": round(tf, 1),
+                                           "lds_conflict": round(lc, 4)}
+                if key == kinds[0][0]:
+                    tot_busy += busy * len(t)
+                    tot_us += us * len(t)
+        if tot_us:
+            sweep_pct = 100 * tot_busy / (1024 * tot_us * 1e-6 * 2.4e9)
+            out += ["", f"sweep kernel, launches weighted as in the trace: MFMA busy {sweep_pct:.1f}%"]
+            json.dump({"kernel_hash": kernel_hash(), "kernel": kinds[0][0], "mfma_busy_pct": round(sweep_pct, 2),
+                       "clock_ghz": 2.4, "by_kernel": summary}, open(UTIL_FILE, "w"), indent=1)
     name = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep.md")
     open(name, "w").write("\n".join(out) + "\n")
     print(f"wrote {name} and {TRAFFIC_FILE}")
@@ -658,6 +728,39 @@ def main():
     achieved = split_bytes / (split_ms * 1e-3) / 1e9
     launches = len(cases) * args.kernel_reps
 
+    # ---------------- pass B2: the read-stream ceiling ----------------
+    # A plain streaming read of each context's KV byte count (one launch,
+    # 16-byte loads, a full grid), rotated over cold buffers and timed like
+    # pass B: what one launch can read from HBM at that size, the ceiling
+    # the split kernel's rate is compared with beside the 8 TB/s peak.
+    flat = [torch.empty(max(kv_bytes(c["hi"]) for c in cases), dtype=torch.uint8, device=dev)
+            for _ in range(args.replicas)]
+    for f in flat:
+        f.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe_bytes, probe_ms = 0.0, 0.0
+    for c, entry in zip(cases, sweep):
+        nb = kv_bytes(c["hi"])
+
+        def reads(nb=nb):
+            for i in range(args.kernel_reps):
+                va.va_read_probe(flat[i % args.replicas], nb, sink, stream=torch.cuda.current_stream())
+        gr = capture(reads)
+        gr.replay()
+        a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record(stream)
+        gr.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        del gr
+        r_avg = a.elapsed_time(b) / args.kernel_reps
+        probe_bytes += nb * args.kernel_reps
+        probe_ms += r_avg * args.kernel_reps
+        entry["read_probe_us"] = round(r_avg * 1e3, 2)
+        entry["read_probe_gbs"] = round(nb / (r_avg * 1e-3) / 1e9, 1)
+    del flat
+    read_ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
+
     # ---------------- pass C: the device-state entry points ----------------
     # One plan for a bucket covering the whole sweep (8 rows at the largest
     # context) fixes the grid; each context's positions and live rows come
@@ -714,10 +817,24 @@ def main():
         except Exception:
             traffic = None
 
+    mfma_busy = None
+    if os.path.exists(UTIL_FILE):
+        try:
+            ut = json.load(open(UTIL_FILE))
+            if ut.get("kernel_hash") == kernel_hash():
+                mfma_busy = ut.get("mfma_busy_pct")
+        except Exception:
+            mfma_busy = None
+
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "split_kernel<D=128,W=3,bf16,NST=4,NPW=2,STATE=false>", "algorithmic_bytes_per_launch": round(split_bytes / launches),
-                "avg_launch_us": round(split_ms / launches * 1e3, 2), "launches": launches}
+                "avg_launch_us": round(split_ms / launches * 1e3, 2), "launches": launches,
+                "mfma_busy_pct": mfma_busy,
+                "read_ceiling": {"kernel": "read_probe_kernel (plain 16-byte streaming read)",
+                                 "achieved": round(read_ceiling, 1),
+                                 "avg_launch_us": round(probe_ms / launches * 1e3, 2),
+                                 "split_frac_of_ceiling": round(achieved / read_ceiling, 4)}}
 
     # ---------------- pass D: the other configurations ----------------
     other = bench_other_configs(torch, va, synth, dev)
@@ -747,11 +864,14 @@ def main():
         # until about 10 s of oracle time, at most 20 passes; the first pass
         # is also the full-size parity check.
         passes = 0
+        t_ctx = [0.0] * len(cases)
         while passes < 20 and (passes == 0 or t_cpu < args.cpu_seconds):
-            for c, (kc, vc, qc, sc, p), (o_gpu, l_gpu) in zip(cases, host, gpu_out0):
+            for i, (c, (kc, vc, qc, sc, p), (o_gpu, l_gpu)) in enumerate(zip(cases, host, gpu_out0)):
                 t = time.perf_counter()
                 ro, rl = oattn.verify_attn_ref(p, qc, oattn.Cache(kc, vc), 1 / math.sqrt(D), sc)
-                t_cpu += time.perf_counter() - t
+                dt = time.perf_counter() - t
+                t_cpu += dt
+                t_ctx[i] += dt
                 if passes:
                     continue
                 L = c["live"]
@@ -763,6 +883,8 @@ def main():
                 max_err = max(max_err, float(err.max()))
                 max_lse = max(max_lse, float(dl.max()))
             passes += 1
+        for entry, tc in zip(sweep, t_ctx):
+            entry["oracle_s_per_call"] = round(tc / passes, 5)
         cpu = {"value": round(passes * bytes_per_step / t_cpu / 1e9, 4), "unit": "GB/s", "cores": int(threads),
                "kind": "oracle",
                "sample": f"{passes} passes over the {len(cases)} contexts (replica 0's stored bytes), "

@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     swa_ring_write, verify_kv_write, verify_attn, workspace_for,
     library_path, load_library, MASKS, KV_FORMATS,
     sample_params, sample_workspace_bytes, sample_workspace_for, va_sample, va_accept, va_sample_accept,
-    PURPOSE_TARGET, PURPOSE_ACCEPT, PURPOSE_RESIDUAL,
+    PURPOSE_TARGET, PURPOSE_ACCEPT, PURPOSE_RESIDUAL, va_read_probe,
 )

@@ -101,12 +101,13 @@ def load_library():
     lib.va_sample.argtypes = [SP, V, V, V, V, V, V, SZ, V]
     lib.va_accept.argtypes = [V, V, V, V, I32, V, V, V, I32, V, I32, ctypes.c_uint64, I64, V, V, V]
     lib.va_sample_accept.argtypes = [SP, V, V, V, V, I32, V, V, V, V, V, V, V, V, SZ, V]
+    lib.va_read_probe.argtypes = [V, SZ, V, V]
     lib.va_status_string.argtypes = [ctypes.c_int]
     lib.va_status_string.restype = ctypes.c_char_p
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
                "verify_attn_split", "verify_attn_combine", "verify_attn_split_state",
                "verify_attn_combine_state", "swa_ring_write", "verify_kv_write", "va_sample", "va_accept",
-               "va_sample_accept"):
+               "va_sample_accept", "va_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -479,3 +480,10 @@ def va_sample_accept(logits, q_ids, q_probs, q_kept, drafts, top_k=20, top_p=0.9
         _ptr(out["tokens"]), _ptr(accepted), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
     return out, accepted, out_tokens
+
+
+def va_read_probe(src, nbytes, sink, stream=None):
+    """Stream nbytes of the device tensor src (measurement only)."""
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds the tensor")
+    _check("va_read_probe", _lib().va_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)))

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libverify_attn.so")
 
-SOURCES = ["verify_attn.hip", "sample.hip", "plan.cpp"]
+SOURCES = ["verify_attn.hip", "sample.hip", "probe.hip", "plan.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

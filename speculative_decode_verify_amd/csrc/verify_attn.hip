@@ -243,11 +243,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel: one workgroup per (split, KV head) with W + NPW wave64s.
+// Split kernel: one workgroup per (split, KV head) with W + NDW + NPW wave64s.
 //   Consumers, waves 0..W-1: wave w owns query matrix rows [16w, 16w + 16)
 //     for the whole split and keeps their online-softmax state in registers;
 //     every consumer walks all of the split's 32-key chunks in order.
-//   Producers, waves W..W+NPW-1: fill a ring of NST LDS stages (chunk j in
+//   Decoders (quantised formats, NDW = 1), waves W..W+NDW-1: convert each
+//     staged chunk to bf16 tiles one chunk ahead of the consumers, a share
+//     each.  Waves go to the four SIMDs in turn, so with six consumers wave
+//     W shares a SIMD that holds one consumer, not two, and the conversion
+//     overlaps the consumers' steps.
+//   Producers, waves W+NDW..W+NDW+NPW-1: fill a ring of NST LDS stages (chunk j in
 //     stage j % NST) with the chunks' K and V tiles by LDS DMA, NST - 1
 //     chunks ahead of the consumers; each producer issues its share of every
 //     chunk's DMA instructions.
@@ -306,22 +311,23 @@ __device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
 
 template <int D, int W, int FMT, int NST, int NPW, bool STATE>
-__global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_kernel(const SplitArgs a) {
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
   constexpr int MD = D / 16;  // O^T row blocks over d
   constexpr int KROW = G::KROW, PIECES = G::PIECES, RPI = G::RPI, NDMA = G::NDMA;
   constexpr int kTileB = G::kTileB, kStageB = G::kStageB, kVm = G::kVm;
   static_assert(NST >= 2, "a ring of at least two stages");
+  constexpr int NDW = FMT == 1 ? 1 : 0;  // decoder waves
   constexpr int U = 2 * NDMA / NPW;           // DMA instructions per chunk and producer
   constexpr int kVmP = U + (FMT == 1 ? 1 : 0);  // the same, with the quantised scales
   static_assert(FMT == 0 || NPW == 1, "the scale DMA belongs to a single producer");
   static_assert((2 * NDMA) % NPW == 0, "producers share a chunk's DMA evenly");
   static_assert((NST - 2) * kVmP <= 63, "vmcnt counts at most 63 loads");
   static_assert(FMT == 0 || NST >= 3, "the quantised pipeline stages one chunk ahead of the decode");
-  // Quantised formats: the consumers decode every chunk once, together, into
-  // bf16 tiles (two buffers, [K | V]); each then reads bf16 operands as for
-  // bf16 caches instead of converting the whole chunk in every wave.
+  // Quantised formats: the decoder waves convert every chunk once into bf16
+  // tiles (two buffers, [K | V]); each consumer then reads bf16 operands as
+  // for bf16 caches instead of converting the whole chunk itself.
   constexpr int kDecRow = 2 * D;                         // bf16 bytes per key row
   constexpr int kDecTile = kChunk * kDecRow;             // one decoded K or V tile
   constexpr int kDecB = FMT == 1 ? 2 * 2 * kDecTile : 0;  // two buffers of K and V
@@ -384,7 +390,84 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
     nch = cq + (split < cr ? 1 : 0);
   };
 
-  if (wave >= W) {
+  // Decoded tiles (quantised formats): buffer b holds K at dec + b*2*kDecTile
+  // and V after it.  V is bf16 in the bf16 layout (piece P of a row at
+  // 16*(P ^ fv0(row)), fv0 = 2*(row % 8)); K keeps each staged 16-code piece
+  // in its staged slot q, expanded to two bf16 halves at 16-byte positions
+  // (2q + half) ^ (row % 16), so that the 16 lanes reading one operand hit
+  // 16 different positions.
+  uint8_t *const dec = smem + NST * kStageB;
+  auto fv0 = [](int row) { return (2 * row) & 14; };
+  // Decoder d converts its share of chunk n: of the 16 * kChunk units of 16
+  // codes (V first, then K), the blocks of 64 consecutive units with index
+  // = d (mod NDW), unit u on lane u % 64, so each load and store is one
+  // kind; all of a lane's code loads are issued before it converts.
+  constexpr int kUnits = 16 * kChunk;
+  constexpr int NU = kUnits / 64 / (NDW > 0 ? NDW : 1);
+  auto decode = [&](int32_t n, int d) {
+    if constexpr (FMT == 1) {
+      const uint8_t *qs = smem + (n % NST) * kStageB;
+      uint8_t *dk = dec + (n & 1) * 2 * kDecTile;
+      uint8_t *dv = dk + kDecTile;
+      u32x4 codes[NU];
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        const int u = lane + 64 * (NDW * i + d);
+        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
+        codes[i] = *(const u32x4 *)(qs + (u < 8 * kChunk ? kTileB : 0) + row * KROW + 16 * pc);
+      }
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        const int u = lane + 64 * (NDW * i + d);
+        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
+        const u32x4 c = codes[i];
+        if (64 * (NDW * i) < 8 * kChunk) {  // INT8 values: exact in bf16 (|code| <= 127)
+          u32x4 h[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = c[e];
+            const float f0 = (float)((int32_t)(w << 24) >> 24), f1 = (float)((int32_t)(w << 16) >> 24);
+            const float f2 = (float)((int32_t)(w << 8) >> 24), f3 = (float)((int32_t)w >> 24);
+            h[e >> 1][2 * (e & 1)] = pack_bf16x2(f0, f1);
+            h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
+          }
+          uint8_t *dst = dv + row * kDecRow + 16 * ((2 * pc) ^ fv0(row));
+          *(u32x4 *)dst = h[0];
+          *(u32x4 *)(dst + 16) = h[1];
+        } else {  // E4M3 keys: exact in bf16
+          u32x4 h[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e >> 1][2 * (e & 1)] = e4m3x2_to_bf16x2<false>(c[e]);
+            h[e >> 1][2 * (e & 1) + 1] = e4m3x2_to_bf16x2<true>(c[e]);
+          }
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            *(u32x4 *)(dk + row * kDecRow + 16 * ((2 * pc + half) ^ (row & 15))) = h[half];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tiles are whole at the next barrier
+    }
+  };
+
+  if constexpr (NDW > 0) {
+    if (wave >= W && wave < W + NDW) {
+      // ================= decoders =================
+      // Barrier n (in the loop) publishes decoded chunk n and staged chunk
+      // n + 1 and frees decode buffer (n + 1) % 2 (last read in step n - 1),
+      // which the decoders fill right after.
+      chunk_range();
+      wg_barrier();  // chunk 0 is staged
+      if (nch > 0) decode(0, wave - W);
+      for (int32_t n = 0; n < nch; ++n) {
+        wg_barrier();
+        if (n + 1 < nch) decode(n + 1, wave - W);
+      }
+      return;
+    }
+  }
+
+  if (wave >= W + NDW) {
     // ================= producers =================
     chunk_range();
     const uint8_t *kbase = kptr + (int64_t)kvh * head_stride;
@@ -458,7 +541,7 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
       for (int j = 0; j < NST - 1; ++j)
         if (j < nch) issue(j, j);
       if constexpr (FMT == 1) {
-        // the consumers decode chunk n + 1 right after barrier n, so chunk 0
+        // the decoders convert chunk n + 1 right after barrier n, so chunk 0
         // must have landed before an extra first barrier, and chunk n + 1
         // before barrier n
         const int32_t ahead = nch - 1;
@@ -486,7 +569,7 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
     if constexpr (NPW == 1) {
       produce(std::integral_constant<int, 0>{});
     } else {
-      if (wave == W) produce(std::integral_constant<int, 0>{});
+      if (wave == W + NDW) produce(std::integral_constant<int, 0>{});
       else produce(std::integral_constant<int, 1>{});
     }
     return;
@@ -601,72 +684,6 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
   // Swizzles of the staged tiles (must match the producer's).
   auto fk = [](int row) { return row & (PIECES - 1); };
   auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
-
-  // Decoded tiles (quantised formats): buffer b holds K at dec + b*2*kDecTile
-  // and V after it.  V is bf16 in the bf16 layout (piece P of a row at
-  // 16*(P ^ fv0(row)), fv0 = 2*(row % 8)); K keeps each staged 16-code piece
-  // in its staged slot q, expanded to two bf16 halves at 16-byte positions
-  // (2q + half) ^ (row % 16), so that the 16 lanes reading one operand hit
-  // 16 different positions.
-  uint8_t *const dec = smem + NST * kStageB;
-  auto fv0 = [](int row) { return (2 * row) & 14; };
-  // A consumer lane's decode units: 16 * kChunk units of 16 codes per chunk
-  // (V first, then K), unit u on lane u % (64 * W) -- 64 consecutive units
-  // per wave, so every wave converts one kind at a time.  The codes are read
-  // before the step of the previous chunk and converted after it, so their
-  // LDS latency hides behind the step.
-  constexpr int kUnits = 16 * kChunk;
-  constexpr int NU = (kUnits + 64 * W - 1) / (64 * W);
-  u32x4 codes[FMT == 1 ? NU : 1];
-  auto decode_load = [&](int32_t n) {
-    if constexpr (FMT == 1) {
-      const uint8_t *qs = smem + (n % NST) * kStageB;
-#pragma unroll
-      for (int i = 0; i < NU; ++i) {
-        const int u = 64 * wave + lane + 64 * W * i;
-        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
-        if (u < kUnits) codes[i] = *(const u32x4 *)(qs + (u < 8 * kChunk ? kTileB : 0) + row * KROW + 16 * pc);
-      }
-    }
-  };
-  auto decode_store = [&](int32_t n) {
-    if constexpr (FMT == 1) {
-      uint8_t *dk = dec + (n & 1) * 2 * kDecTile;
-      uint8_t *dv = dk + kDecTile;
-#pragma unroll
-      for (int i = 0; i < NU; ++i) {
-        const int u = 64 * wave + lane + 64 * W * i;
-        if (u >= kUnits) continue;
-        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
-        const u32x4 c = codes[i];
-        if (u < 8 * kChunk) {  // INT8 values: exact in bf16 (|code| <= 127)
-          u32x4 h[2];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = c[e];
-            const float f0 = (float)((int32_t)(w << 24) >> 24), f1 = (float)((int32_t)(w << 16) >> 24);
-            const float f2 = (float)((int32_t)(w << 8) >> 24), f3 = (float)((int32_t)w >> 24);
-            h[e >> 1][2 * (e & 1)] = pack_bf16x2(f0, f1);
-            h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
-          }
-          uint8_t *dst = dv + row * kDecRow + 16 * ((2 * pc) ^ fv0(row));
-          *(u32x4 *)dst = h[0];
-          *(u32x4 *)(dst + 16) = h[1];
-        } else {  // E4M3 keys: exact in bf16
-          u32x4 h[2];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            h[e >> 1][2 * (e & 1)] = e4m3x2_to_bf16x2<false>(c[e]);
-            h[e >> 1][2 * (e & 1) + 1] = e4m3x2_to_bf16x2<true>(c[e]);
-          }
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-            *(u32x4 *)(dk + row * kDecRow + 16 * ((2 * pc + half) ^ (row & 15))) = h[half];
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is whole at the next barrier
-    }
-  };
 
   auto step = [&](int32_t n, const uint8_t *kt) {
     const uint8_t *vt = kt + kTileB;
@@ -802,20 +819,11 @@ __global__ __launch_bounds__(64 * (W + NPW)) void split_kernel(const SplitArgs a
     for (int md = 0; md < MD; ++md) o[md] = mfma16(vop[md], pb, o[md]);
   };
 
-  if constexpr (FMT == 1) {
-    wg_barrier();  // chunk 0 is staged
-    if (nch > 0) {
-      decode_load(0);
-      decode_store(0);
-    }
-  }
+  if constexpr (FMT == 1) wg_barrier();  // chunk 0 is staged (the decoders convert it)
   int st = 0;  // stage of chunk n
   for (int32_t n = 0; n < nch; ++n) {
     wg_barrier();  // chunk n is in LDS (decoded); every consumer has left chunk n - 1
-    const bool next = n + 1 < nch;
-    if (next) decode_load(n + 1);  // quantised formats: all consumers, active or not
     if (active) step(n, smem + st * kStageB);
-    if (next) decode_store(n + 1);
     st = st + 1 == NST ? 0 : st + 1;
   }
 
@@ -1163,7 +1171,8 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
   dim3 grid(a.splits, a.kv_heads);
-  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE>), grid, dim3(64 * (W + NPW)), 0, stream, a);
+  constexpr int NDW = FMT == 1 ? 1 : 0;
+  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE>), grid, dim3(64 * (W + NDW + NPW)), 0, stream, a);
   return hipGetLastError();
 }
 

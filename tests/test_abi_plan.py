@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"verify_attn_plan", "verify_attn_split", "verify_attn_combine", "swa_ring_write", "verify_kv_write",
                           "verify_attn_split_state", "verify_attn_combine_state",
-                          "va_sample", "va_accept", "va_sample_accept", "va_sample_workspace_bytes",
+                          "va_sample", "va_accept", "va_sample_accept", "va_sample_workspace_bytes", "va_read_probe",
                           "verify_attn_plan_query", "verify_attn_plan_split_range", "va_status_string"}
     for n in names:
         assert hasattr(lib, n), n

@@ -248,12 +248,14 @@ def _q_rounding_bound(q_rot, keys_dec, scale, vis_hi):
     return out
 
 
-def test_config5_quantized_tree():
+@pytest.mark.parametrize("P,live", [(65536, 16), (4000, 9), (3001, 11)])
+def test_config5_quantized_tree(P, live):
     """Config 4's tree and heads at 64K: keys E4M3 after the 128-point WHT,
-    values INT8 with one FP32 scale per (token, head)."""
-    P = 65536
-    rows, live, Hq, Hkv, D = 16, 16, 24, 4, 128
-    g = synth.gen(5000)
+    values INT8 with one FP32 scale per (token, head).  The shorter cases
+    leave some 16-row blocks of the 96 matrix rows without a live row (54
+    and 66 live matrix rows)."""
+    rows, Hq, Hkv, D = 16, 24, 4, 128
+    g = synth.gen(5000 + (P % 997) + live)
     parent = synth.random_tree(rows, g)
     cap = P + rows + 64
     hi = P + live
@@ -277,7 +279,7 @@ def test_config5_quantized_tree():
     p = Problem("tree", rows, live, prefix_len=P, parent=parent)
     ro, rl = oattn.verify_attn_ref(p, q_rot, oattn.Cache(k_dec, v_dec), plan.problem.scale)
     bound = TOL_LSE + _q_rounding_bound(q_rot, k_dec, plan.problem.scale, hi)
-    check(out, lse, ro, rl, live, f"config5 S={plan.splits}", lse_tol=bound)
+    check(out, lse, ro, rl, live, f"config5 P={P} live={live} S={plan.splits}", lse_tol=bound)
 
 
 @pytest.mark.parametrize("call", [0, 1, 2])
@@ -553,6 +555,9 @@ def test_single_visible_key_is_exact():
     (8, 8, 8, 1, 128, 2500, 0),     # 64 matrix rows: two row groups of two blocks
     (16, 13, 5, 1, 64, 1500, 0),    # 80 matrix rows: third block of the second group empty
     (16, 16, 6, 1, 128, 63, 0),     # 96 matrix rows, context shorter than a 64-key tile
+    (16, 11, 6, 1, 128, 2000, 0),   # 66 live of 96: the last wave's second block has no live row
+    (16, 7, 6, 1, 128, 5000, 0),    # 42 live of 96: the middle wave half live, the last idle
+    (16, 5, 6, 1, 64, 3000, 0),     # 30 live of 96 at D 64: one live wave
     (1, 1, 6, 1, 128, 4095, 0),     # a single row
     (8, 7, 6, 1, 128, 100000, 3),   # few long splits
 ])
