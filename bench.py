@@ -377,19 +377,27 @@ def bench_sampler(torch, va, synth, dev, reps=100, replicas=4, cpu_seconds=5.0, 
     plus acceptance of their 7 drafts, over the full 160,000-token vocabulary
     and over a 20,000-token share, with FP32 logits resident in HBM
     (`replicas` copies read in turn).  The draft's lists come from va_sample
-    on perturbed logits (untimed).  Timed from graphs of back-to-back calls;
+    on perturbed logits (untimed).  A third case takes the target's own
+    lists and samples as the drafts (q = p, so every draft is accepted: the
+    acceptance walks all rows).  Timed from graphs of back-to-back calls;
     the full-size outputs of replica 0 are checked against the oracle.
     Prints one JSON line (not the sweep's)."""
     import numpy as np
     from oracle import sampling as osamp
     n, k, top_p, seed, pos0 = 8, 20, 0.95, 20260, 123456
     out = []
-    for name, V in (("full vocabulary", 160000), ("one GPU's share of eight", 20000)):
+    for name, V, all_accepted in (("full vocabulary", 160000, False), ("one GPU's share of eight", 20000, False),
+                                  ("full vocabulary, every draft accepted", 160000, True)):
         g = synth.gen(9300 + V)
         zs = [synth.logits_f32(n, V, g, "lm") for _ in range(replicas)]
+        if all_accepted:
+            zs = [zs[0].clone() for _ in range(replicas)]
         zd = zs[0][: n - 1] + 0.5 * torch.randn((n - 1, V), generator=g)
         zg = [z.to(dev) for z in zs]
-        dr = va.va_sample(zd.to(dev), seed=seed, first_position=pos0, purpose=3)
+        if all_accepted:
+            dr = va.va_sample(zg[0], seed=seed, first_position=pos0)
+        else:
+            dr = va.va_sample(zd.to(dev), seed=seed, first_position=pos0, purpose=3)
         q = (dr["ids"][: n - 1].contiguous(), dr["probs"][: n - 1].contiguous(), dr["kept"][: n - 1].contiguous(),
              dr["tokens"][: n - 1].contiguous())
         p = va.sample_params(n, V, top_k=k, top_p=top_p, seed=seed, first_position=pos0)
@@ -446,6 +454,8 @@ def bench_sampler(torch, va, synth, dev, reps=100, replicas=4, cpu_seconds=5.0, 
                 "logit_bytes": nbytes, "logit_gb_s": round(nbytes / (times["sample_accept"] * 1e-6) / 1e9, 1),
                 "pct_hbm_peak": round(100 * nbytes / (times["sample_accept"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
                 "parity": {"pass": bool(ok), "accepted": int(acc.item())}}
+        if all_accepted and int(acc.item()) != n - 1:
+            raise SystemExit("the every-draft-accepted case did not accept every draft")
         if cpu:
             passes, t_cpu = 1, t_oracle
             while t_cpu < cpu_seconds and passes < 50:

@@ -420,47 +420,85 @@ struct AcceptArgs {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-__device__ void accept_wave(const AcceptArgs &a) {
+// Every load is issued before the first decision: lane i reads row i's kept
+// counts, draft and own sample, and each draft row's two lists (the kept
+// counts mask them afterwards), so the rows cost one memory round trip
+// together instead of two each.  Indices are clamped into the arrays (rows
+// past the last draft row reread it) rather than predicated or branched on,
+// and nothing is computed from a loaded value until every load is issued.
+// R (7 or 15) bounds the draft rows, so eight rows load eight lists.
+template <int R>
+__device__ void accept_rows(const AcceptArgs &a) {
   const int lane = lane_id();
   const int n = a.n;
+  const int lr = lane < n ? lane : n - 1, ld = lane < n - 1 ? lane : n - 2;
+  const int lp = lane < a.p_stride ? lane : 0, lq = lane < a.q_stride ? lane : 0;
+  const int pk_raw = load_agent(a.p_kept + lr);
+  const int tok_l = load_agent(a.p_tokens + lr);
+  const int qk_raw = a.q_kept[ld];
+  const int d_l = a.drafts[ld];
+  int pid[R], qid[R];
+  float pp[R], qp[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int row = i < n - 1 ? i : n - 2;
+    pid[i] = load_agent(a.p_ids + (int64_t)row * a.p_stride + lp);
+    pp[i] = load_agent(a.p_probs + (int64_t)row * a.p_stride + lp);
+    qid[i] = a.q_ids[(int64_t)row * a.q_stride + lq];
+    qp[i] = a.q_probs[(int64_t)row * a.q_stride + lq];
+  }
+  const int pk_l = lane < n ? clampi(pk_raw, 0, a.p_stride) : 0;
+  const int qk_l = lane < n - 1 ? clampi(qk_raw, 0, a.q_stride) : 0;
   int acc = n - 1, tok = -1;
-  for (int i = 0; i < n - 1; ++i) {
-    const int d = a.drafts[i];
-    const int pk = clampi(load_agent(a.p_kept + i), 0, a.p_stride), qk = clampi(a.q_kept[i], 0, a.q_stride);
-    const bool pin = lane < pk, qin = lane < qk;
-    const int pid = pin ? load_agent(a.p_ids + (int64_t)i * a.p_stride + lane) : -1;
-    const float pp = pin ? load_agent(a.p_probs + (int64_t)i * a.p_stride + lane) : 0.f;
-    const int qid = qin ? a.q_ids[(int64_t)i * a.q_stride + lane] : -1;
-    const float qp = qin ? a.q_probs[(int64_t)i * a.q_stride + lane] : 0.f;
-    const u64 ph = __ballot(pin && pid == d), qh = __ballot(qin && qid == d);
-    const float pd = ph ? readlane_f(pp, __builtin_ctzll(ph)) : 0.f;
-    const float qd = qh ? readlane_f(qp, __builtin_ctzll(qh)) : 0.f;
+  bool done = false;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (done || i >= n - 1) break;
+    const int d = __builtin_amdgcn_readlane(d_l, i);
+    const int pk = __builtin_amdgcn_readlane(pk_l, i), qk = __builtin_amdgcn_readlane(qk_l, i);
+    const bool pin = lane < pk, qin = lane < qk;  // kept counts are at most the strides
+    const int pidv = pin ? pid[i] : -1, qidv = qin ? qid[i] : -1;
+    const float ppv = pin ? pp[i] : 0.f, qpv = qin ? qp[i] : 0.f;
+    const u64 ph = __ballot(pin && pidv == d), qh = __ballot(qin && qidv == d);
+    const float pd = ph ? readlane_f(ppv, __builtin_ctzll(ph)) : 0.f;
+    const float qd = qh ? readlane_f(qpv, __builtin_ctzll(qh)) : 0.f;
     const float u = philox_uniform(a.seed, (uint64_t)(a.pos0 + i), VA_PURPOSE_ACCEPT);
     if (u * qd < pd) continue;
     // rejected at row i: replacement from max(0, p - q) over the row's kept tokens
     float qt = 0.f;
     bool found = false;
     for (int j = 0; j < qk; ++j) {
-      const int id2 = __builtin_amdgcn_readlane(qid, j);
-      const float pr2 = readlane_f(qp, j);
-      if (!found && pid == id2) qt = pr2, found = true;
+      const int id2 = __builtin_amdgcn_readlane(qidv, j);
+      const float pr2 = readlane_f(qpv, j);
+      if (!found && pidv == id2) qt = pr2, found = true;
     }
-    const float r = pin ? fmaxf(0.f, pp - qt) : 0.f;
-    const float R = wave_sum(r);
-    if (R > 0.f) {
+    const float r = pin ? fmaxf(0.f, ppv - qt) : 0.f;
+    const float Rsum = wave_sum(r);
+    if (Rsum > 0.f) {
       const float u2 = philox_uniform(a.seed, (uint64_t)(a.pos0 + i), VA_PURPOSE_RESIDUAL);
       const float incl = wave_inclusive_scan(r);
-      const u64 h = __ballot(pin && u2 * R < incl);
-      tok = __builtin_amdgcn_readlane(pid, h ? __builtin_ctzll(h) : pk - 1);
+      const u64 h = __ballot(pin && u2 * Rsum < incl);
+      tok = __builtin_amdgcn_readlane(pidv, h ? __builtin_ctzll(h) : pk - 1);
     } else {
-      tok = load_agent(a.p_tokens + i);
+      tok = __builtin_amdgcn_readlane(tok_l, i);
     }
     acc = i;
-    break;
+    done = true;
   }
-  if (acc == n - 1) tok = load_agent(a.p_tokens + (n - 1));
+  if (acc == n - 1) tok = __builtin_amdgcn_readlane(tok_l, n - 1);
   for (int i = lane; i < n; i += 64) a.out_tokens[i] = i < acc ? a.drafts[i] : (i == acc ? tok : -1);
   if (lane == 0) *a.accepted = acc;
+}
+
+__device__ void accept_wave(const AcceptArgs &a) {
+  if (a.n == 1) {  // no draft: the row's own sample
+    const int tok = load_agent(a.p_tokens);
+    if (lane_id() == 0) *a.out_tokens = tok, *a.accepted = 0;
+  } else if (a.n <= 8) {
+    accept_rows<7>(a);
+  } else {
+    accept_rows<VA_SAMPLE_MAX_ROWS - 1>(a);
+  }
 }
 
 __global__ __launch_bounds__(64) void accept_kernel(const AcceptArgs a) { accept_wave(a); }
