@@ -509,8 +509,28 @@ __global__ __launch_bounds__(64) void accept_kernel(const AcceptArgs a) { accept
 // wait for them before a device-scope counter increment; the workgroup that
 // sees the final count reads with device-scope loads and resets the counter
 // for the next call.
+// Naming a value in an empty asm statement forces it into a scalar register
+// there: applied to every kernel argument at entry, all argument loads issue
+// together in one round trip, not one per first use in a later phase.
+__device__ __forceinline__ void pin(int32_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(uint32_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(int64_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(uint64_t x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
+__device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
+
 template <bool ACCEPT>
-__global__ __launch_bounds__(kTileThreads) void sample_kernel(const SampleArgs a, const AcceptArgs acc) {
+__global__ __launch_bounds__(kTileThreads) void sample_kernel(const SampleArgs ka, const AcceptArgs kacc) {
+  SampleArgs a = ka;
+  pin(a.logits), pin(a.lists), pin(a.row_count), pin(a.done), pin(a.row_stride), pin(a.vocab), pin(a.k);
+  pin(a.tiles), pin(a.rows), pin(a.vec), pin(a.ids), pin(a.probs), pin(a.kept), pin(a.tokens);
+  pin(a.inv_temp), pin(a.top_p), pin(a.seed), pin(a.pos0), pin(a.purpose);
+  AcceptArgs acc = kacc;
+  if constexpr (ACCEPT) {
+    pin(acc.p_ids), pin(acc.p_probs), pin(acc.p_kept), pin(acc.p_tokens), pin(acc.q_ids), pin(acc.q_probs);
+    pin(acc.q_kept), pin(acc.drafts), pin(acc.accepted), pin(acc.out_tokens), pin(acc.seed), pin(acc.pos0);
+    pin(acc.p_stride), pin(acc.q_stride), pin(acc.n);
+  }
   __shared__ SampleShared sh;
   const int tile = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
   u64 x[kPerThread];
