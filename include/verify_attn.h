@@ -123,6 +123,12 @@ typedef struct {
 
 /* Validate *p and build *plan.  Writes the workspace size the split needs to
  * *workspace_bytes (may be NULL).  Pure host code: needs no GPU.
+ * With splits = 0 the plan chooses: C, the number of 32-key granules (one
+ * granule per split), or, where B_p * Hkv >= 4 * B_g, round(sqrt(C * 47.61 *
+ * B_g / (B_p * Hkv))) rounded to the nearest multiple of 8 from 8 up (B_g
+ * the KV bytes of one granule, 32*4*D or 32*(2*D+4) quantised; B_p =
+ * rows*G*(D+2)*4 partial bytes per split and KV head); then at most
+ * num_cus / Hkv (a multiple of 8 from 8 up) and at most C, at least 1.
  * Errors: VA_ERR_INVALID (NULL pointers, counts out of range, parent[i] >= i
  * or < -1, C % 64 != 0, C < W + rows - 1 so that the rows' own writes would
  * evict history an earlier row needs, scale not finite and > 0, positions

@@ -15,23 +15,47 @@ static inline int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
 static inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // Splits: each workgroup streams a contiguous run of 32-key granules, one
-// after another, so the shortest split kernel gives every workgroup as few
-// granules as possible: one per split, up to one workgroup per CU over all
-// KV heads (more than one per CU measured slower: the extra partials cost
-// more than the extra overlap gains).  A capped count of 8 or more is kept a
-// multiple of 8, one share per XCD.
-static const int64_t kMinChunksPerSplit = 1;
+// after another, and writes its rows' partials (m, l, O: rows*G*(D+2)*4
+// bytes per KV head), which the combine reads back.  By default each split
+// takes one granule, up to one workgroup per CU over all KV heads (more than
+// one per CU measured slower), the count kept a multiple of 8 (one share per
+// XCD) from 8 up.  Where a split's partials outweigh its granule four times
+// or more (many matrix rows over several KV heads: the 96-row tree writes
+// 50 KB per split and head against 16 KB read per granule), fewer splits
+// pay: timed as split + combine pairs on MI355X, the best count there is
+// near S = 6.9 * sqrt(C * B_granule / (B_partial * Hkv)) (16 splits for the
+// tree at 2K keys, 32 at 8K, 64 at 32K), which the plan then uses.  For the
+// 48-row shapes (ratio ~1.5) the same fit was no better overall (faster
+// pairs at 4K-32K, slower at 1K and for the window ring) and is not used.
 static const int64_t kWorkgroupsPerCU = 1;
 
-static int32_t choose_splits(int64_t chunks, int32_t kv_heads, int32_t num_cus) {
+// round(sqrt(chunks * k_num / k_den)) exactly: the largest s with
+// (2s - 1)^2 * k_den <= 4 * chunks * k_num (a double estimate, then an
+// integer check either way)
+static int64_t round_sqrt_ratio(int64_t chunks, int64_t k_num, int64_t k_den) {
+  const int64_t rhs = 4 * chunks * k_num;
+  int64_t s = (int64_t)(sqrt((double)chunks * (double)k_num / (double)k_den) + 0.5);
+  if (s > 65536) s = 65536;  // far above any cap; keeps the products below 2^63
+  if (s > 0 && (2 * s - 1) * (2 * s - 1) * k_den > rhs) --s;
+  if ((2 * s + 1) * (2 * s + 1) * k_den <= rhs) ++s;
+  return s;
+}
+
+static int32_t choose_splits(int64_t chunks, int32_t kv_heads, int32_t num_cus, int64_t granule_bytes,
+                             int64_t partial_bytes) {
   if (chunks <= 0) return 1;
   if (num_cus <= 0) num_cus = 256;
   int64_t cap = (kWorkgroupsPerCU * num_cus) / kv_heads;
   if (cap < 1) cap = 1;
-  const int64_t want = (chunks + kMinChunksPerSplit - 1) / kMinChunksPerSplit;
-  if (want <= cap) return (int32_t)want;  // every split gets its minimum
-  int64_t s = cap;
-  if (s >= 8) s = (s / 8) * 8;  // keep whole rounds over the 8 XCDs
+  if (cap >= 8) cap = (cap / 8) * 8;  // whole rounds over the 8 XCDs
+  int64_t s = chunks;                 // one granule per split
+  if (partial_bytes * kv_heads >= 4 * granule_bytes) {
+    s = round_sqrt_ratio(chunks, 4761 * granule_bytes, 100 * partial_bytes * kv_heads);  // 6.9^2 = 47.61
+    if (s >= 8) s = ((s + 4) / 8) * 8;
+  }
+  if (s > cap) s = cap;
+  if (s > chunks) s = chunks;
+  if (s < 1) s = 1;
   return (int32_t)s;
 }
 
@@ -145,7 +169,11 @@ extern "C" va_status verify_attn_plan(const va_problem *p, va_plan *plan, size_t
     d.full_hi = fhi;
   }
 
-  d.splits = p->splits > 0 ? p->splits : choose_splits(d.chunks, d.kv_heads, p->num_cus);
+  const int64_t granule_bytes =
+      (int64_t)VA_SPLIT_KEYS * (p->kv_fmt == VA_KV_K_E4M3_WHT_V_I8 ? 2 * d.head_dim + 4 : 4 * d.head_dim);
+  const int64_t partial_bytes = (int64_t)d.matrix_rows * (d.head_dim + 2) * 4;
+  d.splits = p->splits > 0 ? p->splits
+                           : choose_splits(d.chunks, d.kv_heads, p->num_cus, granule_bytes, partial_bytes);
 
   const uint64_t units = (uint64_t)d.splits * d.kv_heads * d.matrix_rows;
   d.ml_bytes = ((units * 2 * sizeof(float)) + 255) / 256 * 256;

@@ -190,14 +190,29 @@ def test_workspace_size_formula():
 
 
 def test_chosen_splits_are_sane():
-    for P in (1024, 4096, 16384, 32768, 65536, 131072, 196608):
+    """The plan's split count: one 32-key granule per split, or, where a
+    split's partials outweigh a granule four times over, about
+    6.9 * sqrt(C * B_granule / (B_partial * Hkv)) rounded to a multiple of 8;
+    at most one workgroup per CU over the KV heads (a multiple of 8) and at
+    most one split per granule."""
+    want = {1024: 33, 4096: 129, 16384: 256, 32768: 256, 65536: 256, 131072: 256, 196608: 256}
+    for P, S_want in want.items():
         plan = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, first_pos=P,
                        kv_capacity=262144, num_cus=256)
         S, C = plan.splits, plan.info["chunks"]
-        assert 1 <= S <= C and S <= 4096
-        # one 32-key granule per split while that fits one workgroup per CU;
-        # else a multiple of 8 workgroups no larger than the CU count
-        if C <= 256:
-            assert S == C
-        else:
-            assert S <= 256 and S % 8 == 0
+        assert S == S_want, (P, S)
+        assert 1 <= S <= min(C, 256) and (S == C or S % 8 == 0)
+    for P, S_want in {2048: 16, 8192: 32, 32768: 64}.items():
+        plan = va.Plan(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=P,
+                       parent=[-1] * 16, kv_capacity=P + 100, num_cus=256)
+        assert plan.splits == S_want, (P, plan.splits)
+    plan = va.Plan(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=65536,
+                   parent=[-1] * 16, kv_capacity=65536 + 100, kv_fmt="e4m3_wht_i8", num_cus=256)
+    assert plan.splits == 64
+    # a few granules: one split each; the CU cap over KV heads
+    plan = va.Plan(rows=1, live_rows=1, q_heads=1, kv_heads=1, head_dim=64, first_pos=40, kv_capacity=64,
+                   num_cus=256)
+    assert plan.splits == plan.info["chunks"] == 2
+    plan = va.Plan(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=200000,
+                   parent=[-1] * 16, kv_capacity=200100, num_cus=40)
+    assert plan.splits == 8
