@@ -3,14 +3,19 @@
 // Kernels:
 //   split_kernel    one workgroup per (split, KV head); one wave64 per 16
 //                   query matrix rows walks the split's 32-key chunks, which
-//                   a producer wave streams into a ring of LDS stages by LDS
-//                   DMA; QK^T and PV run on MFMA 16x16x32 bf16 with FP32
-//                   accumulation; each wave writes its rows' partials
-//                   (m, l, O) directly.
-//   combine_kernel  one workgroup per (row, query head, 64-wide slice of D):
+//                   one or two producer waves stream into a ring of LDS
+//                   stages by LDS DMA (for quantised caches a decoder wave
+//                   converts each staged chunk to bf16 tiles); QK^T and PV
+//                   run on MFMA 16x16x32 bf16 with FP32 accumulation; each
+//                   wave writes its rows' partials (m, l, O) directly.
+//   combine_kernel  one workgroup per (row, query head, 32-wide slice of D):
 //                   LSE merge of the partials plus the sink, with the partial
-//                   loads issued together into four independent FP32 chains.
+//                   loads issued together into four independent FP32 chains
+//                   per thread.
 //   ring_write_kernel  copies the verification rows' K/V into the window ring.
+//   kv_write_kernel    writes the rows' K/V into a linear cache or the ring,
+//                      bf16 or encoded (rotated E4M3 keys, INT8 values with a
+//                      per-token scale).
 //
 // The method is the one on the IQuestRT report's section "Read only the KV
 // tiles needed by the current positions" (eight rows x six heads packed as
@@ -203,16 +208,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   r[0] = (__bf16)lo;
   r[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
-}
-
-// E4M3FN pair -> two floats (exact), via the gfx950 OCP converter.
-__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float out[4]) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  out[0] = a[0];
-  out[1] = a[1];
-  out[2] = b[0];
-  out[3] = b[1];
 }
 
 // Two E4M3FN codes (bytes 0-1, or 2-3 with hi) -> two bf16, exact (the gfx950
