@@ -8,11 +8,13 @@ keys, contexts 1K, 4K, 16K, 32K, 64K, 128K and 192K; split count chosen by
 the plan.  One step = one verify call (split + combine) at each of the seven
 contexts.
 
-Cold-cache rule: every context of every replica has its own 256K-capacity
-cache (6 replicas x 7 contexts); step i reads replica i % 6, so about 1.4 GB
-of distinct KV is streamed between two reads of the same bytes, more than
-the 256 MB Infinity Cache.  Capacity beyond each read extent is NaN: reading
-it would poison the output, which the full-size parity check below catches.
+Cold-cache rule: for whole steps every context of every replica has its own
+256K-capacity cache (6 replicas x 7 contexts); step i reads replica i % 6,
+so about 1.4 GB of distinct KV is streamed between two reads of the same
+bytes, more than the 256 MB Infinity Cache.  Capacity beyond each read
+extent is NaN: reading it would poison the output, which the full-size
+parity check below catches.  Per-kernel times rotate, per context, over a
+pool of at least 1 GiB of replicas of that context's read extent.
 
 Timing:
   * value / ms_per_step: HIP events (torch's stream, where the library
@@ -49,6 +51,23 @@ UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS
 COPY_PROBE_MIB = 1024
 KERNEL_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "verify_attn.hip")
 SAMPLE_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "sample.hip")
+
+
+POOL_BYTES = 1 << 30  # every per-kernel timing rotates over at least this many distinct bytes
+
+
+def cold_pool(torch, synth, dev, nbytes, seed, tail=0):
+    """A flat uint8 pool of n replicas of nbytes each (n >= 6, n * nbytes >=
+    1 GiB) plus `tail` bytes, filled with N(0,1) bf16 drawn on the GPU in
+    256 MiB pieces.  Returns (pool, n)."""
+    n = max(REPLICAS, -(-POOL_BYTES // nbytes))
+    pool = torch.empty(n * nbytes + tail, dtype=torch.uint8, device=dev)
+    flat = pool.view(torch.bfloat16)
+    piece = 1 << 27
+    for off in range(0, flat.numel(), piece):
+        m = min(piece, flat.numel() - off)
+        flat[off:off + m] = synth.normal_bf16_device((m,), seed + off // piece, dev)
+    return pool, n
 
 
 def kv_bytes(hi):
@@ -152,6 +171,16 @@ def summarize_profiles(d):
     out.append("")
     out.append("bench line of the same command (events; the trace itself slows the launches): "
                f"roofline avg_launch_us {bl['roofline']['avg_launch_us']}, value {bl['value']} GB/s")
+    sw = [x for (kind, n, wgs), v in dur.items() if static_split(n) for x in v]
+    line = (f"roofline kernel (sweep split launches, static plan, D 128, 3 consumers): trace average "
+            f"{sum(sw) / len(sw):.2f} us over {len(sw)} launches")
+    if os.path.exists(os.path.join(d, "bench.log")):
+        pl = bench_line("bench.log")
+        if pl["kernel_hash"] == kernel_hash():
+            line += (f"; the same bench without the profiler ({py} --steps 10 --warmup 3): avg_launch_us "
+                     f"{pl['roofline']['avg_launch_us']}, value {pl['value']} GB/s")
+    out.append("")
+    out.append(line)
     out.append("")
     out.append("## HBM traffic of split_kernel (rocprofv3 --pmc, one counter per run)")
     out.append("")
@@ -472,11 +501,11 @@ def bench_sampler(torch, va, synth, dev, reps=100, replicas=4, cpu_seconds=5.0, 
                       "kernel_hash": sample_hash()}), flush=True)
 
 
-def bench_other_configs(torch, va, synth, dev, reps=20, replicas=4):
+def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
     """The other configurations of the verification call, each timed as one
     call (ring write where the rows' K/V go to the ring first, split,
-    combine) from a graph of `reps` back-to-back calls over `replicas` cold
-    caches:
+    combine) from a graph of `reps` back-to-back calls over cold caches (at
+    least `replicas` and at least 1 GiB of them, read in turn):
       window  Hkv 1, Hq 6, D 64, 8 rows (5 live), window 4,096 over a
               4,160-slot ring, rows at 5,120 / 51,200 / 194,560, sink on;
       tree    Hkv 4, Hq 24, D 128, a 16-node random tree over a 2K / 8K /
@@ -506,16 +535,35 @@ def bench_other_configs(torch, va, synth, dev, reps=20, replicas=4):
         kv_bytes = hkv * (hi - lo) * ((2 * d + 4) if quant else 4 * d)
         q = synth.normal_bf16((rows, hq, d), g).to(dev)
         sink = synth.normal_f32((hq,), g).to(dev) if kind == "window" else None
+        # replicas of the cache (K, V and, quantised, the scales) in one pool
+        # of at least 1 GiB, read in turn
+        esz = 1 if quant else 2
+        kvb = hkv * slots * d * esz
+        per = 2 * kvb + (hkv * slots * 4 if quant else 0)
+        nrep = max(replicas, -(-POOL_BYTES // per))
+        n = nrep
+        pool = torch.empty(n * per, dtype=torch.uint8, device=dev)
+        if quant:
+            kv_all = pool.view(n, per)
+            kv_all[:, :kvb] = torch.randint(0, 126, (n, kvb), dtype=torch.uint8, device=dev)
+            kv_all[:, kvb:2 * kvb] = torch.randint(-127, 128, (n, kvb), dtype=torch.int8, device=dev).view(torch.uint8)
+            kv_all[:, 2 * kvb:] = (torch.rand((n, hkv * slots), device=dev) * 0.02).view(torch.uint8)
+        else:
+            flat = pool.view(torch.bfloat16)
+            piece = 1 << 27
+            for off in range(0, flat.numel(), piece):
+                m = min(piece, flat.numel() - off)
+                flat[off:off + m] = synth.normal_bf16_device((m,), 7000 + pos % 997 + off // piece, dev)
         reps_kv = []
-        for r in range(replicas):
+        for r in range(n):
+            base = pool[r * per:(r + 1) * per]
             if quant:
-                k = torch.randint(0, 126, (hkv, slots, d), dtype=torch.uint8, device=dev)
-                v = torch.randint(-127, 128, (hkv, slots, d), dtype=torch.int8, device=dev)
-                vs = torch.rand((hkv, slots), device=dev) * 0.02
+                k = base[:kvb].view(hkv, slots, d)
+                v = base[kvb:2 * kvb].view(torch.int8).view(hkv, slots, d)
+                vs = base[2 * kvb:].view(torch.float32).view(hkv, slots)
             else:
-                k = synth.normal_bf16_device((hkv, slots, d), 7000 + 10 * r + pos % 997, dev)
-                v = synth.normal_bf16_device((hkv, slots, d), 7001 + 10 * r + pos % 997, dev)
-                vs = None
+                kv = base.view(torch.bfloat16).view(2, hkv, slots, d)
+                k, v, vs = kv[0], kv[1], None
             reps_kv.append((k, v, vs))
         k_new = synth.normal_bf16((rows, hkv, d), g).to(dev)
         v_new = synth.normal_bf16((rows, hkv, d), g).to(dev)
@@ -524,7 +572,7 @@ def bench_other_configs(torch, va, synth, dev, reps=20, replicas=4):
         lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
 
         def one(i, split_only=False):
-            k, v, vs = reps_kv[i % replicas]
+            k, v, vs = reps_kv[i % nrep]
             if kind == "window" and not split_only:
                 va.swa_ring_write(k_new, v_new, pos, k, v, stream=cur())
             va.verify_attn_split(plan, q, k, v, ws, v_scale=vs, stream=cur())
@@ -550,7 +598,7 @@ def bench_other_configs(torch, va, synth, dev, reps=20, replicas=4):
                     "us_per_call": round(times["call"], 2), "split_us": round(times["split"], 2),
                     "kv_gbs_split": round(kv_bytes / (times["split"] * 1e-6) / 1e9, 1),
                     "pct_hbm_peak_split": round(100 * kv_bytes / (times["split"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
-        del reps_kv
+        del reps_kv, pool
     return out
 
 
@@ -562,7 +610,7 @@ def main():
     ap.add_argument("--ctx", type=int, action="append", help="restrict to these contexts")
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0: plan chooses)")
     ap.add_argument("--replicas", type=int, default=REPLICAS)
-    ap.add_argument("--kernel-reps", type=int, default=30, help="event-timed launches per context")
+    ap.add_argument("--kernel-reps", type=int, default=200, help="event-timed launches per context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time to spend on the CPU baseline")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -695,116 +743,101 @@ def main():
     torch.cuda.synchronize()
     eager_ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # ---------------- pass B: per-kernel times ----------------
-    # Each kernel is timed over kernel_reps back-to-back launches replayed
-    # from a graph on the launch stream; the split launches rotate over the
-    # cold replicas like pass A.
+    # ---------------- passes B, B2, C: per-kernel times over cold pools ----------------
+    # Per context, every timed launch reads a replica of that context's
+    # extent from a pool of at least 1 GiB (the never-read capacity tail is
+    # not allocated), so no launch finds its bytes in the 256 MB MALL or an
+    # L2.  Each kernel is timed over kernel_reps back-to-back launches
+    # replayed from a graph on the launch stream.
+    #   B   the split and the combine of the static plan;
+    #   B2  a plain streaming read of the same bytes (va_read_probe: one
+    #       launch, 16-byte loads, a full grid), the ceiling the split
+    #       kernel's rate is compared with beside the 8 TB/s peak;
+    #   C   the device-state entry points: one plan for a bucket covering
+    #       the whole sweep (8 rows at the largest context) fixes the grid;
+    #       each context's positions and live rows come from a state record
+    #       in device memory.  The outputs must match the static call's
+    #       (same partials; the combine may order its FP32 sum differently).
+    bucket = va.Plan(rows=ROWS, live_rows=ROWS, q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
+                     first_pos=max(contexts), kv_capacity=CAP, scale=1 / math.sqrt(D))
+    bws = va.workspace_for(bucket, dev)
+    bout = torch.empty((ROWS, HQ, D), dtype=torch.float32, device=dev)
+    blse = torch.empty((ROWS, HQ), dtype=torch.float32, device=dev)
+    probe_sink = torch.zeros(1, dtype=torch.int32, device=dev)
     sweep = []
-    split_bytes, split_ms = 0.0, 0.0
+    split_bytes, split_ms, probe_bytes, probe_ms = 0.0, 0.0, 0.0, 0.0
+
+    def timed(fn):
+        g = capture(fn)
+        g.replay()
+        a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / args.kernel_reps
+
     for c in cases:
-        def splits(c=c):
+        # replica r: K at pool bytes [r*nb, r*nb + nb/2), V after it; the
+        # views handed to the bucket's state calls are as long as the bucket
+        # (their never-read tails alias the next replicas and a pool tail)
+        nb = kv_bytes(c["hi"])
+        bucket_slots = bucket.info["hi"]
+        pool, npool = cold_pool(torch, synth, dev, nb, seed=50_000 + c["ctx"], tail=2 * bucket_slots * D * 2)
+        fl = pool.view(torch.bfloat16)
+
+        def kv_of(i, slots=None, c=c, fl=fl, npool=npool):
+            slots = slots or c["hi"]
+            kb = (i % npool) * c["hi"] * 2 * D
+            vb = kb + c["hi"] * D
+            return (fl[kb:kb + slots * D].view(HKV, slots, D), fl[vb:vb + slots * D].view(HKV, slots, D))
+
+        def splits(c=c, kv_of=kv_of):
             for i in range(args.kernel_reps):
-                k, v = c["kvs"][i % args.replicas]
+                k, v = kv_of(i)
                 va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=torch.cuda.current_stream())
 
         def combines(c=c):
             for i in range(args.kernel_reps):
                 va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"],
                                        stream=torch.cuda.current_stream())
-        gs, gc = capture(splits), capture(combines)
-        gs.replay()
-        gc.replay()
-        a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(stream)
-        gs.replay()
-        b.record(stream)
-        gc.replay()
-        d.record(stream)
-        torch.cuda.synchronize()
-        del gs, gc
-        s_avg = a.elapsed_time(b) / args.kernel_reps
-        c_avg = b.elapsed_time(d) / args.kernel_reps
-        nb = kv_bytes(c["hi"])
-        split_bytes += nb * args.kernel_reps
-        split_ms += s_avg * args.kernel_reps
-        gbs = nb / (s_avg * 1e-3) / 1e9
-        sweep.append({
-            "ctx": c["ctx"], "live": c["live"], "splits": c["plan"].splits, "kv_bytes": nb,
-            "us_per_call": round((s_avg + c_avg) * 1e3, 2),
-            "split_us": round(s_avg * 1e3, 2), "combine_us": round(c_avg * 1e3, 2),
-            "kv_gbs_split": round(gbs, 1), "pct_hbm_peak_split": round(100 * gbs / HBM_PEAK_GBS, 1),
-            "kv_gbs_call": round(nb / ((s_avg + c_avg) * 1e-3) / 1e9, 1),
-        })
-    achieved = split_bytes / (split_ms * 1e-3) / 1e9
-    launches = len(cases) * args.kernel_reps
 
-    # ---------------- pass B2: the read-stream ceiling ----------------
-    # A plain streaming read of each context's KV byte count (one launch,
-    # 16-byte loads, a full grid), rotated over cold buffers and timed like
-    # pass B: what one launch can read from HBM at that size, the ceiling
-    # the split kernel's rate is compared with beside the 8 TB/s peak.
-    flat = [torch.empty(max(kv_bytes(c["hi"]) for c in cases), dtype=torch.uint8, device=dev)
-            for _ in range(args.replicas)]
-    for f in flat:
-        f.fill_(1)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    probe_bytes, probe_ms = 0.0, 0.0
-    for c, entry in zip(cases, sweep):
-        nb = kv_bytes(c["hi"])
-
-        def reads(nb=nb):
+        def reads(nb=nb, pool=pool, npool=npool):
             for i in range(args.kernel_reps):
-                va.va_read_probe(flat[i % args.replicas], nb, sink, stream=torch.cuda.current_stream())
-        gr = capture(reads)
-        gr.replay()
-        a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-        a.record(stream)
-        gr.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        del gr
-        r_avg = a.elapsed_time(b) / args.kernel_reps
-        probe_bytes += nb * args.kernel_reps
-        probe_ms += r_avg * args.kernel_reps
-        entry["read_probe_us"] = round(r_avg * 1e3, 2)
-        entry["read_probe_gbs"] = round(nb / (r_avg * 1e-3) / 1e9, 1)
-    del flat
-    read_ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
-
-    # ---------------- pass C: the device-state entry points ----------------
-    # One plan for a bucket covering the whole sweep (8 rows at the largest
-    # context) fixes the grid; each context's positions and live rows come
-    # from a state record in device memory.  Timed like pass B; the outputs
-    # must match the static call's (same partials; the combine may order its
-    # FP32 sum differently).
-    bucket = va.Plan(rows=ROWS, live_rows=ROWS, q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
-                     first_pos=max(contexts), kv_capacity=CAP, scale=1 / math.sqrt(D))
-    bws = va.workspace_for(bucket, dev)
-    bout = torch.empty((ROWS, HQ, D), dtype=torch.float32, device=dev)
-    blse = torch.empty((ROWS, HQ), dtype=torch.float32, device=dev)
-    for c, entry in zip(cases, sweep):
+                r = i % npool
+                va.va_read_probe(pool[r * nb:(r + 1) * nb], nb, probe_sink, stream=torch.cuda.current_stream())
         st = va.pack_state(first_pos=c["ctx"], live_rows=c["live"]).to(dev)
 
-        def ssplits(c=c, st=st):
+        def ssplits(c=c, st=st, kv_of=kv_of):
             for i in range(args.kernel_reps):
-                k, v = c["kvs"][i % args.replicas]
+                k, v = kv_of(i, bucket_slots)
                 va.verify_attn_split_state(bucket, st, c["q"], k, v, bws, stream=torch.cuda.current_stream())
 
         def scombines(c=c, st=st):
             for i in range(args.kernel_reps):
                 va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"],
                                              stream=torch.cuda.current_stream())
-        gs, gc = capture(ssplits), capture(scombines)
-        gs.replay()
-        gc.replay()
-        a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(stream)
-        gs.replay()
-        b.record(stream)
-        gc.replay()
-        d.record(stream)
-        torch.cuda.synchronize()
-        del gs, gc
+        s_avg, c_avg = timed(splits), timed(combines)
+        r_avg = timed(reads)
+        ss_avg, sc_avg = timed(ssplits), timed(scombines)
+        del pool, fl
+        split_bytes += nb * args.kernel_reps
+        split_ms += s_avg * args.kernel_reps
+        probe_bytes += nb * args.kernel_reps
+        probe_ms += r_avg * args.kernel_reps
+        gbs = nb / (s_avg * 1e-3) / 1e9
+        sweep.append({
+            "ctx": c["ctx"], "live": c["live"], "splits": c["plan"].splits, "kv_bytes": nb,
+            "cold_pool_replicas": npool,
+            "us_per_call": round((s_avg + c_avg) * 1e3, 2),
+            "split_us": round(s_avg * 1e3, 2), "combine_us": round(c_avg * 1e3, 2),
+            "kv_gbs_split": round(gbs, 1), "pct_hbm_peak_split": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "kv_gbs_call": round(nb / ((s_avg + c_avg) * 1e-3) / 1e9, 1),
+            "read_probe_us": round(r_avg * 1e3, 2), "read_probe_gbs": round(nb / (r_avg * 1e-3) / 1e9, 1),
+            "state_split_us": round(ss_avg * 1e3, 2), "state_combine_us": round(sc_avg * 1e3, 2),
+        })
+        # the state path against the static call on replica 0 of pass A
         call(c, 0)
         k, v = c["kvs"][0]
         va.verify_attn_split_state(bucket, st, c["q"], k, v, bws, stream=stream)
@@ -814,8 +847,9 @@ def main():
         if not (torch.allclose(bout[:L], c["out"][:L], rtol=1e-5, atol=1e-6) and
                 torch.allclose(blse[:L], c["lse"][:L], rtol=1e-6, atol=1e-5)):
             raise SystemExit(f"state path differs from the static call at ctx {c['ctx']}")
-        entry["state_split_us"] = round(a.elapsed_time(b) / args.kernel_reps * 1e3, 2)
-        entry["state_combine_us"] = round(b.elapsed_time(d) / args.kernel_reps * 1e3, 2)
+    achieved = split_bytes / (split_ms * 1e-3) / 1e9
+    read_ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
+    launches = len(cases) * args.kernel_reps
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

@@ -257,6 +257,11 @@ def _split_args(plan, q, k, v, workspace, v_scale):
         raise ValueError("k and v must share shape and strides")
     if k.dim() != 3 or k.shape[0] != plan.kv_heads or k.shape[2] != plan.head_dim or k.stride(2) != 1:
         raise ValueError(f"k/v must be [{plan.kv_heads}, slots, {plan.head_dim}] with contiguous rows")
+    # the kernel reads slots below the ring size, or below the plan's extent
+    # end (a per-call state never reads past it)
+    need = plan.problem.ring_slots or plan.info["hi"]
+    if k.shape[1] < need or (v_scale is not None and (v_scale.dim() != 2 or v_scale.shape[1] < need)):
+        raise ValueError(f"k/v (and v_scale) must hold at least {need} slots")
     _require(workspace, "workspace", (torch.float32,))
     return (_ptr(q), _ptr(k), _ptr(v), _ptr(v_scale), v_scale.stride(0) if v_scale is not None else 0,
             k.stride(0), k.stride(1), _ptr(workspace), workspace.numel() * 4)

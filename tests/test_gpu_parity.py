@@ -603,6 +603,9 @@ def test_bad_arguments_raise():
         va.verify_attn_split(plan, q.to(DEV), k.to(DEV), v.to(DEV), small)
     with pytest.raises(ValueError):
         va.verify_attn_split(plan, q.to(DEV)[:4], k.to(DEV), v.to(DEV), ws)
+    hi = plan.info["hi"]
+    with pytest.raises(ValueError):  # a cache shorter than the keys the plan reads
+        va.verify_attn_split(plan, q.to(DEV), k.to(DEV)[:, :hi - 1], v.to(DEV)[:, :hi - 1], ws)
     flat_k = torch.empty(k.numel() + 1, dtype=torch.bfloat16, device=DEV)
     flat_v = torch.empty(v.numel() + 1, dtype=torch.bfloat16, device=DEV)
     km = flat_k[1:].view(k.shape)      # 2-byte offset: rows not 16-byte aligned
