@@ -16,12 +16,14 @@ extent is NaN: reading it would poison the output, which the full-size
 parity check below catches.  Per-kernel times rotate, per context, over a
 pool of at least 1 GiB of replicas of that context's read extent.
 
-Timing:
-  * value / ms_per_step: HIP events (torch's stream, where the library
-    launches) around `steps` back-to-back steps, no events inside.
-  * per-context kernel times and the roofline: a second pass with an event
-    pair around every split launch (and every combine launch) on the same
-    stream.
+Timing (HIP graphs replayed on the stream the library launches on, HIP
+events around each replay):
+  * value / ms_per_step: `steps` back-to-back steps.
+  * per context, each over `kernel_reps` back-to-back launches: split alone,
+    combine alone, split + combine pairs (us_per_call, what one call costs:
+    the combine reads the partials the split has just written), the plain
+    read of the same bytes, and the device-state split and combine.  The
+    roofline takes the split kernel's average.
 The CPU baseline times the float64 oracle on the same stored bytes (one pass
 over the seven contexts) and doubles as a full-size parity check of the GPU
 outputs of replica 0.
@@ -803,6 +805,13 @@ def main():
                 va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"],
                                        stream=torch.cuda.current_stream())
 
+        def pairs(c=c, kv_of=kv_of):
+            for i in range(args.kernel_reps):
+                k, v = kv_of(i)
+                cur = torch.cuda.current_stream()
+                va.verify_attn_split(c["plan"], c["q"], k, v, c["ws"], stream=cur)
+                va.verify_attn_combine(c["plan"], c["ws"], c["out"], lse=c["lse"], sink=c["sink"], stream=cur)
+
         def reads(nb=nb, pool=pool, npool=npool):
             for i in range(args.kernel_reps):
                 r = i % npool
@@ -818,7 +827,7 @@ def main():
             for i in range(args.kernel_reps):
                 va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"],
                                              stream=torch.cuda.current_stream())
-        s_avg, c_avg = timed(splits), timed(combines)
+        s_avg, c_avg, p_avg = timed(splits), timed(combines), timed(pairs)
         r_avg = timed(reads)
         ss_avg, sc_avg = timed(ssplits), timed(scombines)
         del pool, fl
@@ -830,23 +839,33 @@ def main():
         sweep.append({
             "ctx": c["ctx"], "live": c["live"], "splits": c["plan"].splits, "kv_bytes": nb,
             "cold_pool_replicas": npool,
-            "us_per_call": round((s_avg + c_avg) * 1e3, 2),
+            "us_per_call": round(p_avg * 1e3, 2),
             "split_us": round(s_avg * 1e3, 2), "combine_us": round(c_avg * 1e3, 2),
             "kv_gbs_split": round(gbs, 1), "pct_hbm_peak_split": round(100 * gbs / HBM_PEAK_GBS, 1),
-            "kv_gbs_call": round(nb / ((s_avg + c_avg) * 1e-3) / 1e9, 1),
+            "kv_gbs_call": round(nb / (p_avg * 1e-3) / 1e9, 1),
             "read_probe_us": round(r_avg * 1e3, 2), "read_probe_gbs": round(nb / (r_avg * 1e-3) / 1e9, 1),
             "state_split_us": round(ss_avg * 1e3, 2), "state_combine_us": round(sc_avg * 1e3, 2),
         })
-        # the state path against the static call on replica 0 of pass A
-        call(c, 0)
+        # the state path against a static call with the same split count (the
+        # bucket's, at most one granule each) on replica 0 of pass A: the
+        # same partials, the combine's FP32 order apart
         k, v = c["kvs"][0]
+        p0 = c["plan"].problem
+        eq = va.Plan(rows=ROWS, live_rows=c["live"], q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
+                     first_pos=c["ctx"], kv_capacity=CAP, scale=p0.scale,
+                     splits=max(1, min(bucket.splits, c["plan"].info["chunks"])))
+        eq_ws = va.workspace_for(eq, dev)
+        eq_out, eq_lse = torch.empty_like(c["out"]), torch.empty_like(c["lse"])
+        va.verify_attn_split(eq, c["q"], k, v, eq_ws, stream=stream)
+        va.verify_attn_combine(eq, eq_ws, eq_out, lse=eq_lse, sink=c["sink"], stream=stream)
         va.verify_attn_split_state(bucket, st, c["q"], k, v, bws, stream=stream)
         va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"], stream=stream)
         torch.cuda.synchronize()
         L = c["live"]
-        if not (torch.allclose(bout[:L], c["out"][:L], rtol=1e-5, atol=1e-6) and
-                torch.allclose(blse[:L], c["lse"][:L], rtol=1e-6, atol=1e-5)):
+        if not (torch.allclose(bout[:L], eq_out[:L], rtol=1e-5, atol=1e-6) and
+                torch.allclose(blse[:L], eq_lse[:L], rtol=1e-6, atol=1e-5)):
             raise SystemExit(f"state path differs from the static call at ctx {c['ctx']}")
+        del eq_ws
     achieved = split_bytes / (split_ms * 1e-3) / 1e9
     read_ceiling = probe_bytes / (probe_ms * 1e-3) / 1e9
     launches = len(cases) * args.kernel_reps

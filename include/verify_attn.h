@@ -123,12 +123,13 @@ typedef struct {
 
 /* Validate *p and build *plan.  Writes the workspace size the split needs to
  * *workspace_bytes (may be NULL).  Pure host code: needs no GPU.
- * With splits = 0 the plan chooses: C, the number of 32-key granules (one
- * granule per split), or, where B_p * Hkv >= 4 * B_g, round(sqrt(C * 47.61 *
- * B_g / (B_p * Hkv))) rounded to the nearest multiple of 8 from 8 up (B_g
- * the KV bytes of one granule, 32*4*D or 32*(2*D+4) quantised; B_p =
- * rows*G*(D+2)*4 partial bytes per split and KV head); then at most
- * num_cus / Hkv (a multiple of 8 from 8 up) and at most C, at least 1.
+ * With splits = 0 the plan chooses from C, the number of 32-key granules:
+ * s = round(sqrt(C * 47.61 * B_g / (B_p * Hkv))) (B_g the KV bytes of one
+ * granule, 32*4*D or 32*(2*D+4) quantised; B_p = rows*G*(D+2)*4 partial
+ * bytes per split and KV head); C itself (one granule per split) where
+ * 4 * s >= 3 * C, else s rounded to the nearest multiple of 8 from 8 up;
+ * then at most num_cus / Hkv (a multiple of 8 from 8 up) and at most C, at
+ * least 1.
  * Errors: VA_ERR_INVALID (NULL pointers, counts out of range, parent[i] >= i
  * or < -1, C % 64 != 0, C < W + rows - 1 so that the rows' own writes would
  * evict history an earlier row needs, scale not finite and > 0, positions
@@ -154,7 +155,7 @@ va_status verify_attn_plan_split_range(const va_plan *plan, int32_t s,
  *   O_s = the same weights times v_j, summed (FP32 [D], unnormalised)
  * into the workspace: first the {m, l} pairs as FP32 [S][Hkv][rows*G][2],
  * then, from the next multiple of 256 bytes, O as FP32 [S][Hkv][rows*G][D].
- * Padding rows get m = -inf, l = 0, O = 0.
+ * Padding rows' partials are not written (the combine never reads them).
  *   q        [rows, Hq, D] bf16, contiguous, 16-byte aligned.
  *   k, v     [Hkv, slots, D] with D contiguous: bf16 (VA_KV_BF16) or
  *            uint8 E4M3FN codes / int8 codes.  Slot of position p: p (linear)

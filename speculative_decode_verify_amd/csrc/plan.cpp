@@ -15,18 +15,19 @@ static inline int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
 static inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // Splits: each workgroup streams a contiguous run of 32-key granules, one
-// after another, and writes its rows' partials (m, l, O: rows*G*(D+2)*4
-// bytes per KV head), which the combine reads back.  By default each split
-// takes one granule, up to one workgroup per CU over all KV heads (more than
-// one per CU measured slower), the count kept a multiple of 8 (one share per
-// XCD) from 8 up.  Where a split's partials outweigh its granule four times
-// or more (many matrix rows over several KV heads: the 96-row tree writes
-// 50 KB per split and head against 16 KB read per granule), fewer splits
-// pay: timed as split + combine pairs on MI355X, the best count there is
-// near S = 6.9 * sqrt(C * B_granule / (B_partial * Hkv)) (16 splits for the
-// tree at 2K keys, 32 at 8K, 64 at 32K), which the plan then uses.  For the
-// 48-row shapes (ratio ~1.5) the same fit was no better overall (faster
-// pairs at 4K-32K, slower at 1K and for the window ring) and is not used.
+// after another, and writes its live rows' partials (m, l, O: up to
+// rows*G*(D+2)*4 bytes per KV head), which the combine reads back right
+// after.  More splits shorten the longest walk; fewer shrink the partials
+// that must be written back and read again.  Timed as split + combine pairs
+// over cold caches on MI355X, the best count is near
+// S = 6.9 * sqrt(C * B_granule / (B_partial * Hkv)), with B_partial counted
+// over all rows: for the 48-row full-attention shape (ratio ~1.5) 64 splits
+// at 4K keys, 128 at 16K (1.4 us per pair faster than 256), 176 at 32K; for
+// the 96-row tree over four KV heads 16 / 32 / 64 at 2K / 8K / 32K.  The
+// count is kept a multiple of 8 (one share per XCD) from 8 up and capped at
+// one workgroup per CU over all KV heads (more than one per CU measured
+// slower).  Where the fit comes within a quarter of one granule per split
+// (short reads: 33 granules at 1K keys) every split takes one granule.
 static const int64_t kWorkgroupsPerCU = 1;
 
 // round(sqrt(chunks * k_num / k_den)) exactly: the largest s with
@@ -48,10 +49,12 @@ static int32_t choose_splits(int64_t chunks, int32_t kv_heads, int32_t num_cus, 
   int64_t cap = (kWorkgroupsPerCU * num_cus) / kv_heads;
   if (cap < 1) cap = 1;
   if (cap >= 8) cap = (cap / 8) * 8;  // whole rounds over the 8 XCDs
-  int64_t s = chunks;                 // one granule per split
-  if (partial_bytes * kv_heads >= 4 * granule_bytes) {
-    s = round_sqrt_ratio(chunks, 4761 * granule_bytes, 100 * partial_bytes * kv_heads);  // 6.9^2 = 47.61
-    if (s >= 8) s = ((s + 4) / 8) * 8;
+  // 6.9 * sqrt(chunks * granule_bytes / (partial_bytes * kv_heads)), 6.9^2 = 47.61
+  int64_t s = round_sqrt_ratio(chunks, 4761 * granule_bytes, 100 * partial_bytes * kv_heads);
+  if (4 * s >= 3 * chunks) {
+    s = chunks;  // within a quarter of one granule per split: take one granule each
+  } else if (s >= 8) {
+    s = ((s + 4) / 8) * 8;
   }
   if (s > cap) s = cap;
   if (s > chunks) s = chunks;

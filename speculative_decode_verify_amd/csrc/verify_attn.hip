@@ -822,20 +822,19 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
     st = st + 1 == NST ? 0 : st + 1;
   }
 
-  // ---------------- partials of this wave's rows ----------------
+  // ---------------- partials of this wave's live rows ----------------
   // Normalised to the true maximum M of the split: m = M, l = sum 2^(x - M),
-  // O = sum 2^(x - M) v.
+  // O = sum 2^(x - M) v.  Padding rows store nothing: the combine never
+  // reads them.
+  if (!active) return;
   const float lt = wave_sum16x4(lrow);
   const float f = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - mtrue);
-  if (m < mrows) {
+  if (row_ok) {
     const int64_t unit = ((int64_t)split * kv_heads + kvh) * mrows + m;
-    if (g4 == 0) {
-      *(f32x2 *)(ws_ml + unit * 2) = row_ok ? (f32x2){mtrue, lt * f} : (f32x2){-INFINITY, 0.f};
-    }
+    if (g4 == 0) *(f32x2 *)(ws_ml + unit * 2) = (f32x2){mtrue, lt * f};
     float *op = ws_o + unit * D;
-    const float fo = row_ok ? f : 0.f;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) *(f32x4 *)(op + 16 * md + 4 * g4) = o[md] * fo;
+    for (int md = 0; md < MD; ++md) *(f32x4 *)(op + 16 * md + 4 * g4) = o[md] * f;
   }
 }
 

@@ -2,6 +2,7 @@
 point, rejects every malformed problem, and its host plan agrees bit-exactly
 with the oracle's visibility rules and split rule.  No kernel is launched."""
 import ctypes
+import math
 import os
 import re
 
@@ -190,18 +191,26 @@ def test_workspace_size_formula():
 
 
 def test_chosen_splits_are_sane():
-    """The plan's split count: one 32-key granule per split, or, where a
-    split's partials outweigh a granule four times over, about
-    6.9 * sqrt(C * B_granule / (B_partial * Hkv)) rounded to a multiple of 8;
-    at most one workgroup per CU over the KV heads (a multiple of 8) and at
-    most one split per granule."""
-    want = {1024: 33, 4096: 129, 16384: 256, 32768: 256, 65536: 256, 131072: 256, 196608: 256}
+    """The plan's split count: about 6.9 * sqrt(C * B_granule / (B_partial *
+    Hkv)) rounded to a multiple of 8, or one 32-key granule per split where
+    that comes within a quarter of the granule count; at most one workgroup
+    per CU over the KV heads (a multiple of 8) and at most one split per
+    granule.  The counts are written out for the measured shapes and the
+    rule is recomputed here in floating point for the sweep."""
+    want = {1024: 33, 4096: 64, 16384: 128, 32768: 176, 65536: 256, 131072: 256, 196608: 256}
     for P, S_want in want.items():
         plan = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, first_pos=P,
                        kv_capacity=262144, num_cus=256)
         S, C = plan.splits, plan.info["chunks"]
         assert S == S_want, (P, S)
         assert 1 <= S <= min(C, 256) and (S == C or S % 8 == 0)
+        fit = round(6.9 * math.sqrt(C * (32 * 4 * 128) / (48 * 130 * 4)))
+        expect = C if 4 * fit >= 3 * C else ((fit + 4) // 8) * 8
+        assert S == min(expect, 256, C), (P, S, expect)
+    for t0 in (5120, 51200, 194560):  # window ring, D 64: 129 granules
+        plan = va.Plan(rows=8, live_rows=5, q_heads=6, kv_heads=1, head_dim=64, mask="window", first_pos=t0,
+                       window=4096, ring_slots=4160, num_cus=256)
+        assert plan.info["chunks"] == 129 and plan.splits == 64, (t0, plan.splits)
     for P, S_want in {2048: 16, 8192: 32, 32768: 64}.items():
         plan = va.Plan(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=P,
                        parent=[-1] * 16, kv_capacity=P + 100, num_cus=256)
