@@ -97,6 +97,19 @@ def summarize_profiles(d):
     import csv
     import collections
 
+    def kname(n):
+        """Kernel name without spaces; split_kernel's last template flag (the
+        fused append) becomes ",append" when set and is dropped otherwise."""
+        n = n.replace(" ", "")
+        if "split_kernel<" in n:
+            i = n.index("split_kernel<") + len("split_kernel<")
+            j = n.index(">", i)
+            args = n[i:j].split(",")
+            if len(args) == 7:
+                args = args[:6] + (["append"] if args[6] == "true" else [])
+            n = n[:i] + ",".join(args) + n[j:]
+        return n
+
     def bench_line(log):
         for line in open(os.path.join(d, log)):
             if line.startswith("{") and '"metric"' in line:
@@ -117,7 +130,7 @@ def summarize_profiles(d):
     f_scale = copy_bytes / (sum(cf) / len(cf) * 1024)
     w_scale = copy_bytes / (sum(cw) / len(cw) * 1024)
     def static_split(n):  # the sweep's kernel: static plan, D 128, 3 consumer waves, bf16
-        return "split_kernel<128,3,0,4,2,false>" in n.replace(" ", "")
+        return "split_kernel<128,3,0,4,2,false>" in kname(n)
 
     fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if static_split(n)]
     wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if static_split(n)]
@@ -135,7 +148,7 @@ def summarize_profiles(d):
     trace = list(csv.DictReader(open(os.path.join(d, "trace", "bench_kernel_trace.csv"))))
     dur = collections.defaultdict(list)
     for r in trace:
-        n = r["Kernel_Name"]
+        n = kname(r["Kernel_Name"])
         kind = ("split_kernel" if "split_kernel" in n else "combine_kernel" if "combine_kernel" in n
                 else "read_probe_kernel" if "read_probe_kernel" in n else None)
         if kind and "<" in n:
@@ -225,7 +238,7 @@ def summarize_profiles(d):
             tdur[(kind, wgs)] += v
         vals = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in csv.DictReader(open(up)):
-            n = r["Kernel_Name"].replace(" ", "")
+            n = kname(r["Kernel_Name"])
             wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
             for key, _ in kinds:
                 if key in n:
@@ -573,21 +586,27 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
         o = torch.empty((rows, hq, d), dtype=torch.float32, device=dev)
         lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
 
-        def one(i, split_only=False):
+        def one(i, split_only=False, fused=False):
             k, v, vs = reps_kv[i % nrep]
-            if kind == "window" and not split_only:
-                va.swa_ring_write(k_new, v_new, pos, k, v, stream=cur())
-            va.verify_attn_split(plan, q, k, v, ws, v_scale=vs, stream=cur())
+            if fused:  # the ring write inside the split launch
+                va.verify_attn_split_append(plan, q, k_new, v_new, k, v, ws, stream=cur())
+            else:
+                if kind == "window" and not split_only:
+                    va.swa_ring_write(k_new, v_new, pos, k, v, stream=cur())
+                va.verify_attn_split(plan, q, k, v, ws, v_scale=vs, stream=cur())
             if not split_only:
                 va.verify_attn_combine(plan, ws, o, lse=lse, sink=sink, stream=cur())
         times = {}
-        for label, so in (("call", False), ("split", True)):
+        passes = [("call", False, False), ("split", True, False)]
+        if kind == "window":
+            passes.append(("fused", False, True))
+        for label, so, fu in passes:
             for i in range(2):
-                one(i, so)
+                one(i, so, fu)
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for i in range(reps):
-                    one(i, so)
+                    one(i, so, fu)
             gr.replay()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -596,8 +615,11 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
             torch.cuda.synchronize()
             times[label] = a.elapsed_time(b) * 1e3 / reps
             del gr
+        extra = {}
+        if "fused" in times:  # verify_attn_split_append + combine: two launches, not three
+            extra["us_per_call_append_fused"] = round(times["fused"], 2)
         out.append({"config": kind, "position": pos, "splits": plan.splits, "kv_bytes": kv_bytes,
-                    "us_per_call": round(times["call"], 2), "split_us": round(times["split"], 2),
+                    "us_per_call": round(times["call"], 2), **extra, "split_us": round(times["split"], 2),
                     "kv_gbs_split": round(kv_bytes / (times["split"] * 1e-6) / 1e9, 1),
                     "pct_hbm_peak_split": round(100 * kv_bytes / (times["split"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
         del reps_kv, pool

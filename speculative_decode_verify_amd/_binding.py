@@ -93,6 +93,7 @@ def load_library():
     lib.verify_attn_combine.argtypes = [ctypes.POINTER(va_plan), V, SZ, V, V, V, V]
     lib.verify_attn_split_state.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, I64, V, SZ, V]
     lib.verify_attn_combine_state.argtypes = [ctypes.POINTER(va_plan), V, V, SZ, V, V, V, V]
+    lib.verify_attn_split_append.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, V, SZ, V]
     lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
     lib.verify_kv_write.argtypes = [V, V, I32, I64, I32, I32, I32, V, V, V, I64, I64, I32, I64, I64, V]
     SP = ctypes.POINTER(va_sample_params)
@@ -105,7 +106,7 @@ def load_library():
     lib.va_status_string.argtypes = [ctypes.c_int]
     lib.va_status_string.restype = ctypes.c_char_p
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
-               "verify_attn_split", "verify_attn_combine", "verify_attn_split_state",
+               "verify_attn_split", "verify_attn_combine", "verify_attn_split_state", "verify_attn_split_append",
                "verify_attn_combine_state", "swa_ring_write", "verify_kv_write", "va_sample", "va_accept",
                "va_sample_accept", "va_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -271,6 +272,23 @@ def verify_attn_split(plan, q, k, v, workspace, v_scale=None, stream=None):
     """Partial attention of every split (shapes as in _split_args)."""
     _check("verify_attn_split", _lib().verify_attn_split(
         ctypes.byref(plan.plan), *_split_args(plan, q, k, v, workspace, v_scale), _stream(stream)))
+
+
+def verify_attn_split_append(plan, q, k_new, v_new, k, v, workspace, stream=None):
+    """verify_attn_split that also stores the rows' own K/V (k_new, v_new
+    [rows, Hkv, D] bf16 contiguous) into the cache k, v in the same launch."""
+    import torch
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _require(t, n, (torch.bfloat16,))
+    shape = (plan.rows, plan.kv_heads, plan.head_dim)
+    if not (k_new.is_contiguous() and v_new.is_contiguous()) or tuple(k_new.shape) != shape or \
+            tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new/v_new must be contiguous {list(shape)} bfloat16")
+    if not plan.problem.ring_slots and k.shape[1] < plan.problem.first_pos + plan.rows:
+        raise ValueError(f"k/v must hold the {plan.rows} rows' slots from {plan.problem.first_pos}")
+    qp, kp, vp, _, _, hs, rs, wp, wb = _split_args(plan, q, k, v, workspace, None)
+    _check("verify_attn_split_append", _lib().verify_attn_split_append(
+        ctypes.byref(plan.plan), qp, _ptr(k_new), _ptr(v_new), kp, vp, hs, rs, wp, wb, _stream(stream)))
 
 
 def verify_attn_split_state(plan, state, q, k, v, workspace, v_scale=None, stream=None):

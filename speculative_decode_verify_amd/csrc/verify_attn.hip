@@ -88,6 +88,14 @@ struct SplitArgs {
   // above that depend on positions or rows are then derived from it.
   const va_state *state;
   int64_t bucket_hi;  // the plan's extent end: no state may read beyond it
+  // Append (bf16, chain modes, static plans): the rows' own K/V, [rows, Hkv,
+  // D] bf16 with new_row_stride_b bytes between rows (NULL: no append).
+  // Split 0 stores all rows to slots (append_slot0 + r) mod ring_slots, or
+  // append_slot0 + r for a linear cache; the workgroups whose chunks hold
+  // the live rows' positions put the new rows into their staged tiles.
+  const uint8_t *k_new, *v_new;
+  int64_t new_row_stride_b;
+  int64_t append_slot0;
 };
 
 struct CombineArgs {
@@ -305,8 +313,9 @@ __device__ __forceinline__ void pin(int64_t x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
 
-template <int D, int W, int FMT, int NST, int NPW, bool STATE>
+template <int D, int W, int FMT, int NST, int NPW, bool STATE, bool APP>
 __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_kernel(const SplitArgs a) {
+  static_assert(!APP || (FMT == 0 && NPW == 2 && !STATE), "append: bf16 tiles, one producer per tile kind");
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
   constexpr int MD = D / 16;  // O^T row blocks over d
@@ -376,6 +385,8 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
   pin(ws_ml), pin(ws_o);
 #pragma unroll
   for (int i = 0; i < VA_MAX_ROWS; ++i) pin(anc[i]);
+  const uint8_t *k_new = a.k_new, *v_new = a.v_new;
+  if constexpr (APP) pin(k_new), pin(v_new);
 
   int32_t c_first = 0, nch = 0;
   auto chunk_range = [&]() {
@@ -496,6 +507,37 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
     // arithmetic on constants.
     auto produce = [&](auto pw_const) {
       constexpr int PW = decltype(pw_const)::value;
+      // Append: producer 0 owns the K tiles' DMA, producer 1 the V tiles'
+      // (bf16: U = NDMA), so each takes the new rows of its tile kind, one
+      // 16-byte piece per lane and pass, loaded before the first DMA issue.
+      constexpr int APASS = (VA_MAX_ROWS * PIECES + 63) / 64;
+      const uint8_t *knew = PW == 0 ? k_new : v_new;
+      u32x4 nrow[APASS];
+      if constexpr (APP) {
+        const uint8_t *src = knew + (int64_t)kvh * D * 2;
+#pragma unroll
+        for (int i = 0; i < APASS; ++i) {
+          const int rr = (64 * i + lane) / PIECES;
+          if (rr < a.rows) nrow[i] = *(const u32x4 *)(src + rr * a.new_row_stride_b + 16 * (lane % PIECES));
+        }
+      }
+      // the new live rows of chunk n into its staged tile (after its DMA
+      // landed, before the barrier that publishes it)
+      auto overlay = [&](int32_t n) {
+        const int32_t c0 = (c_first + n) * kChunk;
+        if (t0_rel >= c0 + kChunk || t0_rel + live_rows <= c0) return;
+        uint8_t *tile = smem + (n % NST) * kStageB + (PW == 0 ? 0 : kTileB);
+#pragma unroll
+        for (int i = 0; i < APASS; ++i) {
+          const int rr = (64 * i + lane) / PIECES;
+          const int j = t0_rel + rr - c0;
+          if (rr < live_rows && j >= 0 && j < kChunk) {
+            const int f = PW == 0 ? (j & (PIECES - 1)) : ((2 * j) & (PIECES - 2));
+            *(u32x4 *)(tile + j * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      };
       uint32_t off[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
@@ -551,6 +593,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
         const int32_t later = nch - 1 - n;
         if constexpr (FMT == 0) {
           wait_chunks<kVmP, NST - 2>(later < NST - 2 ? later : NST - 2);
+          if constexpr (APP) overlay(n);
         } else {
           const int32_t after = later - 1;
           wait_chunks<kVmP, NST - 3>(after < NST - 3 ? (after > 0 ? after : 0) : NST - 3);
@@ -558,6 +601,24 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
         wg_barrier();
         if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
         st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
+      }
+      // split 0 stores every row (padding included) to the cache; nothing in
+      // this launch reads those slots from memory: the live rows' keys were
+      // put into the tiles above, and the padding rows' slots lie outside
+      // every row's keys
+      if (APP && split == 0) {
+        uint8_t *dst = (PW == 0 ? const_cast<uint8_t *>(kptr) : const_cast<uint8_t *>(vptr)) +
+                       (int64_t)kvh * head_stride + 16 * (lane % PIECES);
+#pragma unroll
+        for (int i = 0; i < APASS; ++i) {
+          const int rr = (64 * i + lane) / PIECES;
+          if (rr < a.rows) {
+            const int64_t slot =
+                ring_slots ? (int64_t)(((uint64_t)a.append_slot0 + (uint64_t)rr) % (uint64_t)ring_slots)
+                           : a.append_slot0 + rr;
+            *(u32x4 *)(dst + slot * row_stride) = nrow[i];
+          }
+        }
       }
     };
     static_assert(NPW == 1 || NPW == 2, "one or two producers");
@@ -1160,25 +1221,26 @@ constexpr int producers_for() { return FMT == 1 ? 1 : 2; }
 template <int D, int FMT>
 constexpr int stages_for() { return FMT == 1 ? 8 : (D == 64 ? 8 : 4); }
 
-template <int D, int W, int FMT, bool STATE>
+template <int D, int W, int FMT, bool STATE, bool APP>
 hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
   dim3 grid(a.splits, a.kv_heads);
   constexpr int NDW = FMT == 1 ? 1 : 0;
-  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE>), grid, dim3(64 * (W + NDW + NPW)), 0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE, APP>), grid, dim3(64 * (W + NDW + NPW)), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
-template <int D, int FMT, bool STATE>
+template <int D, int FMT, bool STATE, bool APP = false>
 hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
   switch (nb_total) {
-    case 1: return launch_split<D, 1, FMT, STATE>(a, stream);
-    case 2: return launch_split<D, 2, FMT, STATE>(a, stream);
-    case 3: return launch_split<D, 3, FMT, STATE>(a, stream);
-    case 4: return launch_split<D, 4, FMT, STATE>(a, stream);
-    case 5: return launch_split<D, 5, FMT, STATE>(a, stream);
-    case 6: return launch_split<D, 6, FMT, STATE>(a, stream);
+    case 1: return launch_split<D, 1, FMT, STATE, APP>(a, stream);
+    case 2: return launch_split<D, 2, FMT, STATE, APP>(a, stream);
+    case 3: return launch_split<D, 3, FMT, STATE, APP>(a, stream);
+    case 4: return launch_split<D, 4, FMT, STATE, APP>(a, stream);
+    case 5: return launch_split<D, 5, FMT, STATE, APP>(a, stream);
+    case 6: return launch_split<D, 6, FMT, STATE, APP>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -1192,7 +1254,8 @@ hipError_t dispatch_split(const SplitArgs &a, int nb_total, bool quant, int head
 
 va_status split_impl(const va_plan *plan, const va_state *state, const void *q, const void *k, const void *v,
                      const float *v_scale, int64_t v_scale_head_stride, int64_t kv_head_stride,
-                     int64_t kv_row_stride, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                     int64_t kv_row_stride, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                     const void *k_new = nullptr, const void *v_new = nullptr) {
   const va_plan_data *d = plan_of(plan);
   if (!d) return VA_ERR_INVALID;
   if (!workspace || workspace_bytes < d->workspace_bytes) return VA_ERR_WORKSPACE;
@@ -1200,9 +1263,9 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
   if (d->splits > kMaxSplits) return VA_ERR_UNSUPPORTED;
   const bool quant = d->kv_fmt == VA_KV_K_E4M3_WHT_V_I8;
   const int64_t esz = quant ? 1 : 2;
-  // a per-call state may read anywhere in the bucket, so its pointers are
-  // checked even when the plan's own extent is empty
-  if (state || d->hi > d->lo) {
+  // a per-call state may read anywhere in the bucket, and an append writes,
+  // so their pointers are checked even when the plan's own extent is empty
+  if (state || k_new || d->hi > d->lo) {
     if (!q || !k || !v) return VA_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return VA_ERR_INVALID;
     if (kv_head_stride < 0 || kv_row_stride < d->head_dim) return VA_ERR_INVALID;
@@ -1252,9 +1315,21 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
   for (int r = 0; r < VA_MAX_ROWS; ++r) a.anc[r] = d->anc[r];
   a.state = state;
   a.bucket_hi = d->hi;
+  if (k_new) {
+    a.k_new = (const uint8_t *)k_new;
+    a.v_new = (const uint8_t *)v_new;
+    a.new_row_stride_b = (int64_t)d->kv_heads * d->head_dim * 2;
+    a.append_slot0 = d->ring_slots ? d->first_pos % d->ring_slots : d->first_pos;
+  }
   const int nb_total = (d->matrix_rows + 15) / 16;
-  const hipError_t e = state ? dispatch_split<true>(a, nb_total, quant, d->head_dim, stream)
-                             : dispatch_split<false>(a, nb_total, quant, d->head_dim, stream);
+  hipError_t e;
+  if (k_new) {  // bf16 and static only (checked by the entry point)
+    e = d->head_dim == 64 ? dispatch_rows<64, 0, false, true>(a, nb_total, stream)
+                          : dispatch_rows<128, 0, false, true>(a, nb_total, stream);
+  } else {
+    e = state ? dispatch_split<true>(a, nb_total, quant, d->head_dim, stream)
+              : dispatch_split<false>(a, nb_total, quant, d->head_dim, stream);
+  }
   return e == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
 
@@ -1300,6 +1375,19 @@ extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const
                                        size_t workspace_bytes, hipStream_t stream) {
   return split_impl(plan, nullptr, q, k, v, v_scale, v_scale_head_stride, kv_head_stride, kv_row_stride,
                     workspace, workspace_bytes, stream);
+}
+
+extern "C" va_status verify_attn_split_append(const va_plan *plan, const void *q, const void *k_new,
+                                              const void *v_new, void *k, void *v, int64_t kv_head_stride,
+                                              int64_t kv_row_stride, void *workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  const va_plan_data *d = plan_of(plan);
+  if (!d) return VA_ERR_INVALID;
+  if (d->mask == VA_MASK_TREE || d->kv_fmt != VA_KV_BF16) return VA_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return VA_ERR_INVALID;
+  if (!d->ring_slots && d->first_pos + d->rows > d->kv_capacity) return VA_ERR_CAPACITY;
+  return split_impl(plan, nullptr, q, k, v, nullptr, 0, kv_head_stride, kv_row_stride, workspace, workspace_bytes,
+                    stream, k_new, v_new);
 }
 
 extern "C" va_status verify_attn_combine(const va_plan *plan, const void *workspace, size_t workspace_bytes,

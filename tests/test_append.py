@@ -1,0 +1,177 @@
+"""verify_attn_split_append: the rows' own K/V stored and read in one launch.
+
+Gates:
+* window ring (config-3 shapes, and a 64-slot ring that wraps inside the
+  step): the outputs against the float64 oracle on its own replayed ring,
+  and the ring contents after the call bit-exact against that replay;
+* every case: the split partials bit-identical to swa_ring_write /
+  verify_kv_write followed by verify_attn_split on a copy of the same
+  cache, and the cache contents after the call identical too;
+* the new rows straddling a 32-key chunk boundary and a split boundary
+  (two workgroups put rows into their tiles), no live row (the rows are
+  stored, nothing read), 16 rows at D 128;
+* tree mode and quantised caches are refused; a linear cache too short for
+  the rows is refused before any launch.
+The stale contents of the slots the rows take are scaled by 100, so a key
+read from memory instead of from the new rows would show.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decode_verify_amd as va
+from speculative_decode_verify_amd import synth
+from oracle import attn as oattn
+from oracle import masks as omasks
+from oracle.masks import Problem
+from test_gpu_parity import NAN, check, f64, partials, plan_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _ws(plan):
+    return torch.full(((plan.workspace_bytes + 3) // 4,), NAN, dtype=torch.float32, device=DEV)
+
+
+def _both(plan, q, k_new, v_new, k, v, write_then_split, sink):
+    """(fused partials, out, lse, k, v), (reference partials, out, lse, k, v)."""
+    res = []
+    for fused in (True, False):
+        kc, vc = k.clone(), v.clone()
+        ws = _ws(plan)
+        out = torch.full((plan.rows, plan.q_heads, plan.head_dim), NAN, dtype=torch.float32, device=DEV)
+        lse = torch.full((plan.rows, plan.q_heads), NAN, dtype=torch.float32, device=DEV)
+        if fused:
+            va.verify_attn_split_append(plan, q, k_new, v_new, kc, vc, ws)
+        else:
+            write_then_split(kc, vc, ws)
+        va.verify_attn_combine(plan, ws, out, lse=lse, sink=sink)
+        torch.cuda.synchronize()
+        res.append((partials(plan, ws.cpu()), out.cpu(), lse.cpu(), kc.cpu(), vc.cpu()))
+    return res
+
+
+def _same(fused, ref, live, name):
+    (mf, lf, of), out_f, lse_f, kf, vf = fused
+    (mr, lr, orr), out_r, lse_r, kr, vr = ref
+    for a, b, what in ((mf, mr, "m"), (lf, lr, "l"), (of, orr, "O")):
+        assert np.array_equal(a[:, :live], b[:, :live], equal_nan=True), f"{name}: {what} partials differ"
+    assert torch.equal(out_f.view(torch.int32), out_r.view(torch.int32)), f"{name}: out differs"
+    assert torch.equal(lse_f.view(torch.int32), lse_r.view(torch.int32)), f"{name}: lse differs"
+    assert torch.equal(kf.view(torch.int16), kr.view(torch.int16)), f"{name}: K cache differs"
+    assert torch.equal(vf.view(torch.int16), vr.view(torch.int16)), f"{name}: V cache differs"
+
+
+@pytest.mark.parametrize("t0,W,C,live,splits", [(5120, 4096, 4160, 5, 0), (51200, 4096, 4160, 8, 0),
+                                                (194560, 4096, 4160, 7, 0), (999, 57, 64, 8, 3),
+                                                (1021, 57, 64, 6, 2)])
+def test_append_window_ring(t0, W, C, live, splits):
+    rows, Hq, Hkv, D = 8, 6, 1, 64
+    g = synth.gen(12000 + t0 + live)
+    base = t0 - C
+    n = C + rows
+    kl = synth.normal_bf16((Hkv, n, D), g)     # position base + i
+    vl = synth.normal_bf16((Hkv, n, D), g)
+    q = synth.normal_bf16((rows, Hq, D), g)
+    s = synth.normal_f32((Hq,), g)
+    k_ring = torch.empty((Hkv, C, D), dtype=torch.bfloat16)
+    v_ring = torch.empty((Hkv, C, D), dtype=torch.bfloat16)
+    for i in range(C):
+        k_ring[:, (base + i) % C] = kl[:, i]
+        v_ring[:, (base + i) % C] = vl[:, i]
+    for r in range(rows):  # stale, loud contents in the slots the rows take
+        k_ring[:, (t0 + r) % C] = kl[:, r] * 100
+        v_ring[:, (t0 + r) % C] = vl[:, r] * 100
+    k_new = kl[:, C:C + rows].permute(1, 0, 2).contiguous().to(DEV)
+    v_new = vl[:, C:C + rows].permute(1, 0, 2).contiguous().to(DEV)
+    plan = plan_for(rows, live, Hq, Hkv, D, "window", first_pos=t0, window=W, ring_slots=C,
+                    scale=1 / math.sqrt(D), splits=splits)
+    qd, sd = q.to(DEV), s.to(DEV)
+
+    def ref(kc, vc, ws):
+        va.swa_ring_write(k_new, v_new, t0, kc, vc)
+        va.verify_attn_split(plan, qd, kc, vc, ws)
+
+    fused, unfused = _both(plan, qd, k_new, v_new, k_ring.to(DEV), v_ring.to(DEV), ref, sd)
+    name = f"append window t0={t0} C={C} live={live}"
+    _same(fused, unfused, live, name)
+    # oracle: its own ring from the linear data, replaying the same positions
+    labels = omasks.ring_replay(C, list(range(base, t0 + rows)))
+    exp_k = torch.stack([kl[:, lab - base] for lab in labels], dim=1)
+    assert torch.equal(fused[3].view(torch.int16), exp_k.view(torch.int16)), f"{name}: ring contents"
+    ring_k = np.zeros((Hkv, C, D))
+    ring_v = np.zeros((Hkv, C, D))
+    for pos in range(base, t0 + rows):
+        ring_k[:, pos % C] = f64(kl[:, pos - base])
+        ring_v[:, pos % C] = f64(vl[:, pos - base])
+    p = Problem("window", rows, live, first_pos=t0, window=W, ring_slots=C)
+    ro, rl = oattn.verify_attn_ref(p, f64(q), oattn.Cache(ring_k, ring_v, ring_slots=C), plan.problem.scale, f64(s))
+    check(fused[1], fused[2], ro, rl, live, name)
+
+
+@pytest.mark.parametrize("rows,live,Hq,Hkv,D,fp,splits", [
+    (8, 8, 6, 1, 128, 4093, 0),      # rows 4093..4100 straddle a chunk boundary
+    (8, 6, 6, 1, 128, 1021, 32),     # the chunk boundary is a split boundary too
+    (16, 16, 8, 2, 128, 20005, 0),   # 16 rows at D 128, two KV heads
+    (8, 5, 6, 1, 64, 3000, 0),
+    (8, 0, 6, 1, 128, 500, 0),       # no live row: stored, nothing read
+])
+def test_append_linear(rows, live, Hq, Hkv, D, fp, splits):
+    g = synth.gen(13000 + fp + rows)
+    cap = fp + rows + 40
+    k = synth.normal_bf16((Hkv, cap, D), g)
+    v = synth.normal_bf16((Hkv, cap, D), g)
+    k_new = synth.normal_bf16((rows, Hkv, D), g)
+    v_new = synth.normal_bf16((rows, Hkv, D), g)
+    k[:, fp:fp + rows] = k_new.permute(1, 0, 2) * 100   # stale, loud
+    v[:, fp:fp + rows] = v_new.permute(1, 0, 2) * 100
+    k[:, fp + rows:] = NAN
+    v[:, fp + rows:] = NAN
+    q = synth.normal_bf16((rows, Hq, D), g)
+    s = synth.normal_f32((Hq,), g)
+    plan = plan_for(rows, live, Hq, Hkv, D, "causal", first_pos=fp, kv_capacity=cap, scale=1 / math.sqrt(D),
+                    splits=splits)
+    qd, kn, vn = q.to(DEV), k_new.to(DEV), v_new.to(DEV)
+
+    def ref(kc, vc, ws):
+        va.verify_kv_write(kn, vn, fp, kc, vc)
+        va.verify_attn_split(plan, qd, kc, vc, ws)
+
+    fused, unfused = _both(plan, qd, kn, vn, k.to(DEV), v.to(DEV), ref, s.to(DEV))
+    name = f"append linear fp={fp} rows={rows} live={live} D={D}"
+    _same(fused, unfused, live, name)
+    assert torch.equal(fused[3][:, fp:fp + rows].view(torch.int16),
+                       k_new.permute(1, 0, 2).contiguous().view(torch.int16)), f"{name}: stored K"
+    if live:
+        kf = k.clone()
+        vf = v.clone()
+        kf[:, fp:fp + rows] = k_new.permute(1, 0, 2)
+        vf[:, fp:fp + rows] = v_new.permute(1, 0, 2)
+        hi = fp + live
+        p = Problem("causal", rows, live, first_pos=fp)
+        ro, rl = oattn.verify_attn_ref(p, f64(q), oattn.Cache(f64(kf[:, :hi]), f64(vf[:, :hi])),
+                                       plan.problem.scale, f64(s))
+        check(fused[1], fused[2], ro, rl, live, name)
+
+
+def test_append_refused():
+    g = synth.gen(13999)
+    q = synth.normal_bf16((8, 6, 128), g).to(DEV)
+    kn = synth.normal_bf16((8, 1, 128), g).to(DEV)
+    k = torch.zeros((1, 600, 128), dtype=torch.bfloat16, device=DEV)
+    tree = plan_for(8, 8, 6, 1, 128, "tree", prefix_len=500, parent=[-1] * 8, kv_capacity=600)
+    with pytest.raises(va.VAError):
+        va.verify_attn_split_append(tree, q, kn, kn, k, k.clone(), va.workspace_for(tree, DEV))
+    # capacity 506 holds the live rows' keys (hi = 504) but not all 8 rows:
+    # refused by the library (the tensor is longer than the plan's capacity)
+    # and by the binding (a tensor too short for the rows)
+    short = plan_for(8, 4, 6, 1, 128, "causal", first_pos=500, kv_capacity=506)
+    with pytest.raises(va.VAError):
+        va.verify_attn_split_append(short, q, kn, kn, k, k.clone(), va.workspace_for(short, DEV))
+    ks = torch.zeros((1, 506, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        va.verify_attn_split_append(short, q, kn, kn, ks, ks.clone(), va.workspace_for(short, DEV))
+    torch.cuda.synchronize()
