@@ -527,7 +527,12 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
               32K prefix, no sink;
       tree-q  the same tree over a 64K prefix, keys E4M3 after the rotation,
               values INT8 with an FP32 scale per (token, head).
-    KV bytes are the algorithmic read (visible keys once per KV head)."""
+    KV bytes are the algorithmic read (visible keys once per KV head).
+    Window and bf16 tree calls are also timed with the rows' KV write inside
+    the split launch (verify_attn_split_append: us_per_call_append_fused),
+    and tree calls with the write as a launch of its own
+    (us_per_call_with_kv_write); the tree's plain call reads a cache that
+    already holds the node keys."""
     out = []
     g = synth.gen(9500)
     cases = []
@@ -586,27 +591,31 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
         o = torch.empty((rows, hq, d), dtype=torch.float32, device=dev)
         lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
 
-        def one(i, split_only=False, fused=False):
+        def one(i, split_only=False, fused=False, write=False):
             k, v, vs = reps_kv[i % nrep]
-            if fused:  # the ring write inside the split launch
+            if fused:  # the rows' KV write inside the split launch
                 va.verify_attn_split_append(plan, q, k_new, v_new, k, v, ws, stream=cur())
             else:
                 if kind == "window" and not split_only:
                     va.swa_ring_write(k_new, v_new, pos, k, v, stream=cur())
+                if write:  # the tree's node keys written first, a launch of their own
+                    va.verify_kv_write(k_new, v_new, pos, k, v, stream=cur())
                 va.verify_attn_split(plan, q, k, v, ws, v_scale=vs, stream=cur())
             if not split_only:
                 va.verify_attn_combine(plan, ws, o, lse=lse, sink=sink, stream=cur())
         times = {}
-        passes = [("call", False, False), ("split", True, False)]
-        if kind == "window":
-            passes.append(("fused", False, True))
-        for label, so, fu in passes:
+        passes = [("call", False, False, False), ("split", True, False, False)]
+        if kind == "tree":
+            passes.append(("write_call", False, False, True))
+        if kind in ("window", "tree"):
+            passes.append(("fused", False, True, False))
+        for label, so, fu, wr in passes:
             for i in range(2):
-                one(i, so, fu)
+                one(i, so, fu, wr)
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for i in range(reps):
-                    one(i, so, fu)
+                    one(i, so, fu, wr)
             gr.replay()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -616,7 +625,9 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
             times[label] = a.elapsed_time(b) * 1e3 / reps
             del gr
         extra = {}
-        if "fused" in times:  # verify_attn_split_append + combine: two launches, not three
+        if "write_call" in times:  # verify_kv_write + split + combine
+            extra["us_per_call_with_kv_write"] = round(times["write_call"], 2)
+        if "fused" in times:  # verify_attn_split_append + combine: the KV write inside the split launch
             extra["us_per_call_append_fused"] = round(times["fused"], 2)
         out.append({"config": kind, "position": pos, "splits": plan.splits, "kv_bytes": kv_bytes,
                     "us_per_call": round(times["call"], 2), **extra, "split_us": round(times["split"], 2),

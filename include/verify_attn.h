@@ -191,21 +191,22 @@ va_status verify_attn_combine(const va_plan *plan, const void *workspace, size_t
  * right before the read (IQuestRT report, "IQuestRT execution": row 0's KV
  * is written before the attention that reads it; "Read only the KV tiles
  * needed by the current positions" and "Let correctness checks change the
- * design" for the ring).  bf16 caches in causal or window mode; static
- * plans only.
+ * design" for the ring; 4090 post, "More tokens per round: verify trees" for
+ * the tree's node keys).  bf16 caches; static plans only.
  *   k_new, v_new  [rows, Hkv, D] bf16, contiguous, 16-byte aligned: every
  *                 row, padding included, is stored to slot (first_pos + r)
- *                 mod ring_slots (ring) or first_pos + r (linear cache),
- *                 exactly as swa_ring_write / verify_kv_write would.
+ *                 mod ring_slots (ring), first_pos + r (linear cache) or
+ *                 prefix_len + r (tree), exactly as swa_ring_write /
+ *                 verify_kv_write would.
  *   the rest as verify_attn_split; k and v are written.
  * The partials equal those of swa_ring_write (or verify_kv_write) followed by
  * verify_attn_split on the same stream: the live rows' keys and values are
  * taken from k_new / v_new for the split's own read, so no workgroup
  * depends on another's cache store.  The window ring's size guarantees that
  * no stored slot holds a key any row still sees.
- * Errors: as verify_attn_split, plus VA_ERR_UNSUPPORTED (tree mode or a
- * quantised cache), VA_ERR_INVALID (NULL or misaligned k_new / v_new) and
- * VA_ERR_CAPACITY (linear cache with first_pos + rows > kv_capacity). */
+ * Errors: as verify_attn_split, plus VA_ERR_UNSUPPORTED (a quantised cache),
+ * VA_ERR_INVALID (NULL or misaligned k_new / v_new) and VA_ERR_CAPACITY
+ * (linear cache or tree with the rows' last slot at or past kv_capacity). */
 va_status verify_attn_split_append(const va_plan *plan, const void *q, const void *k_new, const void *v_new,
                                    void *k, void *v, int64_t kv_head_stride, int64_t kv_row_stride,
                                    void *workspace, size_t workspace_bytes, hipStream_t stream);

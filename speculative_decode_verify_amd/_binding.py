@@ -284,8 +284,9 @@ def verify_attn_split_append(plan, q, k_new, v_new, k, v, workspace, stream=None
     if not (k_new.is_contiguous() and v_new.is_contiguous()) or tuple(k_new.shape) != shape or \
             tuple(v_new.shape) != shape:
         raise ValueError(f"k_new/v_new must be contiguous {list(shape)} bfloat16")
-    if not plan.problem.ring_slots and k.shape[1] < plan.problem.first_pos + plan.rows:
-        raise ValueError(f"k/v must hold the {plan.rows} rows' slots from {plan.problem.first_pos}")
+    first = plan.problem.prefix_len if plan.problem.mask == MASKS["tree"] else plan.problem.first_pos
+    if not plan.problem.ring_slots and k.shape[1] < first + plan.rows:
+        raise ValueError(f"k/v must hold the {plan.rows} rows' slots from {first}")
     qp, kp, vp, _, _, hs, rs, wp, wb = _split_args(plan, q, k, v, workspace, None)
     _check("verify_attn_split_append", _lib().verify_attn_split_append(
         ctypes.byref(plan.plan), qp, _ptr(k_new), _ptr(v_new), kp, vp, hs, rs, wp, wb, _stream(stream)))

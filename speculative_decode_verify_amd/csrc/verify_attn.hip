@@ -88,8 +88,8 @@ struct SplitArgs {
   // above that depend on positions or rows are then derived from it.
   const va_state *state;
   int64_t bucket_hi;  // the plan's extent end: no state may read beyond it
-  // Append (bf16, chain modes, static plans): the rows' own K/V, [rows, Hkv,
-  // D] bf16 with new_row_stride_b bytes between rows (NULL: no append).
+  // Append (bf16, static plans): the rows' own K/V, [rows, Hkv, D] bf16 with
+  // new_row_stride_b bytes between rows (NULL: no append).
   // Split 0 stores all rows to slots (append_slot0 + r) mod ring_slots, or
   // append_slot0 + r for a linear cache; the workgroups whose chunks hold
   // the live rows' positions put the new rows into their staged tiles.
@@ -523,14 +523,17 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
       }
       // the new live rows of chunk n into its staged tile (after its DMA
       // landed, before the barrier that publishes it)
+      // relative key of row 0's own key: chain rows at t0_rel + r, tree
+      // nodes at tree_lo + r
+      const int32_t new0 = tree ? tree_lo : t0_rel;
       auto overlay = [&](int32_t n) {
         const int32_t c0 = (c_first + n) * kChunk;
-        if (t0_rel >= c0 + kChunk || t0_rel + live_rows <= c0) return;
+        if (new0 >= c0 + kChunk || new0 + live_rows <= c0) return;
         uint8_t *tile = smem + (n % NST) * kStageB + (PW == 0 ? 0 : kTileB);
 #pragma unroll
         for (int i = 0; i < APASS; ++i) {
           const int rr = (64 * i + lane) / PIECES;
-          const int j = t0_rel + rr - c0;
+          const int j = new0 + rr - c0;
           if (rr < live_rows && j >= 0 && j < kChunk) {
             const int f = PW == 0 ? (j & (PIECES - 1)) : ((2 * j) & (PIECES - 2));
             *(u32x4 *)(tile + j * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
@@ -1319,7 +1322,9 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
     a.k_new = (const uint8_t *)k_new;
     a.v_new = (const uint8_t *)v_new;
     a.new_row_stride_b = (int64_t)d->kv_heads * d->head_dim * 2;
-    a.append_slot0 = d->ring_slots ? d->first_pos % d->ring_slots : d->first_pos;
+    a.append_slot0 = d->mask == VA_MASK_TREE ? d->prefix_len
+                     : d->ring_slots      ? d->first_pos % d->ring_slots
+                                          : d->first_pos;
   }
   const int nb_total = (d->matrix_rows + 15) / 16;
   hipError_t e;
@@ -1383,9 +1388,10 @@ extern "C" va_status verify_attn_split_append(const va_plan *plan, const void *q
                                               hipStream_t stream) {
   const va_plan_data *d = plan_of(plan);
   if (!d) return VA_ERR_INVALID;
-  if (d->mask == VA_MASK_TREE || d->kv_fmt != VA_KV_BF16) return VA_ERR_UNSUPPORTED;
+  if (d->kv_fmt != VA_KV_BF16) return VA_ERR_UNSUPPORTED;
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return VA_ERR_INVALID;
-  if (!d->ring_slots && d->first_pos + d->rows > d->kv_capacity) return VA_ERR_CAPACITY;
+  const int64_t first = d->mask == VA_MASK_TREE ? d->prefix_len : d->first_pos;
+  if (!d->ring_slots && first + d->rows > d->kv_capacity) return VA_ERR_CAPACITY;
   return split_impl(plan, nullptr, q, k, v, nullptr, 0, kv_head_stride, kv_row_stride, workspace, workspace_bytes,
                     stream, k_new, v_new);
 }

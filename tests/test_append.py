@@ -10,8 +10,10 @@ Gates:
 * the new rows straddling a 32-key chunk boundary and a split boundary
   (two workgroups put rows into their tiles), no live row (the rows are
   stored, nothing read), 16 rows at D 128;
-* tree mode and quantised caches are refused; a linear cache too short for
-  the rows is refused before any launch.
+* tree mode: the node keys at prefix_len + i, a random tree, one case
+  straddling a chunk boundary;
+* quantised caches are refused; a linear cache too short for the rows is
+  refused before any launch.
 The stale contents of the slots the rows take are scaled by 100, so a key
 read from memory instead of from the new rows would show.
 """
@@ -157,14 +159,50 @@ def test_append_linear(rows, live, Hq, Hkv, D, fp, splits):
         check(fused[1], fused[2], ro, rl, live, name)
 
 
+@pytest.mark.parametrize("P,live,Hq,Hkv,splits", [(2048, 16, 24, 4, 0), (700, 11, 6, 1, 0), (700, 16, 6, 1, 22)])
+def test_append_tree(P, live, Hq, Hkv, splits):
+    rows, D = 16, 128
+    g = synth.gen(14000 + P + live)
+    parent = synth.random_tree(rows, g)
+    cap = P + rows + 40
+    k = synth.normal_bf16((Hkv, cap, D), g)
+    v = synth.normal_bf16((Hkv, cap, D), g)
+    k_new = synth.normal_bf16((rows, Hkv, D), g)
+    v_new = synth.normal_bf16((rows, Hkv, D), g)
+    k[:, P:P + rows] = k_new.permute(1, 0, 2) * 100   # stale, loud
+    v[:, P:P + rows] = v_new.permute(1, 0, 2) * 100
+    k[:, P + rows:] = NAN
+    v[:, P + rows:] = NAN
+    q = synth.normal_bf16((rows, Hq, D), g)
+    plan = plan_for(rows, live, Hq, Hkv, D, "tree", prefix_len=P, parent=parent, kv_capacity=cap,
+                    scale=1 / math.sqrt(D), splits=splits)
+    qd, kn, vn = q.to(DEV), k_new.to(DEV), v_new.to(DEV)
+
+    def ref(kc, vc, ws):
+        va.verify_kv_write(kn, vn, P, kc, vc)
+        va.verify_attn_split(plan, qd, kc, vc, ws)
+
+    fused, unfused = _both(plan, qd, kn, vn, k.to(DEV), v.to(DEV), ref, None)
+    name = f"append tree P={P} live={live} Hkv={Hkv}"
+    _same(fused, unfused, live, name)
+    kf, vf = k.clone(), v.clone()
+    kf[:, P:P + rows] = k_new.permute(1, 0, 2)
+    vf[:, P:P + rows] = v_new.permute(1, 0, 2)
+    hi = P + live
+    p = Problem("tree", rows, live, prefix_len=P, parent=parent)
+    ro, rl = oattn.verify_attn_ref(p, f64(q), oattn.Cache(f64(kf[:, :hi]), f64(vf[:, :hi])), plan.problem.scale,
+                                   None)
+    check(fused[1], fused[2], ro, rl, live, name)
+
+
 def test_append_refused():
     g = synth.gen(13999)
     q = synth.normal_bf16((8, 6, 128), g).to(DEV)
     kn = synth.normal_bf16((8, 1, 128), g).to(DEV)
     k = torch.zeros((1, 600, 128), dtype=torch.bfloat16, device=DEV)
-    tree = plan_for(8, 8, 6, 1, 128, "tree", prefix_len=500, parent=[-1] * 8, kv_capacity=600)
-    with pytest.raises(va.VAError):
-        va.verify_attn_split_append(tree, q, kn, kn, k, k.clone(), va.workspace_for(tree, DEV))
+    quant = plan_for(8, 8, 6, 1, 128, "causal", kv_fmt="e4m3_wht_i8", first_pos=500, kv_capacity=600)
+    with pytest.raises((va.VAError, ValueError, TypeError)):
+        va.verify_attn_split_append(quant, q, kn, kn, k, k.clone(), va.workspace_for(quant, DEV))
     # capacity 506 holds the live rows' keys (hi = 504) but not all 8 rows:
     # refused by the library (the tensor is longer than the plan's capacity)
     # and by the binding (a tensor too short for the rows)
