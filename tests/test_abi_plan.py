@@ -119,6 +119,30 @@ def test_query_rejects_garbage_plan():
     assert lib.verify_attn_plan_query(ctypes.byref(plan), ctypes.byref(info)) == 1
 
 
+def test_append_refusals_before_any_launch():
+    """verify_attn_split_append checks its plan and buffers on the host: a
+    quantised cache is unsupported, missing new rows are invalid, and a
+    linear cache (or tree) without room for every row is a capacity error;
+    none of these reaches the GPU."""
+    lib = va.load_library()
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every case fails before use
+
+    def call(plan, k_new=fake):
+        return lib.verify_attn_split_append(ctypes.byref(plan.plan), fake, k_new, fake, fake, fake, 0, 128,
+                                            fake, plan.workspace_bytes, None)
+
+    quant = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, kv_fmt="e4m3_wht_i8",
+                    first_pos=500, kv_capacity=600)
+    assert call(quant) == 2
+    ok = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, first_pos=500, kv_capacity=600)
+    assert call(ok, k_new=None) == 1
+    short = va.Plan(rows=8, live_rows=4, q_heads=6, kv_heads=1, head_dim=128, first_pos=500, kv_capacity=506)
+    assert call(short) == 3
+    tree = va.Plan(rows=16, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, mask="tree", prefix_len=500,
+                   parent=[-1] * 16, kv_capacity=510)
+    assert call(tree) == 3
+
+
 def _oracle_problem(kw):
     return Problem(kw.get("mask", "causal"), kw["rows"], kw["live_rows"], first_pos=kw.get("first_pos", 0),
                    prefix_len=kw.get("prefix_len", 0), parent=kw.get("parent"), window=kw.get("window", 0),
