@@ -250,6 +250,19 @@ va_status verify_attn_split_state(const va_plan *plan, const va_state *state, co
 va_status verify_attn_combine_state(const va_plan *plan, const va_state *state, const void *workspace,
                                     size_t workspace_bytes, const float *sink, float *out, float *lse,
                                     hipStream_t stream);
+/* verify_attn_split_append with the per-call state read from device memory,
+ * as verify_attn_split_state: the rows' own K/V stored (and read) in the
+ * split launch of a device-driven step, so a captured step of one bucket
+ * needs two launches.  Row r is stored to the slot of its own key under the
+ * state's positions; in a linear cache, rows whose slot would be at or past
+ * kv_capacity (padding rows of a state near the end of the bucket) are not
+ * stored.  A state outside the bucket stores nothing.
+ * Errors: as verify_attn_split_state and verify_attn_split_append (no host
+ * capacity check: the state is on the device). */
+va_status verify_attn_split_append_state(const va_plan *plan, const va_state *state, const void *q,
+                                         const void *k_new, const void *v_new, void *k, void *v,
+                                         int64_t kv_head_stride, int64_t kv_row_stride, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /* Store the verification rows' own K/V into the sliding-window ring before
  * the read (IQuestRT report, "Read only the KV tiles needed by the current

@@ -94,6 +94,7 @@ def load_library():
     lib.verify_attn_split_state.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, I64, V, SZ, V]
     lib.verify_attn_combine_state.argtypes = [ctypes.POINTER(va_plan), V, V, SZ, V, V, V, V]
     lib.verify_attn_split_append.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, V, SZ, V]
+    lib.verify_attn_split_append_state.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, V, I64, I64, V, SZ, V]
     lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
     lib.verify_kv_write.argtypes = [V, V, I32, I64, I32, I32, I32, V, V, V, I64, I64, I32, I64, I64, V]
     SP = ctypes.POINTER(va_sample_params)
@@ -107,6 +108,7 @@ def load_library():
     lib.va_status_string.restype = ctypes.c_char_p
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
                "verify_attn_split", "verify_attn_combine", "verify_attn_split_state", "verify_attn_split_append",
+               "verify_attn_split_append_state",
                "verify_attn_combine_state", "swa_ring_write", "verify_kv_write", "va_sample", "va_accept",
                "va_sample_accept", "va_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -274,9 +276,7 @@ def verify_attn_split(plan, q, k, v, workspace, v_scale=None, stream=None):
         ctypes.byref(plan.plan), *_split_args(plan, q, k, v, workspace, v_scale), _stream(stream)))
 
 
-def verify_attn_split_append(plan, q, k_new, v_new, k, v, workspace, stream=None):
-    """verify_attn_split that also stores the rows' own K/V (k_new, v_new
-    [rows, Hkv, D] bf16 contiguous) into the cache k, v in the same launch."""
+def _append_rows(plan, k_new, v_new):
     import torch
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _require(t, n, (torch.bfloat16,))
@@ -284,12 +284,31 @@ def verify_attn_split_append(plan, q, k_new, v_new, k, v, workspace, stream=None
     if not (k_new.is_contiguous() and v_new.is_contiguous()) or tuple(k_new.shape) != shape or \
             tuple(v_new.shape) != shape:
         raise ValueError(f"k_new/v_new must be contiguous {list(shape)} bfloat16")
+
+
+def verify_attn_split_append(plan, q, k_new, v_new, k, v, workspace, stream=None):
+    """verify_attn_split that also stores the rows' own K/V (k_new, v_new
+    [rows, Hkv, D] bf16 contiguous) into the cache k, v in the same launch."""
+    _append_rows(plan, k_new, v_new)
     first = plan.problem.prefix_len if plan.problem.mask == MASKS["tree"] else plan.problem.first_pos
     if not plan.problem.ring_slots and k.shape[1] < first + plan.rows:
         raise ValueError(f"k/v must hold the {plan.rows} rows' slots from {first}")
     qp, kp, vp, _, _, hs, rs, wp, wb = _split_args(plan, q, k, v, workspace, None)
     _check("verify_attn_split_append", _lib().verify_attn_split_append(
         ctypes.byref(plan.plan), qp, _ptr(k_new), _ptr(v_new), kp, vp, hs, rs, wp, wb, _stream(stream)))
+
+
+def verify_attn_split_append_state(plan, state, q, k_new, v_new, k, v, workspace, stream=None):
+    """verify_attn_split_append with positions, live rows and tree read on the
+    device from `state`; a linear cache must hold kv_capacity slots."""
+    _require_state(state)
+    _append_rows(plan, k_new, v_new)
+    if not plan.problem.ring_slots and k.shape[1] < plan.problem.kv_capacity:
+        raise ValueError(f"k/v must hold the plan's {plan.problem.kv_capacity} slots")
+    qp, kp, vp, _, _, hs, rs, wp, wb = _split_args(plan, q, k, v, workspace, None)
+    _check("verify_attn_split_append_state", _lib().verify_attn_split_append_state(
+        ctypes.byref(plan.plan), _ptr(state), qp, _ptr(k_new), _ptr(v_new), kp, vp, hs, rs, wp, wb,
+        _stream(stream)))
 
 
 def verify_attn_split_state(plan, state, q, k, v, workspace, v_scale=None, stream=None):

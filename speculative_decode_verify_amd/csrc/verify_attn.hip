@@ -88,14 +88,14 @@ struct SplitArgs {
   // above that depend on positions or rows are then derived from it.
   const va_state *state;
   int64_t bucket_hi;  // the plan's extent end: no state may read beyond it
-  // Append (bf16, static plans): the rows' own K/V, [rows, Hkv, D] bf16 with
-  // new_row_stride_b bytes between rows (NULL: no append).
-  // Split 0 stores all rows to slots (append_slot0 + r) mod ring_slots, or
-  // append_slot0 + r for a linear cache; the workgroups whose chunks hold
-  // the live rows' positions put the new rows into their staged tiles.
+  // Append (bf16): the rows' own K/V, [rows, Hkv, D] bf16 with
+  // new_row_stride_b bytes between rows (NULL: no append).  Split 0 stores
+  // every row to the slot of its own key (ring: mod ring_slots; a linear
+  // cache: below kv_capacity only); the workgroups whose chunks hold the
+  // live rows' keys put the new rows into their staged tiles.
   const uint8_t *k_new, *v_new;
   int64_t new_row_stride_b;
-  int64_t append_slot0;
+  int64_t kv_capacity;
 };
 
 struct CombineArgs {
@@ -315,7 +315,7 @@ __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); 
 
 template <int D, int W, int FMT, int NST, int NPW, bool STATE, bool APP>
 __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_kernel(const SplitArgs a) {
-  static_assert(!APP || (FMT == 0 && NPW == 2 && !STATE), "append: bf16 tiles, one producer per tile kind");
+  static_assert(!APP || (FMT == 0 && NPW == 2), "append: bf16 tiles, one producer per tile kind");
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
   constexpr int MD = D / 16;  // O^T row blocks over d
@@ -615,12 +615,12 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
 #pragma unroll
         for (int i = 0; i < APASS; ++i) {
           const int rr = (64 * i + lane) / PIECES;
-          if (rr < a.rows) {
-            const int64_t slot =
-                ring_slots ? (int64_t)(((uint64_t)a.append_slot0 + (uint64_t)rr) % (uint64_t)ring_slots)
-                           : a.append_slot0 + rr;
-            *(u32x4 *)(dst + slot * row_stride) = nrow[i];
-          }
+          // row rr's key: relative new0 + rr, absolute kv_base + new0 + rr
+          // (ring_base + new0 + rr < 2^32: both terms are below 2^31)
+          const int64_t slot = ring_slots ? (int64_t)(((uint32_t)ring_base + (uint32_t)(new0 + rr)) %
+                                                      (uint32_t)ring_slots)
+                                          : kv_base + new0 + rr;
+          if (rr < a.rows && (ring_slots || slot < a.kv_capacity)) *(u32x4 *)(dst + slot * row_stride) = nrow[i];
         }
       }
     };
@@ -1322,13 +1322,14 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
     a.k_new = (const uint8_t *)k_new;
     a.v_new = (const uint8_t *)v_new;
     a.new_row_stride_b = (int64_t)d->kv_heads * d->head_dim * 2;
-    a.append_slot0 = d->mask == VA_MASK_TREE ? d->prefix_len
-                     : d->ring_slots      ? d->first_pos % d->ring_slots
-                                          : d->first_pos;
+    a.kv_capacity = d->kv_capacity;
   }
   const int nb_total = (d->matrix_rows + 15) / 16;
   hipError_t e;
-  if (k_new) {  // bf16 and static only (checked by the entry point)
+  if (k_new && state) {  // bf16 only (checked by the entry points)
+    e = d->head_dim == 64 ? dispatch_rows<64, 0, true, true>(a, nb_total, stream)
+                          : dispatch_rows<128, 0, true, true>(a, nb_total, stream);
+  } else if (k_new) {
     e = d->head_dim == 64 ? dispatch_rows<64, 0, false, true>(a, nb_total, stream)
                           : dispatch_rows<128, 0, false, true>(a, nb_total, stream);
   } else {
@@ -1393,6 +1394,19 @@ extern "C" va_status verify_attn_split_append(const va_plan *plan, const void *q
   const int64_t first = d->mask == VA_MASK_TREE ? d->prefix_len : d->first_pos;
   if (!d->ring_slots && first + d->rows > d->kv_capacity) return VA_ERR_CAPACITY;
   return split_impl(plan, nullptr, q, k, v, nullptr, 0, kv_head_stride, kv_row_stride, workspace, workspace_bytes,
+                    stream, k_new, v_new);
+}
+
+extern "C" va_status verify_attn_split_append_state(const va_plan *plan, const va_state *state, const void *q,
+                                                    const void *k_new, const void *v_new, void *k, void *v,
+                                                    int64_t kv_head_stride, int64_t kv_row_stride,
+                                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const va_plan_data *d = plan_of(plan);
+  if (!d) return VA_ERR_INVALID;
+  if (!state || !aligned8(state)) return VA_ERR_INVALID;
+  if (d->kv_fmt != VA_KV_BF16) return VA_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return VA_ERR_INVALID;
+  return split_impl(plan, state, q, k, v, nullptr, 0, kv_head_stride, kv_row_stride, workspace, workspace_bytes,
                     stream, k_new, v_new);
 }
 

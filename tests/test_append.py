@@ -12,6 +12,8 @@ Gates:
   stored, nothing read), 16 rows at D 128;
 * tree mode: the node keys at prefix_len + i, a random tree, one case
   straddling a chunk boundary;
+* the device-state variant under one bucket: partials and cache contents
+  equal to the static append of the state's own problem;
 * quantised caches are refused; a linear cache too short for the rows is
   refused before any launch.
 The stale contents of the slots the rows take are scaled by 100, so a key
@@ -193,6 +195,70 @@ def test_append_tree(P, live, Hq, Hkv, splits):
     ro, rl = oattn.verify_attn_ref(p, f64(q), oattn.Cache(f64(kf[:, :hi]), f64(vf[:, :hi])), plan.problem.scale,
                                    None)
     check(fused[1], fused[2], ro, rl, live, name)
+
+
+@pytest.mark.parametrize("mode,pos,live", [("causal", 20000, 8), ("causal", 4093, 8), ("causal", 19990, 5),
+                                           ("causal", 100, 0), ("window", 51200, 5), ("window", 5120, 8),
+                                           ("tree", 700, 11), ("tree", 2048, 16)])
+def test_append_state_matches_static(mode, pos, live):
+    """verify_attn_split_append_state under one bucket against
+    verify_attn_split_append of the state's own problem with the state's
+    split count (the bucket's, at most one granule each): the same partials
+    bit for bit, the same cache contents, outputs equal up to the combine's
+    FP32 order."""
+    g = synth.gen(15000 + pos + live)
+    Hq, Hkv = 6, 1
+    if mode == "window":
+        rows, D, W, C = 8, 64, 4096, 4160
+        bucket_kw = dict(mask="window", first_pos=51200, window=W, ring_slots=C)
+        state_kw = dict(mask="window", first_pos=pos, window=W, ring_slots=C)
+        slots = C
+        st = va.pack_state(first_pos=pos, live_rows=live)
+    elif mode == "tree":
+        rows, D = 16, 128
+        parent = synth.random_tree(rows, g)
+        slots = 2048 + rows + 64
+        bucket_kw = dict(mask="tree", prefix_len=2048, parent=synth.random_tree(rows, g), kv_capacity=slots)
+        state_kw = dict(mask="tree", prefix_len=pos, parent=parent, kv_capacity=slots)
+        st = va.pack_state(prefix_len=pos, live_rows=live, parent=parent)
+    else:
+        rows, D = 8, 128
+        slots = 20000 + rows + 64
+        bucket_kw = dict(mask="causal", first_pos=20000, kv_capacity=slots)
+        state_kw = dict(mask="causal", first_pos=pos, kv_capacity=slots)
+        st = va.pack_state(first_pos=pos, live_rows=live)
+    bucket = plan_for(rows, rows, Hq, Hkv, D, scale=1 / math.sqrt(D), **bucket_kw)
+    own = plan_for(rows, live, Hq, Hkv, D, scale=1 / math.sqrt(D), **state_kw)
+    S_eff = max(1, min(bucket.splits, own.info["chunks"]))
+    stat = plan_for(rows, live, Hq, Hkv, D, scale=1 / math.sqrt(D), splits=S_eff, **state_kw)
+    k = synth.normal_bf16((Hkv, slots, D), g).to(DEV)
+    v = synth.normal_bf16((Hkv, slots, D), g).to(DEV)
+    kn = synth.normal_bf16((rows, Hkv, D), g).to(DEV)
+    vn = synth.normal_bf16((rows, Hkv, D), g).to(DEV)
+    q = synth.normal_bf16((rows, Hq, D), g).to(DEV)
+    sink = synth.normal_f32((Hq,), g).to(DEV)
+    std = st.to(DEV)
+    name = f"append state {mode} pos={pos} live={live}"
+    ks, vs_ = k.clone(), v.clone()
+    ws_s = _ws(bucket)
+    out_s = torch.full((rows, Hq, D), NAN, dtype=torch.float32, device=DEV)
+    va.verify_attn_split_append_state(bucket, std, q, kn, vn, ks, vs_, ws_s)
+    va.verify_attn_combine_state(bucket, std, ws_s, out_s, sink=sink)
+    kt, vt = k.clone(), v.clone()
+    ws_t = _ws(stat)
+    out_t = torch.full((rows, Hq, D), NAN, dtype=torch.float32, device=DEV)
+    va.verify_attn_split_append(stat, q, kn, vn, kt, vt, ws_t)
+    va.verify_attn_combine(stat, ws_t, out_t, sink=sink)
+    torch.cuda.synchronize()
+    ms, ls, Os = partials(bucket, ws_s.cpu())
+    mt, lt, Ot = partials(stat, ws_t.cpu())
+    for a, b, what in ((ms, mt, "m"), (ls, lt, "l"), (Os, Ot, "O")):
+        assert np.array_equal(a[:S_eff, :live], b[:, :live], equal_nan=True), f"{name}: {what} partials differ"
+    assert torch.equal(ks.view(torch.int16), kt.view(torch.int16)), f"{name}: K cache differs"
+    assert torch.equal(vs_.view(torch.int16), vt.view(torch.int16)), f"{name}: V cache differs"
+    o, ot = out_s.cpu()[:live].double().numpy(), out_t.cpu()[:live].double().numpy()
+    assert np.allclose(o, ot, rtol=1e-5, atol=1e-6), f"{name}: out differs"
+    assert torch.all(out_s.cpu()[live:] == 0), f"{name}: padding rows"
 
 
 def test_append_refused():
