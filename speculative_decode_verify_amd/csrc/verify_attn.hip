@@ -96,6 +96,7 @@ struct SplitArgs {
   const uint8_t *k_new, *v_new;
   int64_t new_row_stride_b;
   int64_t kv_capacity;
+  int64_t append_pos0;  // absolute position of row 0's key (first_pos, or prefix_len for a tree)
 };
 
 struct CombineArgs {
@@ -115,6 +116,7 @@ struct CombineArgs {
 // ancestor bits) and the split kernel's relative coordinates.
 struct StateGeo {
   int64_t base;
+  int64_t pos0;  // absolute position of row 0's key (first_pos, or prefix_len for a tree)
   int32_t rel_lo, rel_hi, full_lo, full_hi, cq, cr, splits, live_rows, ring_base, t0_rel, tree_lo;
   uint32_t anc[VA_MAX_ROWS];
   bool valid;
@@ -180,6 +182,7 @@ __device__ __forceinline__ StateGeo geo_from_state(const va_state *stp, int32_t 
   g.t0_rel = tree ? 0 : (int32_t)(fp - g.base);
   // tree: base is 0 and P < hi <= the bucket's hi < 2^31; unused otherwise
   g.tree_lo = tree ? (int32_t)P : 0;
+  g.pos0 = tree ? P : fp;
   g.live_rows = live;
 #pragma unroll
   for (int i = 0; i < VA_MAX_ROWS; ++i) g.anc[i] = anc[i];
@@ -351,6 +354,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
   const int32_t ring_slots = a.ring_slots;
   int32_t ring_base = a.ring_base_slot;
   int64_t kv_base = a.base;
+  int64_t append_pos0 = a.append_pos0;
   const int64_t row_stride = a.kv_row_stride_b, head_stride = a.kv_head_stride_b;
   const uint8_t *kptr = a.k, *vptr = a.v;
   const float *vsc = a.v_scale;
@@ -373,6 +377,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
     // the bucket, read nothing (uniform over the workgroup, before any barrier)
     if (!g.valid || split >= g.splits) return;
     cq = g.cq, cr = g.cr, rel_lo = g.rel_lo, rel_hi = g.rel_hi, ring_base = g.ring_base, kv_base = g.base;
+    append_pos0 = g.pos0;
     live_rows = g.live_rows, tree_lo = g.tree_lo, t0_rel = g.t0_rel, full_lo = g.full_lo, full_hi = g.full_hi;
 #pragma unroll
     for (int i = 0; i < VA_MAX_ROWS; ++i) anc[i] = g.anc[i];
@@ -615,11 +620,11 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
 #pragma unroll
         for (int i = 0; i < APASS; ++i) {
           const int rr = (64 * i + lane) / PIECES;
-          // row rr's key: relative new0 + rr, absolute kv_base + new0 + rr
-          // (ring_base + new0 + rr < 2^32: both terms are below 2^31)
-          const int64_t slot = ring_slots ? (int64_t)(((uint32_t)ring_base + (uint32_t)(new0 + rr)) %
-                                                      (uint32_t)ring_slots)
-                                          : kv_base + new0 + rr;
+          // from the absolute position (64-bit: a state without live rows
+          // may sit anywhere in [0, 2^61], where the relative coordinates
+          // do not reach); positions are never negative
+          const int64_t p = append_pos0 + rr;
+          const int64_t slot = ring_slots ? (int64_t)((uint64_t)p % (uint64_t)ring_slots) : p;
           if (rr < a.rows && (ring_slots || slot < a.kv_capacity)) *(u32x4 *)(dst + slot * row_stride) = nrow[i];
         }
       }
@@ -1323,6 +1328,7 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
     a.v_new = (const uint8_t *)v_new;
     a.new_row_stride_b = (int64_t)d->kv_heads * d->head_dim * 2;
     a.kv_capacity = d->kv_capacity;
+    a.append_pos0 = d->mask == VA_MASK_TREE ? d->prefix_len : d->first_pos;
   }
   const int nb_total = (d->matrix_rows + 15) / 16;
   hipError_t e;

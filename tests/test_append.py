@@ -261,6 +261,45 @@ def test_append_state_matches_static(mode, pos, live):
     assert torch.all(out_s.cpu()[live:] == 0), f"{name}: padding rows"
 
 
+@pytest.mark.parametrize("mode", ["causal", "window"])
+def test_append_state_without_live_rows_far_away(mode):
+    """A state with no live rows is valid at any position up to 2^61.  Its
+    rows go to the slots of their own keys: none in a linear cache far
+    shorter than the position (nothing stored, nothing read), slot
+    (pos + r) mod C in a ring."""
+    g = synth.gen(15999)
+    rows, Hq, Hkv = 8, 6, 1
+    pos = 3_000_000_123
+    if mode == "window":
+        D, W, C = 64, 4096, 4160
+        bucket = plan_for(rows, rows, Hq, Hkv, D, "window", first_pos=51200, window=W, ring_slots=C)
+        slots = C
+    else:
+        D = 128
+        slots = 20000 + rows + 64
+        bucket = plan_for(rows, rows, Hq, Hkv, D, "causal", first_pos=20000, kv_capacity=slots)
+    k = synth.normal_bf16((Hkv, slots, D), g).to(DEV)
+    v = synth.normal_bf16((Hkv, slots, D), g).to(DEV)
+    kn = synth.normal_bf16((rows, Hkv, D), g).to(DEV)
+    vn = synth.normal_bf16((rows, Hkv, D), g).to(DEV)
+    q = synth.normal_bf16((rows, Hq, D), g).to(DEV)
+    st = va.pack_state(first_pos=pos, live_rows=0).to(DEV)
+    ks, vs_ = k.clone(), v.clone()
+    ws = _ws(bucket)
+    out = torch.full((rows, Hq, D), NAN, dtype=torch.float32, device=DEV)
+    va.verify_attn_split_append_state(bucket, st, q, kn, vn, ks, vs_, ws)
+    va.verify_attn_combine_state(bucket, st, ws, out)
+    torch.cuda.synchronize()
+    assert torch.all(out.cpu() == 0)
+    ek, ev = k.clone(), v.clone()
+    if mode == "window":
+        for r in range(rows):
+            ek[:, (pos + r) % C] = kn[r]
+            ev[:, (pos + r) % C] = vn[r]
+    assert torch.equal(ks.view(torch.int16), ek.view(torch.int16))
+    assert torch.equal(vs_.view(torch.int16), ev.view(torch.int16))
+
+
 def test_append_refused():
     g = synth.gen(13999)
     q = synth.normal_bf16((8, 6, 128), g).to(DEV)
