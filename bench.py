@@ -860,9 +860,15 @@ def main():
             for i in range(args.kernel_reps):
                 va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"],
                                              stream=torch.cuda.current_stream())
+        def spairs(c=c, st=st, kv_of=kv_of):
+            for i in range(args.kernel_reps):
+                k, v = kv_of(i, bucket_slots)
+                cur = torch.cuda.current_stream()
+                va.verify_attn_split_state(bucket, st, c["q"], k, v, bws, stream=cur)
+                va.verify_attn_combine_state(bucket, st, bws, bout, lse=blse, sink=c["sink"], stream=cur)
         s_avg, c_avg, p_avg = timed(splits), timed(combines), timed(pairs)
         r_avg = timed(reads)
-        ss_avg, sc_avg = timed(ssplits), timed(scombines)
+        ss_avg, sc_avg, sp_avg = timed(ssplits), timed(scombines), timed(spairs)
         del pool, fl
         split_bytes += nb * args.kernel_reps
         split_ms += s_avg * args.kernel_reps
@@ -878,6 +884,7 @@ def main():
             "kv_gbs_call": round(nb / (p_avg * 1e-3) / 1e9, 1),
             "read_probe_us": round(r_avg * 1e3, 2), "read_probe_gbs": round(nb / (r_avg * 1e-3) / 1e9, 1),
             "state_split_us": round(ss_avg * 1e3, 2), "state_combine_us": round(sc_avg * 1e3, 2),
+            "state_us_per_call": round(sp_avg * 1e3, 2),
         })
         # the state path against a static call with the same split count (the
         # bucket's, at most one granule each) on replica 0 of pass A: the
