@@ -15,9 +15,12 @@ silent:
 * Values: one FP32 scale per (token, KV head), s = max|v| / 127; codes are
   round-half-even of v / s clamped to [-127, 127]; s = 0 gives all-zero codes.
   Dequantisation is code * s.
-* Where a code is decided from a rotated key, the rotation is taken in FP32
-  (`wht_f32`, the precision a GPU encoder works in) so that both sides round
-  the same value.
+* A key's code is e4m3_encode(wht(k)), the rotation in float64.  An encoder
+  that rotates in FP32 may round a value within FP32 error of an E4M3 rounding
+  midpoint to the other neighbour; `e4m3_codes_acceptable` takes the
+  definition's code wherever the FP32 error bound of the rotation
+  (`wht_f32_error_bound`) keeps every midpoint away, and either neighbour
+  elsewhere.
 """
 
 import numpy as np
@@ -76,47 +79,86 @@ def wht(x):
     return x @ hadamard(n).T / np.sqrt(n)
 
 
-def wht_f32(x):
-    """The normalised rotation as a GPU computes it in FP32: the fast
-    Walsh-Hadamard transform in natural order, one butterfly stage per bit of
-    the index from the lowest (width 1, 2, 4, ..., n/2), each stage replacing
-    the pair (a, b) at indices (i, i + width) by (a + b, a - b) in float32,
-    then a float32 multiply by float32(1/sqrt(n)).
-
-    Rounding the rotated key to FP8 is decided on this FP32 value, so an
-    encoder in FP32 and this function must agree bit for bit; the float64
-    `wht` is the definition it approximates (to FP32 rounding).
-    """
-    y = np.array(x, dtype=np.float32, copy=True)
-    n = y.shape[-1]
-    if n & (n - 1):
-        raise ValueError("length must be a power of two")
-    width = 1
-    while width < n:
-        z = y.reshape(y.shape[:-1] + (n // (2 * width), 2, width))
-        a = z[..., 0, :].copy()
-        b = z[..., 1, :].copy()
-        z[..., 0, :] = a + b
-        z[..., 1, :] = a - b
-        y = z.reshape(y.shape)
-        width *= 2
-    return y * np.float32(1.0 / np.sqrt(n))
+# FP32 rounding-error bound of an encoder's rotation, in units of 2^-24:
+# every fast 128-point Walsh-Hadamard transform is seven levels of additions
+# and subtractions, and the result is scaled by the FP32-rounded 1/sqrt(128)
+# (before or after the levels).  The computed sum of n signed terms through a
+# tree of depth d is within d*u*(1 + d*u)*sum|x| of the exact sum (u = 2^-24,
+# the unit roundoff of round-to-nearest); the FP32 scale constant and the
+# product's rounding add u*sum|x|/sqrt(n) and u*|y|.  The constants below
+# cover those terms with margin.
+WHT_F32_ERR_SUM = 9.0
+WHT_F32_ERR_OUT = 2.0
 
 
-def encode_keys_f32(k):
-    """E4M3FN codes of the FP32-rotated keys: e4m3_encode(wht_f32(k))."""
-    return e4m3_encode(wht_f32(k).astype(np.float64))
+def wht_f32_error_bound(x):
+    """Upper bound on |fl32(H x / sqrt(n)) - H x / sqrt(n)| for any FP32
+    encoder of the rotation (see the constants above), per output element:
+    (9 * sum|x| / sqrt(n) + 2 |y|) * 2^-24, broadcast over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    y = wht(x)
+    s = np.abs(x).sum(axis=-1, keepdims=True) / np.sqrt(n)
+    return (WHT_F32_ERR_SUM * s + WHT_F32_ERR_OUT * np.abs(y)) * 2.0 ** -24 * (1 + 1e-9)
+
+
+def e4m3_code_interval(y, bound):
+    """Codes that an encoder may store for the exact value y when it rounds a
+    value it computed within `bound` of y: (lo, hi) = (e4m3_encode(y - bound),
+    e4m3_encode(y + bound)), and `decided` = no E4M3 rounding midpoint (and
+    no zero) lies within the bound, so that the code is unique (lo == hi).
+    Elsewhere every code whose value lies in [value(lo), value(hi)] is a
+    correct rounding of some value in the interval."""
+    y = np.asarray(y, dtype=np.float64)
+    b = np.broadcast_to(np.asarray(bound, dtype=np.float64), y.shape)
+    lo = e4m3_encode(y - b)
+    hi = e4m3_encode(y + b)
+    decided = (lo == hi) & ~((y - b <= 0) & (y + b >= 0))
+    return lo, hi, decided
+
+
+def e4m3_codes_acceptable(codes, y, bound):
+    """Per element: True where `codes` is a correct E4M3FN code for an encoder
+    whose rotated value lies within `bound` of the exact y (the definition's
+    code where it is decided; a code between the interval's end codes
+    elsewhere; 0x7F where y is NaN).  Returns (ok, decided)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    y = np.asarray(y, dtype=np.float64)
+    lo, hi, decided = e4m3_code_interval(np.nan_to_num(y), bound)
+    v = e4m3_decode(codes)
+    inside = (v >= e4m3_decode(lo)) & (v <= e4m3_decode(hi))
+    ok = np.where(decided, codes == lo, inside & ~np.isnan(v))
+    nan = np.isnan(y)
+    return np.where(nan, codes == 0x7F, ok), decided & ~nan
+
+
+def _rne(x):
+    """Round half to even (numpy's rounding of exact halves)."""
+    return np.round(x)
 
 
 def i8_encode(v):
-    """Per-row INT8 codes and FP32 scale.  v: [..., D] -> (codes, scale[...])."""
+    """Per-row INT8 codes and FP32 scale.  v: [..., D] -> (codes, scale[...]).
+
+    s = max|v| / 127 rounded to FP32 (the float64 quotient of a value with at
+    most 24 significant bits by 127 never lies on an FP32 rounding midpoint,
+    so rounding it again to FP32 is the correctly rounded FP32 quotient);
+    codes = round-half-even(v / s) clamped to [-127, 127].  v / s is taken in
+    float64: for v with at most 24 significant bits and |v / s| <= 127.5 the
+    float64 quotient lies on a half-integer only when the exact one does, so
+    the rounding is that of the exact quotient.  s = 0 gives zero codes.  A
+    row holding NaN or an infinity has a NaN or infinite scale and zero codes
+    (its dequantised values are then NaN)."""
     v = np.asarray(v, dtype=np.float64)
-    amax = np.abs(v).max(axis=-1)
-    scale = (amax / 127.0).astype(np.float32)
+    amax = np.abs(v).max(axis=-1)                          # NaN propagates
+    with np.errstate(invalid="ignore", over="ignore"):
+        scale = (amax / 127.0).astype(np.float32)
     s64 = scale.astype(np.float64)[..., None]
-    safe = np.where(s64 == 0, 1.0, s64)
-    q = np.clip(np.round(v / safe), -127, 127)             # np.round: half to even
-    q = np.where(s64 == 0, 0, q)
+    usable = np.isfinite(s64) & (s64 != 0)
+    safe = np.where(usable, s64, 1.0)
+    with np.errstate(invalid="ignore"):
+        q = np.clip(_rne(np.where(usable, v, 0.0) / safe), -127, 127)
+    q = np.where(usable, q, 0)
     return q.astype(np.int8), scale
 
 

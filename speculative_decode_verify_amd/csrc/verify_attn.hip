@@ -538,10 +538,18 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
 #pragma unroll
         for (int i = 0; i < APASS; ++i) {
           const int rr = (64 * i + lane) / PIECES;
-          const int j = new0 + rr - c0;
-          if (rr < live_rows && j >= 0 && j < kChunk) {
-            const int f = PW == 0 ? (j & (PIECES - 1)) : ((2 * j) & (PIECES - 2));
-            *(u32x4 *)(tile + j * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
+          const int32_t x = new0 + rr;  // this row's key (relative)
+          const int jx = x - c0;
+          if (rr < live_rows && jx >= 0 && jx < kChunk) {
+            // tile rows whose key is clamped to x read x's slot too (keys past
+            // rel_hi - 1, or before rel_lo): they take this row as well, so no
+            // masked key carries the slot's stale contents into P V
+            const int jlo = x == rel_lo ? 0 : jx;
+            const int jhi = x == rel_hi - 1 ? kChunk - 1 : jx;
+            for (int j = jlo; j <= jhi; ++j) {
+              const int f = PW == 0 ? (j & (PIECES - 1)) : ((2 * j) & (PIECES - 2));
+              *(u32x4 *)(tile + j * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
+            }
           }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1135,11 +1143,12 @@ __global__ __launch_bounds__(256) void ring_write_kernel(const uint8_t *k_new, c
 // KV write with the cache's codec: one wave per (row, KV head).
 // ---------------------------------------------------------------------------
 // E4M3FN code of y: nearest finite value, ties to the even code, saturating
-// at 448, sign copied from y.  Integer-exact: the mantissa is rounded as
-// rint(|y| * 2^(3 - e)) in [8, 16] for |y| >= 2^-6 (e = floor(log2 |y|); a
-// carry to 16 moves to the next binade), and as rint(|y| * 2^9) for the
-// subnormal step 2^-9 below; both scalings are exact powers of two.
+// at 448, sign copied from y; NaN gives 0x7F.  Integer-exact: the mantissa is
+// rounded as rint(|y| * 2^(3 - e)) in [8, 16] for |y| >= 2^-6 (e = floor(log2
+// |y|); a carry to 16 moves to the next binade), and as rint(|y| * 2^9) for
+// the subnormal step 2^-9 below; both scalings are exact powers of two.
 __device__ __forceinline__ uint32_t e4m3_code(float y) {
+  if (y != y) return 0x7Fu;
   const uint32_t sign = (__float_as_uint(y) >> 31) << 7;
   const float a = fminf(fabsf(y), 448.f);
   uint32_t code;
@@ -1193,12 +1202,15 @@ __global__ __launch_bounds__(64) void kv_write_kernel(const uint16_t *k_new, con
     *(uint16_t *)(k_cache + dst + 2 * lane) = (uint16_t)kc;
 
     const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
-    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    // maximum of |v| with NaN kept (fmaxf would drop it): a row holding NaN
+    // or an infinity gets a non-finite scale and zero codes
+    auto nmax = [](float a, float b) { return (a > b || a != a) ? a : b; };
+    float amax = nmax(fabsf(v0), fabsf(v1));
 #pragma unroll
-    for (int h = 1; h < 64; h <<= 1) amax = fmaxf(amax, __shfl_xor(amax, h, 64));
+    for (int h = 1; h < 64; h <<= 1) amax = nmax(amax, __shfl_xor(amax, h, 64));
     const float sc = amax / 127.f;  // IEEE division, correctly rounded
     int c0 = 0, c1 = 0;
-    if (sc != 0.f) {
+    if (sc != 0.f && __builtin_isfinite(sc)) {
       c0 = (int)rint((double)v0 / (double)sc);
       c1 = (int)rint((double)v1 / (double)sc);
       c0 = c0 < -127 ? -127 : (c0 > 127 ? 127 : c0);

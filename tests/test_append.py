@@ -17,7 +17,9 @@ Gates:
 * quantised caches are refused; a linear cache too short for the rows is
   refused before any launch.
 The stale contents of the slots the rows take are scaled by 100, so a key
-read from memory instead of from the new rows would show.
+read from memory instead of from the new rows would show, or NaN (a fresh or
+poisoned cache): no key of the read, masked ones included, may carry them
+into the result.
 """
 import math
 
@@ -69,10 +71,11 @@ def _same(fused, ref, live, name):
     assert torch.equal(vf.view(torch.int16), vr.view(torch.int16)), f"{name}: V cache differs"
 
 
-@pytest.mark.parametrize("t0,W,C,live,splits", [(5120, 4096, 4160, 5, 0), (51200, 4096, 4160, 8, 0),
-                                                (194560, 4096, 4160, 7, 0), (999, 57, 64, 8, 3),
-                                                (1021, 57, 64, 6, 2)])
-def test_append_window_ring(t0, W, C, live, splits):
+@pytest.mark.parametrize("t0,W,C,live,splits,stale", [
+    (5120, 4096, 4160, 5, 0, "loud"), (51200, 4096, 4160, 8, 0, "loud"), (194560, 4096, 4160, 7, 0, "loud"),
+    (999, 57, 64, 8, 3, "loud"), (1021, 57, 64, 6, 2, "loud"),
+    (5120, 4096, 4160, 5, 0, "nan"), (999, 57, 64, 8, 3, "nan"), (1021, 57, 64, 6, 2, "nan")])
+def test_append_window_ring(t0, W, C, live, splits, stale):
     rows, Hq, Hkv, D = 8, 6, 1, 64
     g = synth.gen(12000 + t0 + live)
     base = t0 - C
@@ -86,9 +89,9 @@ def test_append_window_ring(t0, W, C, live, splits):
     for i in range(C):
         k_ring[:, (base + i) % C] = kl[:, i]
         v_ring[:, (base + i) % C] = vl[:, i]
-    for r in range(rows):  # stale, loud contents in the slots the rows take
-        k_ring[:, (t0 + r) % C] = kl[:, r] * 100
-        v_ring[:, (t0 + r) % C] = vl[:, r] * 100
+    for r in range(rows):  # stale contents in the slots the rows take
+        k_ring[:, (t0 + r) % C] = kl[:, r] * 100 if stale == "loud" else NAN
+        v_ring[:, (t0 + r) % C] = vl[:, r] * 100 if stale == "loud" else NAN
     k_new = kl[:, C:C + rows].permute(1, 0, 2).contiguous().to(DEV)
     v_new = vl[:, C:C + rows].permute(1, 0, 2).contiguous().to(DEV)
     plan = plan_for(rows, live, Hq, Hkv, D, "window", first_pos=t0, window=W, ring_slots=C,
@@ -100,7 +103,7 @@ def test_append_window_ring(t0, W, C, live, splits):
         va.verify_attn_split(plan, qd, kc, vc, ws)
 
     fused, unfused = _both(plan, qd, k_new, v_new, k_ring.to(DEV), v_ring.to(DEV), ref, sd)
-    name = f"append window t0={t0} C={C} live={live}"
+    name = f"append window t0={t0} C={C} live={live} stale={stale}"
     _same(fused, unfused, live, name)
     # oracle: its own ring from the linear data, replaying the same positions
     labels = omasks.ring_replay(C, list(range(base, t0 + rows)))
@@ -116,22 +119,27 @@ def test_append_window_ring(t0, W, C, live, splits):
     check(fused[1], fused[2], ro, rl, live, name)
 
 
-@pytest.mark.parametrize("rows,live,Hq,Hkv,D,fp,splits", [
-    (8, 8, 6, 1, 128, 4093, 0),      # rows 4093..4100 straddle a chunk boundary
-    (8, 6, 6, 1, 128, 1021, 32),     # the chunk boundary is a split boundary too
-    (16, 16, 8, 2, 128, 20005, 0),   # 16 rows at D 128, two KV heads
-    (8, 5, 6, 1, 64, 3000, 0),
-    (8, 0, 6, 1, 128, 500, 0),       # no live row: stored, nothing read
+@pytest.mark.parametrize("rows,live,Hq,Hkv,D,fp,splits,stale", [
+    (8, 8, 6, 1, 128, 4093, 0, "loud"),      # rows 4093..4100 straddle a chunk boundary
+    (8, 6, 6, 1, 128, 1021, 32, "loud"),     # the chunk boundary is a split boundary too
+    (16, 16, 8, 2, 128, 20005, 0, "loud"),   # 16 rows at D 128, two KV heads
+    (8, 5, 6, 1, 64, 3000, 0, "loud"),
+    (8, 0, 6, 1, 128, 500, 0, "loud"),       # no live row: stored, nothing read
+    (8, 8, 6, 1, 128, 4093, 0, "nan"),
+    (8, 6, 6, 1, 128, 1021, 32, "nan"),
+    (16, 16, 8, 2, 128, 20005, 0, "nan"),
+    (8, 5, 6, 1, 64, 3000, 0, "nan"),
+    (8, 3, 6, 1, 128, 4000, 0, "nan"),       # the last live key mid-chunk, masked keys after it
 ])
-def test_append_linear(rows, live, Hq, Hkv, D, fp, splits):
+def test_append_linear(rows, live, Hq, Hkv, D, fp, splits, stale):
     g = synth.gen(13000 + fp + rows)
     cap = fp + rows + 40
     k = synth.normal_bf16((Hkv, cap, D), g)
     v = synth.normal_bf16((Hkv, cap, D), g)
     k_new = synth.normal_bf16((rows, Hkv, D), g)
     v_new = synth.normal_bf16((rows, Hkv, D), g)
-    k[:, fp:fp + rows] = k_new.permute(1, 0, 2) * 100   # stale, loud
-    v[:, fp:fp + rows] = v_new.permute(1, 0, 2) * 100
+    k[:, fp:fp + rows] = k_new.permute(1, 0, 2) * 100 if stale == "loud" else NAN   # stale
+    v[:, fp:fp + rows] = v_new.permute(1, 0, 2) * 100 if stale == "loud" else NAN
     k[:, fp + rows:] = NAN
     v[:, fp + rows:] = NAN
     q = synth.normal_bf16((rows, Hq, D), g)
@@ -145,7 +153,7 @@ def test_append_linear(rows, live, Hq, Hkv, D, fp, splits):
         va.verify_attn_split(plan, qd, kc, vc, ws)
 
     fused, unfused = _both(plan, qd, kn, vn, k.to(DEV), v.to(DEV), ref, s.to(DEV))
-    name = f"append linear fp={fp} rows={rows} live={live} D={D}"
+    name = f"append linear fp={fp} rows={rows} live={live} D={D} stale={stale}"
     _same(fused, unfused, live, name)
     assert torch.equal(fused[3][:, fp:fp + rows].view(torch.int16),
                        k_new.permute(1, 0, 2).contiguous().view(torch.int16)), f"{name}: stored K"
@@ -161,8 +169,10 @@ def test_append_linear(rows, live, Hq, Hkv, D, fp, splits):
         check(fused[1], fused[2], ro, rl, live, name)
 
 
-@pytest.mark.parametrize("P,live,Hq,Hkv,splits", [(2048, 16, 24, 4, 0), (700, 11, 6, 1, 0), (700, 16, 6, 1, 22)])
-def test_append_tree(P, live, Hq, Hkv, splits):
+@pytest.mark.parametrize("P,live,Hq,Hkv,splits,stale", [
+    (2048, 16, 24, 4, 0, "loud"), (700, 11, 6, 1, 0, "loud"), (700, 16, 6, 1, 22, "loud"),
+    (2048, 16, 24, 4, 0, "nan"), (700, 11, 6, 1, 0, "nan"), (700, 16, 6, 1, 22, "nan")])
+def test_append_tree(P, live, Hq, Hkv, splits, stale):
     rows, D = 16, 128
     g = synth.gen(14000 + P + live)
     parent = synth.random_tree(rows, g)
@@ -171,8 +181,8 @@ def test_append_tree(P, live, Hq, Hkv, splits):
     v = synth.normal_bf16((Hkv, cap, D), g)
     k_new = synth.normal_bf16((rows, Hkv, D), g)
     v_new = synth.normal_bf16((rows, Hkv, D), g)
-    k[:, P:P + rows] = k_new.permute(1, 0, 2) * 100   # stale, loud
-    v[:, P:P + rows] = v_new.permute(1, 0, 2) * 100
+    k[:, P:P + rows] = k_new.permute(1, 0, 2) * 100 if stale == "loud" else NAN   # stale
+    v[:, P:P + rows] = v_new.permute(1, 0, 2) * 100 if stale == "loud" else NAN
     k[:, P + rows:] = NAN
     v[:, P + rows:] = NAN
     q = synth.normal_bf16((rows, Hq, D), g)
@@ -185,7 +195,7 @@ def test_append_tree(P, live, Hq, Hkv, splits):
         va.verify_attn_split(plan, qd, kc, vc, ws)
 
     fused, unfused = _both(plan, qd, kn, vn, k.to(DEV), v.to(DEV), ref, None)
-    name = f"append tree P={P} live={live} Hkv={Hkv}"
+    name = f"append tree P={P} live={live} Hkv={Hkv} stale={stale}"
     _same(fused, unfused, live, name)
     kf, vf = k.clone(), v.clone()
     kf[:, P:P + rows] = k_new.permute(1, 0, 2)
@@ -197,10 +207,12 @@ def test_append_tree(P, live, Hq, Hkv, splits):
     check(fused[1], fused[2], ro, rl, live, name)
 
 
-@pytest.mark.parametrize("mode,pos,live", [("causal", 20000, 8), ("causal", 4093, 8), ("causal", 19990, 5),
-                                           ("causal", 100, 0), ("window", 51200, 5), ("window", 5120, 8),
-                                           ("tree", 700, 11), ("tree", 2048, 16)])
-def test_append_state_matches_static(mode, pos, live):
+@pytest.mark.parametrize("mode,pos,live,stale", [
+    ("causal", 20000, 8, "loud"), ("causal", 4093, 8, "loud"), ("causal", 19990, 5, "loud"),
+    ("causal", 100, 0, "loud"), ("window", 51200, 5, "loud"), ("window", 5120, 8, "loud"),
+    ("tree", 700, 11, "loud"), ("tree", 2048, 16, "loud"),
+    ("causal", 19990, 5, "nan"), ("window", 5120, 5, "nan"), ("tree", 700, 11, "nan")])
+def test_append_state_matches_static(mode, pos, live, stale):
     """verify_attn_split_append_state under one bucket against
     verify_attn_split_append of the state's own problem with the state's
     split count (the bucket's, at most one granule each): the same partials
@@ -237,8 +249,14 @@ def test_append_state_matches_static(mode, pos, live):
     vn = synth.normal_bf16((rows, Hkv, D), g).to(DEV)
     q = synth.normal_bf16((rows, Hq, D), g).to(DEV)
     sink = synth.normal_f32((Hq,), g).to(DEV)
+    if stale == "nan":  # the slots the rows take hold NaN
+        first = pos
+        for r in range(rows):
+            sl = (first + r) % slots if mode == "window" else first + r
+            k[:, sl] = NAN
+            v[:, sl] = NAN
     std = st.to(DEV)
-    name = f"append state {mode} pos={pos} live={live}"
+    name = f"append state {mode} pos={pos} live={live} stale={stale}"
     ks, vs_ = k.clone(), v.clone()
     ws_s = _ws(bucket)
     out_s = torch.full((rows, Hq, D), NAN, dtype=torch.float32, device=DEV)

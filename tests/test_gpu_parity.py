@@ -346,12 +346,20 @@ def _label_values(Hkv, n, D, base=0):
 
 
 @pytest.mark.parametrize("case", ["causal", "causal_many_splits", "window", "window_small_ring", "tree", "tree96",
-                                  "quant"])
+                                  "quant", "causal_s300", "causal_s600"])
 def test_counting_partials_bit_exact(case):
     """q = 0: every visible score is 0, so each split's m = 0, l = the number
     of visible keys and O = the sum of their integer labels, all exact."""
     g = synth.gen(6000 + hash(case) % 1000)
-    if case.startswith("causal"):
+    if case in ("causal_s300", "causal_s600"):
+        # config-2 shapes with more than 256 splits: the combine's widest
+        # batch, and (600) more than one round of batches per thread
+        rows, live, Hq, Hkv, D = 8, 7, 6, 1, 128
+        P, S = (16384, 300) if case == "causal_s300" else (32768, 600)
+        kw = dict(rows=rows, live=live, mask="causal", first_pos=P)
+        cap = P + rows + 64
+        plan = plan_for(rows, live, Hq, Hkv, D, "causal", first_pos=P, kv_capacity=cap, splits=S)
+    elif case.startswith("causal"):
         rows, live, Hq, Hkv, D, P = 8, 6, 6, 1, 64, 1000
         S = 4 if case == "causal" else 40
         kw = dict(rows=rows, live=live, mask="causal", first_pos=P)
@@ -562,6 +570,8 @@ def test_single_visible_key_is_exact():
     (16, 5, 6, 1, 64, 3000, 0),     # 30 live of 96 at D 64: one live wave
     (1, 1, 6, 1, 128, 4095, 0),     # a single row
     (8, 7, 6, 1, 128, 100000, 3),   # few long splits
+    (8, 6, 6, 1, 128, 16384, 300),  # more than 256 splits: the combine's widest batch
+    (8, 8, 6, 1, 128, 32768, 600),  # two rounds of combine batches per thread
 ])
 def test_shapes_and_split_counts(rows, live, Hq, Hkv, D, P, S):
     plan, kw, q, k, v, s = linear_case(9100 + P, rows, live, Hq, Hkv, D, "causal", first_pos=P, splits=S)

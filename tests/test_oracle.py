@@ -384,40 +384,70 @@ def test_e4m3_encode_saturates_and_midpoints():
     assert codec.e4m3_encode(np.array([np.nan])).tolist() == [0x7F]
 
 
-def test_wht_f32_exact_on_integers():
-    """Small integer inputs keep every butterfly exact in FP32, so the FP32
-    rotation is exactly float32(H x) * float32(1/sqrt(128)) with H the
-    Sylvester matrix from scipy -- any wrong pairing or sign fails."""
-    rng = np.random.default_rng(21)
-    x = rng.integers(-50, 51, size=(40, 128)).astype(np.float64)
-    exact = (x @ scipy.linalg.hadamard(128).T).astype(np.float32)
-    want = exact * np.float32(1.0 / math.sqrt(128))
-    got = codec.wht_f32(x.astype(np.float32))
-    assert got.dtype == np.float32
-    assert np.array_equal(got.view(np.int32), want.view(np.int32))
+def test_e4m3_code_interval_at_midpoints():
+    """1.0625 is the midpoint of 1.0 (0x38) and 1.125 (0x39): with no error
+    the definition's tie-to-even code 0x38 is decided; within any error both
+    neighbours are correct and nothing else is; a value far from every
+    midpoint is decided; zero accepts both signed zeros; NaN only 0x7F."""
+    lo, hi, dec = codec.e4m3_code_interval(np.array([1.0625, 1.0625, 1.02, 0.0, 500.0]),
+                                           np.array([0.0, 1e-6, 1e-6, 1e-7, 1.0]))
+    assert lo.tolist() == [0x38, 0x38, 0x38, 0x80, 0x7E]
+    assert hi.tolist() == [0x38, 0x39, 0x38, 0x00, 0x7E]
+    assert dec.tolist() == [True, False, True, False, True]
+    y = np.array([1.0625] * 4 + [1.02] * 2 + [0.0] * 3 + [np.nan, np.nan])
+    b = np.array([1e-6] * 4 + [1e-6] * 2 + [1e-7] * 3 + [0.0, 0.0])
+    codes = np.array([0x38, 0x39, 0x3A, 0xB8, 0x38, 0x39, 0x00, 0x80, 0x01, 0x7F, 0xFF], np.uint8)
+    ok, decided = codec.e4m3_codes_acceptable(codes, y, b)
+    assert ok.tolist() == [True, True, False, False, True, False, True, True, False, True, False]
+    assert decided.tolist() == [False] * 4 + [True] * 2 + [False] * 5
 
 
-def test_wht_f32_within_fp32_rounding_of_definition():
-    """Seven FP32 butterfly stages and one multiply: each output is within
-    8 * 2^-24 * sum|x| / sqrt(128) + 2^-24 |y| of the float64 rotation."""
-    rng = np.random.default_rng(22)
-    x = (rng.standard_normal((64, 128)) * rng.choice([1e-3, 1.0, 40.0], size=(64, 1))).astype(np.float32)
+def _fwht_f32(x, order, scale_first):
+    """An FP32 encoder's rotation, written here only to exercise the bound:
+    butterflies (a, b) -> (a + b, a - b) in float32, stage widths in the
+    given order, scaled by float32(1/sqrt(n)) before or after them."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    inv = np.float32(1.0 / math.sqrt(n))
+    if scale_first:
+        y = y * inv
+    for width in order:
+        z = y.reshape(y.shape[:-1] + (n // (2 * width), 2, width))
+        a, b = z[..., 0, :].copy(), z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(y.shape)
+    return y if scale_first else y * inv
+
+
+@pytest.mark.parametrize("order,scale_first", [((1, 2, 4, 8, 16, 32, 64), False),
+                                               ((64, 32, 16, 8, 4, 2, 1), False),
+                                               ((1, 2, 4, 8, 16, 32, 64), True)])
+def test_wht_error_bound_covers_fp32_encoders(order, scale_first):
+    """The bound holds for FP32 rotations in several evaluation orders (and
+    is not vacuous: the worst error reaches a fair share of it); the codes of
+    such an encoder are acceptable everywhere, and the cases left undecided
+    by the bound are rare at the data's magnitudes."""
+    rng = np.random.default_rng(24)
+    x = (rng.standard_normal((3000, 128)) * rng.choice([2.0 ** -12, 1e-3, 1.0, 40.0, 3000.0],
+                                                       size=(3000, 1))).astype(np.float32)
     y = codec.wht(x.astype(np.float64))
-    got = codec.wht_f32(x).astype(np.float64)
-    bound = 8 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True) / math.sqrt(128) \
-        + 2.0 ** -24 * np.abs(y)
-    assert np.all(np.abs(got - y) <= bound)
-    assert np.abs(got - y).max() > 0  # FP32, not a float64 computation in disguise
+    got = _fwht_f32(x, order, scale_first).astype(np.float64)
+    b = codec.wht_f32_error_bound(x.astype(np.float64))
+    err = np.abs(got - y)
+    assert np.all(err <= b)
+    assert (err / b).max() > 0.05
+    ok, decided = codec.e4m3_codes_acceptable(codec.e4m3_encode(got), y, b)
+    assert ok.all()
+    assert (~decided).mean() < 2e-3
 
 
-def test_encode_keys_f32_is_the_rotation_then_e4m3():
-    rng = np.random.default_rng(23)
-    x = rng.integers(-3, 4, size=(16, 128)).astype(np.float32)  # FP32-exact rotation
-    assert np.array_equal(codec.encode_keys_f32(x), codec.e4m3_encode(codec.wht(x.astype(np.float64))))
-    # a one-hot key rotates to +-c/sqrt(128) everywhere: one code magnitude, signs from H's column
-    k = np.zeros((1, 128), np.float32)
+def test_key_codes_of_a_one_hot_key():
+    """A one-hot key rotates to +-c/sqrt(128) everywhere: one code magnitude,
+    signs from the Hadamard column (scipy's matrix)."""
+    k = np.zeros((1, 128))
     k[0, 5] = 2.0
-    codes = codec.encode_keys_f32(k)[0]
+    codes = codec.e4m3_encode(codec.wht(k))[0]
     mag = codec.e4m3_encode(np.array([2.0 / math.sqrt(128)]))[0]
     signs = scipy.linalg.hadamard(128)[:, 5] < 0
     assert np.array_equal(codes, np.where(signs, mag | 0x80, mag).astype(np.uint8))
@@ -449,6 +479,66 @@ def test_i8_codec():
     assert np.all(np.abs(dq - v) <= scale[..., None].astype(np.float64) * 0.5 * (1 + 1e-6))
     # dequantisation is exact: every product is a float64 without rounding
     assert np.array_equal(dq, codes.astype(np.float64) * scale.astype(np.float64)[..., None])
+
+
+def test_i8_ties_round_half_even():
+    """Exact ties.  A row with max 127 has s = 1 and one with max 63.5 has
+    s = 0.5 (both exact in FP32), so v / s = +-0.5, 1.5, 2.5, 3.5, 126.5 are
+    exact halves: round-half-even gives 0, 2, 2, 4, 126 (half away from zero
+    would give 1, 2, 3, 4, 127)."""
+    v = np.zeros((2, 128))
+    v[0, :12] = [127, 0.5, 1.5, 2.5, 3.5, 126.5, -0.5, -1.5, -2.5, -3.5, -126.5, 0.25]
+    v[1, :8] = [63.5, 0.25, 0.75, 1.25, -0.25, -0.75, -1.25, 63.25]
+    codes, scale = codec.i8_encode(v)
+    assert scale.tolist() == [1.0, 0.5]
+    assert codes[0, :12].tolist() == [127, 0, 2, 2, 4, 126, 0, -2, -2, -4, -126, 0]
+    assert codes[1, :8].tolist() == [127, 0, 2, 2, 0, -2, -2, 126]
+
+
+def _fp32_round_exact(fr):
+    """Correctly rounded FP32 value of a rational (nearest, ties to even),
+    from exact comparisons with the neighbours of a first guess."""
+    from fractions import Fraction
+    f = np.float32(float(fr))
+    cands = {f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))}
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(np.array(c).view(np.int32)) & 1))
+    return best
+
+
+def test_i8_codes_equal_exact_rational_rounding():
+    """Scale and codes against exact rational arithmetic: s = the correctly
+    rounded FP32 of max|v| / 127, code = the integer nearest v / s (ties to
+    even), clamped -- no float64 division involved."""
+    from fractions import Fraction
+    rng = np.random.default_rng(25)
+    v = (rng.standard_normal((48, 128)) * rng.choice([1e-3, 1.0, 40.0], size=(48, 1)))
+    v = v.astype(np.float32).astype(np.float64)
+    v[3, 7] = 0.0
+    codes, scale = codec.i8_encode(v)
+    for r in range(v.shape[0]):
+        amax = max(abs(Fraction(float(t))) for t in v[r])
+        s = _fp32_round_exact(amax / 127)
+        assert scale[r] == s
+        sf = Fraction(float(s))
+        for d in range(v.shape[1]):
+            qv = Fraction(float(v[r, d])) / sf
+            n = math.floor(qv)
+            frac = qv - n
+            want = n + 1 if (frac > Fraction(1, 2) or (frac == Fraction(1, 2) and n % 2 == 1)) else n
+            assert codes[r, d] == max(-127, min(127, want)), (r, d)
+
+
+def test_i8_non_finite_and_zero_rows():
+    v = np.ones((3, 128))
+    v[0] = 0.0
+    v[1, 4] = np.nan
+    v[2, 9] = -np.inf
+    codes, scale = codec.i8_encode(v)
+    assert scale[0] == 0 and np.isnan(scale[1]) and np.isinf(scale[2])
+    assert (codes == 0).all()
+    dq = codec.i8_decode(codes, scale)
+    assert (dq[0] == 0).all() and np.isnan(dq[1]).all() and np.isnan(dq[2]).all()
+
 
 
 # ---------------------------------------------------------------- planted mistakes
@@ -521,3 +611,19 @@ def test_planted_tree_non_ancestor_fails_star_pin(monkeypatch):
     monkeypatch.setattr(masks, "tree_ancestors", extra)
     with pytest.raises(AssertionError):
         test_chain_tree_is_causal_and_star_tree_is_prefix_plus_self()
+
+
+def test_planted_half_away_rounding_fails_tie_pin(monkeypatch):
+    """INT8 codes rounded half away from zero must be caught by the tie pin."""
+    monkeypatch.setattr(codec, "_rne", lambda x: np.sign(x) * np.floor(np.abs(x) + 0.5))
+    with pytest.raises(AssertionError):
+        test_i8_ties_round_half_even()
+
+
+def test_planted_tight_bound_fails_fp32_encoder_pin(monkeypatch):
+    """An error bound that ignores the FP32 rotation's rounding leaves codes
+    the FP32 encoder rounds the other way rejected."""
+    monkeypatch.setattr(codec, "WHT_F32_ERR_SUM", 0.0)
+    monkeypatch.setattr(codec, "WHT_F32_ERR_OUT", 0.0)
+    with pytest.raises(AssertionError):
+        test_wht_error_bound_covers_fp32_encoders((1, 2, 4, 8, 16, 32, 64), False)
