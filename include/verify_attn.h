@@ -294,10 +294,16 @@ va_status swa_ring_write(const void *k_new, const void *v_new, int32_t rows, int
  *                 is formed in FP32 by the fast transform (butterflies of
  *                 width 1, 2, ..., 64, each (a, b) -> (a + b, a - b), then a
  *                 multiply by FP32 1/sqrt(128)) and stored as the nearest
- *                 E4M3FN code (ties to even, saturating at 448, sign kept);
+ *                 E4M3FN code (ties to even, saturating at 448, sign kept;
+ *                 a NaN key element makes the row's codes 0x7F).  This is
+ *                 the code of the exact rotation except where an E4M3
+ *                 rounding midpoint lies within the FP32 rounding error of
+ *                 the rotated value, where it may be the other neighbour.
  *                 s = max|v| / 127 in FP32 goes to v_scale and each value is
  *                 stored as the round-half-even of v / s (taken in FP64)
- *                 clamped to [-127, 127] (all codes 0 when s = 0).
+ *                 clamped to [-127, 127] (all codes 0 when s = 0, or when
+ *                 the row holds NaN or an infinity, whose s is then NaN or
+ *                 infinite).
  *   k_cache, v_cache  [kv_heads, slots, head_dim]: bf16, or uint8 (keys) and
  *                 int8 (values) codes, element strides kv_head_stride and
  *                 kv_row_stride, 16-byte aligned rows.
@@ -315,6 +321,30 @@ va_status verify_kv_write(const void *k_new, const void *v_new, int32_t rows, in
                           void *v_cache, float *v_scale, int64_t v_scale_head_stride,
                           int64_t kv_capacity, int32_t ring_slots, int64_t kv_head_stride,
                           int64_t kv_row_stride, hipStream_t stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * verify_attn_split followed by verify_attn_combine on `stream`, with the
+ * partials kept in a workspace that the library holds in a static device
+ * array of VA_NOALLOC_WORKSPACE_BYTES per GPU (allocated when the library's
+ * code object is loaded on that GPU, held until the process ends) instead of
+ * a caller workspace.  No allocation, free or synchronisation happens in the
+ * call.  The first call on a device (the device current at the call) looks
+ * the array's address up on that device (not a stream operation); make it
+ * outside a graph capture.
+ * Arguments as verify_attn_split (q, k, v, v_scale, strides) and
+ * verify_attn_combine (sink, out, lse).  The array needs no clearing: every
+ * partial the combine reads is written by the split of the same call.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * Errors: VA_ERR_WORKSPACE when the plan's workspace exceeds
+ * VA_NOALLOC_WORKSPACE_BYTES; VA_ERR_HIP when the array's address cannot be
+ * looked up; otherwise as verify_attn_split and verify_attn_combine. */
+#define VA_NOALLOC_WORKSPACE_BYTES (16u << 20)
+va_status verify_attn_noalloc(const va_plan *plan, const void *q, const void *k, const void *v,
+                              const float *v_scale, int64_t v_scale_head_stride, int64_t kv_head_stride,
+                              int64_t kv_row_stride, const float *sink, float *out, float *lse,
+                              hipStream_t stream);
 
 /* Static text for a status code. */
 const char *va_status_string(va_status s);

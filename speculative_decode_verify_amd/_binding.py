@@ -93,6 +93,7 @@ def load_library():
     lib.verify_attn_combine.argtypes = [ctypes.POINTER(va_plan), V, SZ, V, V, V, V]
     lib.verify_attn_split_state.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, I64, V, SZ, V]
     lib.verify_attn_combine_state.argtypes = [ctypes.POINTER(va_plan), V, V, SZ, V, V, V, V]
+    lib.verify_attn_noalloc.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, I64, I64, I64, V, V, V, V]
     lib.verify_attn_split_append.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, I64, I64, V, SZ, V]
     lib.verify_attn_split_append_state.argtypes = [ctypes.POINTER(va_plan), V, V, V, V, V, V, I64, I64, V, SZ, V]
     lib.swa_ring_write.argtypes = [V, V, I32, I64, I32, I32, V, V, I32, I64, I64, V]
@@ -109,7 +110,7 @@ def load_library():
     for fn in ("verify_attn_plan", "verify_attn_plan_query", "verify_attn_plan_split_range",
                "verify_attn_split", "verify_attn_combine", "verify_attn_split_state", "verify_attn_split_append",
                "verify_attn_split_append_state",
-               "verify_attn_combine_state", "swa_ring_write", "verify_kv_write", "va_sample", "va_accept",
+               "verify_attn_combine_state", "verify_attn_noalloc", "swa_ring_write", "verify_kv_write", "va_sample", "va_accept",
                "va_sample_accept", "va_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
@@ -342,6 +343,21 @@ def verify_attn_combine(plan, workspace, out, lse=None, sink=None, stream=None):
     """Merge the splits' partials into out (and lse); shapes as in _combine_args."""
     _check("verify_attn_combine", _lib().verify_attn_combine(
         ctypes.byref(plan.plan), *_combine_args(plan, workspace, out, lse, sink), _stream(stream)))
+
+
+def verify_attn_noalloc(plan, q, k, v, out, lse=None, sink=None, v_scale=None, stream=None):
+    """verify_attn_split + verify_attn_combine with the library's static
+    per-GPU workspace (no allocation anywhere in the call); shapes as in
+    _split_args and _combine_args."""
+    import torch
+    empty = torch.empty(0, dtype=torch.float32, device=q.device)   # placeholder: no workspace is passed
+    qp, kp, vp, vsp, vss, khs, krs, _, _ = _split_args(plan, q, k, v, empty, v_scale)
+    _, _, sp, op, lp = _combine_args(plan, empty, out, lse, sink)
+    _check("verify_attn_noalloc", _lib().verify_attn_noalloc(
+        ctypes.byref(plan.plan), qp, kp, vp, vsp, vss, khs, krs, sp, op, lp, _stream(stream)))
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20
 
 
 def verify_attn_combine_state(plan, state, workspace, out, lse=None, sink=None, stream=None):

@@ -39,6 +39,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "plan_data.h"
@@ -1448,6 +1450,50 @@ extern "C" va_status verify_attn_combine_state(const va_plan *plan, const va_sta
                                                hipStream_t stream) {
   if (!state || !aligned8(state)) return VA_ERR_INVALID;
   return combine_impl(plan, state, workspace, workspace_bytes, sink, out, lse, stream);
+}
+
+// Workspace of verify_attn_noalloc: one copy per GPU, at a per-GPU address
+// looked up once per device with hipGetSymbolAddress (host code never passes
+// the array's name itself to a kernel or a copy: that is a host-side stand-in,
+// not a device address).
+static __device__ __align__(256) uint8_t scratch[VA_NOALLOC_WORKSPACE_BYTES];
+
+namespace va_detail {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The array's address on the current device, or nullptr.
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = addr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace va_detail
+
+extern "C" va_status verify_attn_noalloc(const va_plan *plan, const void *q, const void *k, const void *v,
+                                         const float *v_scale, int64_t v_scale_head_stride,
+                                         int64_t kv_head_stride, int64_t kv_row_stride, const float *sink,
+                                         float *out, float *lse, hipStream_t stream) {
+  const va_plan_data *d = plan_of(plan);
+  if (!d) return VA_ERR_INVALID;
+  if (d->workspace_bytes > VA_NOALLOC_WORKSPACE_BYTES) return VA_ERR_WORKSPACE;
+  void *ws = scratch_on_current_device();
+  if (!ws) return VA_ERR_HIP;
+  const va_status st = split_impl(plan, nullptr, q, k, v, v_scale, v_scale_head_stride, kv_head_stride,
+                                  kv_row_stride, ws, VA_NOALLOC_WORKSPACE_BYTES, stream);
+  if (st != VA_OK) return st;
+  return combine_impl(plan, nullptr, ws, VA_NOALLOC_WORKSPACE_BYTES, sink, out, lse, stream);
 }
 
 extern "C" va_status swa_ring_write(const void *k_new, const void *v_new, int32_t rows, int64_t first_pos,
