@@ -28,7 +28,17 @@ The CPU baseline times the float64 oracle on the same stored bytes (one pass
 over the seven contexts) and doubles as a full-size parity check of the GPU
 outputs of replica 0.
 
-Prints one JSON line.
+Prints one JSON line, with a `provenance` object: GPU name and ISA, compute
+units, ROCm / HIP / torch versions, the library's build record (git revision,
+hipcc version, flags), hashes of the library and the kernel source, the
+command line, and the clocks amd-smi reads right after the timed region.
+
+`--compare LIB [LIB ...]` times other builds of the library against the
+built one instead (split alone and split + combine pairs per context, cold
+pools as above) in drift-cancelling order: rounds alternate ABC... and
+...CBA, and the built library appears twice, as arms A and A', so the A/A
+spread bounds run-to-run noise.  It prints one JSON line with the median,
+minimum and maximum per arm.
 """
 import argparse
 import hashlib
@@ -70,6 +80,54 @@ def cold_pool(torch, synth, dev, nbytes, seed, tail=0):
         m = min(piece, flat.numel() - off)
         flat[off:off + m] = synth.normal_bf16_device((m,), seed + off // piece, dev)
     return pool, n
+
+
+def _amd_smi_clocks():
+    """Current gfx clocks (mean over the XCDs) and the memory clock, from
+    amd-smi (None if it is not available)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout[r.stdout.index("{"):])
+        clk = d["gpu_data"][0]["clock"]
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        mem = clk.get("mem_0", {}).get("clk", {})
+        gmax = next((v["max_clk"]["value"] for k, v in clk.items()
+                     if k.startswith("gfx_") and isinstance(v.get("max_clk"), dict)), None)
+        return {"gfx_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
+                "gfx_mhz_max": gmax, "mem_mhz": mem.get("value") if isinstance(mem, dict) else None,
+                "source": "amd-smi metric --clock, read right after the timed region"}
+    except Exception as e:  # noqa: BLE001
+        return {"error": f"amd-smi unavailable: {type(e).__name__}"}
+
+
+def provenance(torch, clocks=None):
+    """Where a result came from: hardware, software, build and command."""
+    props = torch.cuda.get_device_properties(0)
+    lib = os.path.join(ROOT, "speculative_decode_verify_amd", "lib", "libverify_attn.so")
+    info_path = os.path.join(ROOT, "speculative_decode_verify_amd", "lib", "build_info.json")
+    build = {}
+    if os.path.exists(info_path):
+        try:
+            build = json.load(open(info_path))
+        except Exception:  # noqa: BLE001
+            build = {}
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    lib_hash = None
+    if os.path.exists(lib):
+        with open(lib, "rb") as f:
+            lib_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm, "hip_runtime": torch.version.hip,
+            "torch": torch.__version__, "git_revision": build.get("git_revision"),
+            "worktree_modified": build.get("worktree_modified"), "hipcc": build.get("hipcc"),
+            "build_flags": build.get("flags"), "built_at_utc": build.get("built_at_utc"),
+            "library_sha16": lib_hash, "kernel_source_sha16": kernel_hash(),
+            "command": " ".join([os.path.basename(sys.executable)] + sys.argv), "clocks": clocks}
 
 
 def kv_bytes(hi):
@@ -637,6 +695,95 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
     return out
 
 
+def compare_libraries(torch, va, synth, dev, args):
+    """Split alone and split + combine pairs of several library builds, per
+    context, over cold pools (as pass B), in alternating order with the
+    built library as two arms (A and A')."""
+    import statistics
+    import speculative_decode_verify_amd._binding as binding
+    contexts = args.ctx or CONTEXTS
+    stream = torch.cuda.current_stream()
+    built = binding.load_library()
+    arms = [("A", built), ("A'", built)]
+    for i, path in enumerate(args.compare):
+        binding._LIB = None
+        saved = binding._LIB_PATH
+        binding._LIB_PATH = os.path.abspath(path)
+        arms.append((f"B{i}:{os.path.basename(path)}", binding.load_library()))
+        binding._LIB_PATH = saved
+    binding._LIB = built
+    cases = []
+    for ctx in contexts:
+        g = synth.gen(2000 + ctx // 1024)
+        live = synth.live_count(g)
+        hi = ctx + live
+        nb = kv_bytes(hi)
+        pool, npool = cold_pool(torch, synth, dev, nb, seed=50_000 + ctx)
+        q = synth.normal_bf16((ROWS, HQ, D), g).to(dev)
+        sink = synth.normal_f32((HQ,), g).to(dev)
+        cases.append(dict(ctx=ctx, live=live, hi=hi, nb=nb, pool=pool, npool=npool, q=q, sink=sink))
+    state = {}
+    for name, lib in arms:
+        binding._LIB = lib
+        for c in cases:
+            plan = va.Plan(rows=ROWS, live_rows=c["live"], q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
+                           first_pos=c["ctx"], kv_capacity=CAP, scale=1 / math.sqrt(D), splits=args.splits)
+            state[(name, c["ctx"])] = (plan, va.workspace_for(plan, dev),
+                                       torch.empty((ROWS, HQ, D), dtype=torch.float32, device=dev),
+                                       torch.empty((ROWS, HQ), dtype=torch.float32, device=dev))
+    binding._LIB = built
+
+    def kv_of(c, i):
+        fl = c["pool"].view(torch.bfloat16)
+        kb = (i % c["npool"]) * c["hi"] * 2 * D
+        vb = kb + c["hi"] * D
+        return fl[kb:kb + c["hi"] * D].view(HKV, c["hi"], D), fl[vb:vb + c["hi"] * D].view(HKV, c["hi"], D)
+
+    def timed(fn):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        gr.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gr.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.kernel_reps * 1e3
+
+    res = {}
+    for r in range(args.rounds):
+        order = arms if r % 2 == 0 else arms[::-1]
+        for name, lib in order:
+            binding._LIB = lib
+            for c in cases:
+                plan, ws, out, lse = state[(name, c["ctx"])]
+
+                def splits(c=c, plan=plan, ws=ws):
+                    for i in range(args.kernel_reps):
+                        k, v = kv_of(c, i)
+                        va.verify_attn_split(plan, c["q"], k, v, ws, stream=torch.cuda.current_stream())
+
+                def pairs(c=c, plan=plan, ws=ws, out=out, lse=lse):
+                    for i in range(args.kernel_reps):
+                        k, v = kv_of(c, i)
+                        cur = torch.cuda.current_stream()
+                        va.verify_attn_split(plan, c["q"], k, v, ws, stream=cur)
+                        va.verify_attn_combine(plan, ws, out, lse=lse, sink=c["sink"], stream=cur)
+                res.setdefault((name, c["ctx"], "split_us"), []).append(timed(splits))
+                res.setdefault((name, c["ctx"], "us_per_call"), []).append(timed(pairs))
+    binding._LIB = built
+    table = {}
+    for (name, ctx, what), xs in res.items():
+        table.setdefault(name, {}).setdefault(str(ctx), {})[what] = {
+            "median": round(statistics.median(xs), 3), "min": round(min(xs), 3), "max": round(max(xs), 3)}
+    aa = {str(c["ctx"]): {w: round(abs(table["A"][str(c["ctx"])][w]["median"] -
+                                       table["A'"][str(c["ctx"])][w]["median"]), 3)
+                          for w in ("split_us", "us_per_call")} for c in cases}
+    print(json.dumps({"compare": table, "aa_spread_us": aa, "rounds": args.rounds, "reps": args.kernel_reps,
+                      "order": "alternating (forward, reversed)", "provenance": provenance(torch)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -656,6 +803,9 @@ def main():
                     help="time va_sample_accept (sampling + acceptance) instead of the attention sweep")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (HBM counter calibration)")
+    ap.add_argument("--compare", nargs="+", metavar="LIB",
+                    help="time these builds of the library against the built one (ABBA rounds, A/A arm)")
+    ap.add_argument("--rounds", type=int, default=4, help="--compare: rounds (alternating order)")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
@@ -688,6 +838,9 @@ def main():
         return
     if args.sampler:
         bench_sampler(torch, va, synth, dev, cpu=not args.no_cpu_baseline)
+        return
+    if args.compare:
+        compare_libraries(torch, va, synth, dev, args)
         return
     contexts = args.ctx or CONTEXTS
     stream = torch.cuda.current_stream()
@@ -939,6 +1092,8 @@ def main():
                                  "avg_launch_us": round(probe_ms / launches * 1e3, 2),
                                  "split_frac_of_ceiling": round(achieved / read_ceiling, 4)}}
 
+    clocks = _amd_smi_clocks()
+
     # ---------------- pass D: the other configurations ----------------
     other = bench_other_configs(torch, va, synth, dev)
 
@@ -1007,6 +1162,7 @@ def main():
         "eager_launch_ms_per_step": round(eager_ms_per_step, 4),
         "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "sweep": sweep, "other_configs": other,
         "wall_s_timed": round(t_wall, 4), "kernel_hash": kernel_hash(),
+        "provenance": provenance(torch, clocks),
     }
     print(json.dumps(line), flush=True)
 

@@ -524,7 +524,8 @@ def va_accept(p_ids, p_probs, p_kept, p_tokens, q_ids, q_probs, q_kept, drafts, 
 def va_sample_accept(logits, q_ids, q_probs, q_kept, drafts, top_k=20, top_p=0.95, temperature=1.0, seed=0,
                      first_position=0, purpose=PURPOSE_TARGET, workspace=None, out=None, accepted=None,
                      out_tokens=None, stream=None):
-    """va_sample of the n verification rows, then the acceptance, in two launches.
+    """va_sample of the n verification rows and the acceptance in one launch (the
+    last row's merging workgroup runs the acceptance).
     Returns (dict as va_sample, accepted [1], out_tokens [n])."""
     import torch
     p, ws, out = _sample_call_args(logits, top_k, top_p, temperature, seed, first_position, purpose, workspace, out)

@@ -25,9 +25,13 @@ static inline int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 // at 4K keys, 128 at 16K (1.4 us per pair faster than 256), 176 at 32K; for
 // the 96-row tree over four KV heads 16 / 32 / 64 at 2K / 8K / 32K.  The
 // count is kept a multiple of 8 (one share per XCD) from 8 up and capped at
-// one workgroup per CU over all KV heads (more than one per CU measured
-// slower).  Where the fit comes within a quarter of one granule per split
-// (short reads: 33 granules at 1K keys) every split takes one granule.
+// one workgroup per CU over all KV heads.  Two workgroups of the 48-row
+// kernel fit on a CU (124 VGPRs and 64 KiB of LDS each), but twice the
+// splits write and read back twice the partials: pairs measured 9.7 / 14.9
+// / 15.5 / 27.6 us at 16K / 32K / 64K / 192K keys against 8.9 / 11.1 / 13.2
+// / 24.1 us at one workgroup per CU.  Where the fit comes within a quarter
+// of one granule per split (short reads: 33 granules at 1K keys) every split
+// takes one granule.
 static const int64_t kWorkgroupsPerCU = 1;
 
 // round(sqrt(chunks * k_num / k_den)) exactly: the largest s with

@@ -1001,6 +1001,10 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
 
   float M = -INFINITY, den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // the sink logit (used by wave 0's merge lanes, whose split group is 0 and
+  // so always runs the first batch) is loaded right after that batch's
+  // partials and used only at the end: no round trip of its own
+  float sink_raw = -INFINITY;
   for (int s0 = sg; s0 < S; s0 += kCombNSG * BATCH) {
     f32x2 mlv[BATCH];
     f32x4 ov[BATCH];
@@ -1015,6 +1019,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
       ov[j] = *(const f32x4 *)(ob + se * o_step);
       mlv[j][0] += s < S ? 0.f : -INFINITY;
     }
+    if (s0 == sg && sinkp && t < kCombDQ) sink_raw = sinkp[h];
     asm volatile("" ::: "memory");  // keeps every load of the batch above the first use
     float bm = M;
 #pragma unroll
@@ -1053,7 +1058,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
   }
 
   if (t < kCombDQ) {  // wave 0, one lane per dq: merge the waves and the sink
-    const float sink2 = sinkp ? sinkp[h] * LOG2E_F : -INFINITY;
+    const float sink2 = sinkp ? sink_raw * LOG2E_F : -INFINITY;
     float Mt = sink2;
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
     float dt = 0.f;
@@ -1089,10 +1094,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
 // kComb1WaveBatch (no LDS merge, no barrier); else four waves.  The batch is
 // the smallest power of two that covers S in one round (fewer instructions
 // for short reads); larger S loop over rounds of kCombMaxBatch.
-#ifndef VA_COMB_1WAVE_BATCH
-#define VA_COMB_1WAVE_BATCH 8
-#endif
-constexpr int kComb1WaveBatch = VA_COMB_1WAVE_BATCH;
+constexpr int kComb1WaveBatch = 8;
 
 template <int WAVES, bool STATE>
 hipError_t launch_combine_w(const CombineArgs &a, dim3 grid, int per, hipStream_t stream) {
