@@ -92,7 +92,7 @@ def _waves(name):
     m = re.match(r".*split_kernel<(\d+), (\d+), (\d+), (\d+), (\d+),", name)
     if m:
         _, w, fmt, _, npw = map(int, m.groups())
-        return w + (1 if fmt == 1 else 0) + npw
+        return w + (2 if fmt == 1 else 0) + npw
     m = re.match(r".*combine_kernel<(\d+), (\d+),", name)
     if m:
         return int(m.group(2))

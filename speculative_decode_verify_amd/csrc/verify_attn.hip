@@ -4,8 +4,8 @@
 //   split_kernel    one workgroup per (split, KV head); one wave64 per 16
 //                   query matrix rows walks the split's 32-key chunks, which
 //                   one or two producer waves stream into a ring of LDS
-//                   stages by LDS DMA (for quantised caches a decoder wave
-//                   converts each staged chunk to bf16 tiles); QK^T and PV
+//                   stages by LDS DMA (for quantised caches two decoder
+//                   waves convert each staged chunk to bf16 tiles); QK^T and PV
 //                   run on MFMA 16x16x32 bf16 with FP32 accumulation; each
 //                   wave writes its rows' partials (m, l, O) directly.
 //   combine_kernel  one workgroup per (row, query head, 32-wide slice of D):
@@ -255,11 +255,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *p) {
 //   Consumers, waves 0..W-1: wave w owns query matrix rows [16w, 16w + 16)
 //     for the whole split and keeps their online-softmax state in registers;
 //     every consumer walks all of the split's 32-key chunks in order.
-//   Decoders (quantised formats, NDW = 1), waves W..W+NDW-1: convert each
-//     staged chunk to bf16 tiles one chunk ahead of the consumers, a share
-//     each.  Waves go to the four SIMDs in turn, so with six consumers wave
-//     W shares a SIMD that holds one consumer, not two, and the conversion
-//     overlaps the consumers' steps.
+//   Decoders (quantised formats, NDW = 2), waves W..W+NDW-1: convert each
+//     staged chunk to bf16 tiles one chunk ahead of the consumers, half of
+//     it each.  Waves go to the four SIMDs in turn, so with six consumers
+//     the two decoders share the two SIMDs that hold one consumer each, and
+//     the conversion overlaps the consumers' steps.
 //   Producers, waves W+NDW..W+NDW+NPW-1: fill a ring of NST LDS stages (chunk j in
 //     stage j % NST) with the chunks' K and V tiles by LDS DMA, NST - 1
 //     chunks ahead of the consumers; each producer issues its share of every
@@ -319,7 +319,7 @@ __device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
 
 template <int D, int W, int FMT, int NST, int NPW, bool STATE, bool APP>
-__global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_kernel(const SplitArgs a) {
   static_assert(!APP || (FMT == 0 && NPW == 2), "append: bf16 tiles, one producer per tile kind");
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
   constexpr int KROW = G::KROW, PIECES = G::PIECES, RPI = G::RPI, NDMA = G::NDMA;
   constexpr int kTileB = G::kTileB, kStageB = G::kStageB, kVm = G::kVm;
   static_assert(NST >= 2, "a ring of at least two stages");
-  constexpr int NDW = FMT == 1 ? 1 : 0;  // decoder waves
+  constexpr int NDW = FMT == 1 ? 2 : 0;  // decoder waves
   constexpr int U = 2 * NDMA / NPW;           // DMA instructions per chunk and producer
   constexpr int kVmP = U + (FMT == 1 ? 1 : 0);  // the same, with the quantised scales
   static_assert(FMT == 0 || NPW == 1, "the scale DMA belongs to a single producer");
@@ -434,13 +434,14 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
         const int u = lane + 64 * (NDW * i + d);
         const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
         const u32x4 c = codes[i];
-        if (64 * (NDW * i) < 8 * kChunk) {  // INT8 values: exact in bf16 (|code| <= 127)
+        if (64 * (NDW * i + d) < 8 * kChunk) {  // INT8 values times the token's scale, rounded to bf16
+          const float sc = ((const float *)(qs + 2 * kTileB))[row];
           u32x4 h[2];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t w = c[e];
-            const float f0 = (float)((int32_t)(w << 24) >> 24), f1 = (float)((int32_t)(w << 16) >> 24);
-            const float f2 = (float)((int32_t)(w << 8) >> 24), f3 = (float)((int32_t)w >> 24);
+            const float f0 = (float)((int32_t)(w << 24) >> 24) * sc, f1 = (float)((int32_t)(w << 16) >> 24) * sc;
+            const float f2 = (float)((int32_t)(w << 8) >> 24) * sc, f3 = (float)((int32_t)w >> 24) * sc;
             h[e >> 1][2 * (e & 1)] = pack_bf16x2(f0, f1);
             h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
           }
@@ -788,7 +789,6 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
     // ---- V^T operands: lane (i16 = d within block md, g4) takes the keys
     //      {4g..4g+3, 16+4g..16+4g+3} of column d ----
     bf16x8 vop[MD];
-    float vs[8];
     if constexpr (FMT == 0) {
       // Two transpose reads per block: lane s of group g4 addresses row
       // 4*g4 + s/4 (then +16), columns 16*md + 4*(s%4) .. +3, so output lane
@@ -817,9 +817,6 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
         const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
         vop[md] = __builtin_bit_cast(bf16x8, w);
       }
-      const float *sct = (const float *)(vt + kTileB);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) vs[t] = sct[t < 4 ? 4 * g4 + t : 16 + 4 * g4 + (t - 4)];
     }
 
     // ---- S^T = K Q^T ----
@@ -833,6 +830,8 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
     }
 
     // ---- scale, boundary mask, row maximum ----
+    // (The exponent below subtracts the maximum from the same rounded
+    // products, so a row's largest key gets p = 1 exactly.)
     float x[8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -879,10 +878,6 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 1 : 0))) void split_ker
       psum += p[t];
     }
     lrow += psum;
-    if constexpr (FMT == 1) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) p[t] *= vs[t];
-    }
     u32x4 pw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
@@ -1250,7 +1245,7 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
   dim3 grid(a.splits, a.kv_heads);
-  constexpr int NDW = FMT == 1 ? 1 : 0;
+  constexpr int NDW = FMT == 1 ? 2 : 0;
   hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE, APP>), grid, dim3(64 * (W + NDW + NPW)), 0, stream,
                      a);
   return hipGetLastError();
