@@ -760,10 +760,11 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   auto fk = [](int row) { return row & (PIECES - 1); };
   auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
 
-  auto step = [&](int32_t n, const uint8_t *kt) {
+  // kt: the chunk's staged tiles; db: its decoded-tile buffer (quantised formats)
+  auto step = [&](int32_t n, const uint8_t *kt, int db) {
     const uint8_t *vt = kt + kTileB;
     const int32_t c0 = (c_first + n) * kChunk;
-    const uint8_t *dk = dec + (n & 1) * 2 * kDecTile;  // decoded tiles (quantised formats)
+    const uint8_t *dk = dec + db * 2 * kDecTile;  // decoded tiles (quantised formats)
     const uint8_t *dv = dk + kDecTile;
 
     // ---- K operands: A operand of block mb is keys 16*mb + i16 ----
@@ -889,11 +890,18 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   };
 
   if constexpr (FMT == 1) wg_barrier();  // chunk 0 is staged (the decoders convert it)
-  int st = 0;  // stage of chunk n
-  for (int32_t n = 0; n < nch; ++n) {
-    wg_barrier();  // chunk n is in LDS (decoded); every consumer has left chunk n - 1
-    if (active) step(n, smem + st * kStageB);
-    st = st + 1 == NST ? 0 : st + 1;
+  // Chunk n sits in stage n % NST (and decoded buffer n % 2): the loop is
+  // unrolled over the stages, so each copy reads LDS at constant offsets
+  // from lane bases computed once (no address arithmetic per chunk).
+  static_assert(NST % 2 == 0, "decoded buffers alternate with the chunk index");
+  for (int32_t n0 = 0; n0 < nch; n0 += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      if (n0 + j < nch) {
+        wg_barrier();  // chunk n0 + j is in LDS (decoded); every consumer has left the one before
+        if (active) step(n0 + j, smem + j * kStageB, j & 1);
+      }
+    }
   }
 
   // ---------------- partials of this wave's live rows ----------------
