@@ -76,6 +76,11 @@ def library_path():
     return _LIB_PATH
 
 
+def trace_library_path():
+    """The trace build (phase timestamps; include/verify_probe.h)."""
+    return os.path.join(os.path.dirname(_LIB_PATH), "libverify_attn_trace.so")
+
+
 def load_library():
     """Load libverify_attn.so (raises if it is missing)."""
     global _LIB

@@ -24,6 +24,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libverify_attn.so")
+# the same sources with VA_PHASE_TRACE: per-workgroup phase timestamps
+# (include/verify_probe.h); loaded only by `bench.py --phases`
+TRACE_LIB = os.path.join(LIB_DIR, "libverify_attn_trace.so")
 
 SOURCES = ["verify_attn.hip", "sample.hip", "probe.hip", "plan.cpp"]
 
@@ -66,19 +69,28 @@ def _hipcc_version():
         return None
 
 
-def build(verbose=False):
+def build(verbose=False, trace=True):
+    """Compile the library (and, with trace, its trace build: the two hipcc
+    runs go in parallel)."""
     os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS,
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libverify_attn.so")
-    os.replace(tmp, LIB)
+    jobs = []
+    for out, extra in [(LIB, [])] + ([(TRACE_LIB, ["-DVA_PHASE_TRACE"])] if trace else []):
+        cmd = [hipcc(), *HIPCC_FLAGS, *extra,
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+               *[os.path.join(CSRC, s) for s in SOURCES], "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for out, p in jobs:
+        log = p.communicate()[0]
+        if p.returncode != 0:
+            sys.stderr.write(log)
+            failed.append(os.path.basename(out))
+    if failed:
+        raise RuntimeError(f"hipcc failed building {', '.join(failed)}")
+    for out, _ in jobs:
+        os.replace(out + ".tmp", out)
     rev, dirty = _git_revision()
     info = {"git_revision": rev, "worktree_modified": dirty, "hipcc": _hipcc_version(),
             "flags": HIPCC_FLAGS, "built_at_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}

@@ -318,16 +318,43 @@ __device__ __forceinline__ void pin(int64_t x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(float x) { asm volatile("" ::"s"(x)); }
 __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); }
 
+// Phase trace (builds with VA_PHASE_TRACE only; see include/verify_probe.h):
+// lane 0 of a chosen wave stores the 100 MHz constant-rate clock
+// (s_memrealtime, the same on every CU) into slot `slot` of its workgroup's
+// record.  Records: split_kernel 8 slots per workgroup, combine_kernel 8.
+#ifdef VA_PHASE_TRACE
+constexpr int kTraceWG = 8192;
+__device__ uint64_t va_trace_split[kTraceWG * 8];
+__device__ uint64_t va_trace_comb[kTraceWG * 8];
+__device__ __forceinline__ uint64_t trace_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ void trace_put(uint64_t *rec, int slot, uint64_t v, bool lane0) {
+  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  if (lane0 && wg < kTraceWG) rec[wg * 8 + slot] = v;
+}
+#define VA_TRACE(rec, slot, lane0) trace_put(rec, slot, trace_now(), lane0)
+#define VA_TRACE_VAL(rec, slot, v, lane0) trace_put(rec, slot, v, lane0)
+#else
+#define VA_TRACE(rec, slot, lane0) ((void)0)
+#define VA_TRACE_VAL(rec, slot, v, lane0) ((void)0)
+#endif
+
+// Decoder waves of the quantised formats.
+template <int FMT>
+constexpr int decoders_for() { return FMT == 1 ? 2 : 0; }
+
 template <int D, int W, int FMT, int NST, int NPW, bool STATE, bool APP>
-__global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_kernel(const SplitArgs a) {
   static_assert(!APP || (FMT == 0 && NPW == 2), "append: bf16 tiles, one producer per tile kind");
+#ifdef VA_PHASE_TRACE
+  const uint64_t t_entry = trace_now();
+#endif
   using G = StageGeom<D, FMT>;
   constexpr int KS = D / 32;  // QK contraction steps
   constexpr int MD = D / 16;  // O^T row blocks over d
   constexpr int KROW = G::KROW, PIECES = G::PIECES, RPI = G::RPI, NDMA = G::NDMA;
   constexpr int kTileB = G::kTileB, kStageB = G::kStageB, kVm = G::kVm;
   static_assert(NST >= 2, "a ring of at least two stages");
-  constexpr int NDW = FMT == 1 ? 2 : 0;  // decoder waves
+  constexpr int NDW = decoders_for<FMT>();
   constexpr int U = 2 * NDMA / NPW;           // DMA instructions per chunk and producer
   constexpr int kVmP = U + (FMT == 1 ? 1 : 0);  // the same, with the quantised scales
   static_assert(FMT == 0 || NPW == 1, "the scale DMA belongs to a single producer");
@@ -340,7 +367,11 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   constexpr int kDecRow = 2 * D;                         // bf16 bytes per key row
   constexpr int kDecTile = kChunk * kDecRow;             // one decoded K or V tile
   constexpr int kDecB = FMT == 1 ? 2 * 2 * kDecTile : 0;  // two buffers of K and V
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * kStageB + kDecB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kDecB + NST * kStageB];
+  // The decoded tiles sit at the start of LDS, below 64 KiB, so the
+  // consumers' reads of them take their buffer offset as an instruction
+  // immediate; the staged ring follows.
+  uint8_t *const ring = smem + kDecB;
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps chunk indices and mask decisions in scalar registers
@@ -409,7 +440,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   // in its staged slot q, expanded to two bf16 halves at 16-byte positions
   // (2q + half) ^ (row % 16), so that the 16 lanes reading one operand hit
   // 16 different positions.
-  uint8_t *const dec = smem + NST * kStageB;
+  uint8_t *const dec = smem;
   auto fv0 = [](int row) { return (2 * row) & 14; };
   // Decoder d converts its share of chunk n: of the 16 * kChunk units of 16
   // codes (V first, then K), the blocks of 64 consecutive units with index
@@ -419,7 +450,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   constexpr int NU = kUnits / 64 / (NDW > 0 ? NDW : 1);
   auto decode = [&](int32_t n, int d) {
     if constexpr (FMT == 1) {
-      const uint8_t *qs = smem + (n % NST) * kStageB;
+      const uint8_t *qs = ring + (n % NST) * kStageB;
       uint8_t *dk = dec + (n & 1) * 2 * kDecTile;
       uint8_t *dv = dk + kDecTile;
       u32x4 codes[NU];
@@ -537,7 +568,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
       auto overlay = [&](int32_t n) {
         const int32_t c0 = (c_first + n) * kChunk;
         if (new0 >= c0 + kChunk || new0 + live_rows <= c0) return;
-        uint8_t *tile = smem + (n % NST) * kStageB + (PW == 0 ? 0 : kTileB);
+        uint8_t *tile = ring + (n % NST) * kStageB + (PW == 0 ? 0 : kTileB);
 #pragma unroll
         for (int i = 0; i < APASS; ++i) {
           const int rr = (64 * i + lane) / PIECES;
@@ -575,7 +606,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
         const int64_t row0 = chunk_row(c0);
         const uint8_t *kc = kbase + row0 * row_stride;
         const uint8_t *vc = vbase + row0 * row_stride;
-        uint8_t *stg = smem + st * kStageB + 1024 * PW * U;
+        uint8_t *stg = ring + st * kStageB + 1024 * PW * U;
         if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
 #pragma unroll
           for (int i = 0; i < U; ++i) dma16((PW * U + i >= NDMA ? vc : kc) + off[i], stg + 1024 * i);
@@ -590,12 +621,13 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
         }
         if constexpr (FMT == 1) {
           const float *sc = vsc + (int64_t)kvh * vsc_stride + row0;
-          dma4(sc + clampx(lane & 31, c0), smem + st * kStageB + 2 * kTileB);
+          dma4(sc + clampx(lane & 31, c0), ring + st * kStageB + 2 * kTileB);
         }
       };
 #pragma unroll
       for (int j = 0; j < NST - 1; ++j)
         if (j < nch) issue(j, j);
+      VA_TRACE(va_trace_split, 2, PW == 0 && lane == 0);  // first chunks' DMA issued
       if constexpr (FMT == 1) {
         // the decoders convert chunk n + 1 right after barrier n, so chunk 0
         // must have landed before an extra first barrier, and chunk n + 1
@@ -652,6 +684,8 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
 
   // ================= consumers =================
   chunk_range();
+  VA_TRACE_VAL(va_trace_split, 0, t_entry, threadIdx.x == 0);  // kernel entry
+  VA_TRACE(va_trace_split, 1, threadIdx.x == 0 && nch >= 0);   // arguments in registers
 
   // lane column i16 of this wave is query matrix row m = 16*wave + i16 =
   // r*G + (h - kvh*G); live matrix rows are [0, live_rows * G).
@@ -716,7 +750,10 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
       x[j] = u + v;
       x[j + 16] = u - v;
     }
-    const float inv = 0.08838834764831845f;  // 1/sqrt(128)
+    // 1/sqrt(128) and the softmax scale (log2 units) in one factor: the
+    // rotated q is rounded to bf16 either way, and the scores then come
+    // out of the MFMA already scaled.
+    const float inv = 0.08838834764831845f * scale_log2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 w;
@@ -754,11 +791,40 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   f32x4 o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) o[md] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float mref = -INFINITY, mtrue = -INFINITY, lrow = 0.f;
+  // mref: the row's reference maximum (log2 units, uniform over the row's
+  // four lane groups); mlane: this lane's running maximum of its raw
+  // scores; lrow: this lane's share of the row's sum of weights.
+  float mref = -INFINITY, mlane = -INFINITY, lrow = 0.f;
+  // scores times cs are in log2 units (quantised caches carry the scale in q)
+  const float cs = FMT == 1 ? 1.f : scale_log2;
 
   // Swizzles of the staged tiles (must match the producer's).
   auto fk = [](int row) { return row & (PIECES - 1); };
   auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
+
+  // Quantised formats: each lane's byte offsets of its decoded K and V
+  // operands within a buffer, computed once; the buffer's own offset is a
+  // constant of each unrolled step, so a read needs no address arithmetic.
+  // (The empty asm keeps each sum in a register instead of letting the
+  // compiler re-add its two parts at every read.)
+  uint32_t dko[KS / 2][2], dvo[MD];
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int kp2 = 0; kp2 < KS / 2; ++kp2)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int q = (4 * kp2 + g4) ^ fk(i16);
+        dko[kp2][half] = (uint32_t)(i16 * kDecRow + 16 * ((2 * q + half) ^ (i16 & 15)));
+        asm volatile("" : "+v"(dko[kp2][half]));
+      }
+    const int rowA = 4 * g4 + (i16 >> 2);
+    const int F = fv0(rowA) >> 1;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      dvo[md] = (uint32_t)(rowA * kDecRow + 8 * (i16 & 3) + 32 * (md ^ F));
+      asm volatile("" : "+v"(dvo[md]));
+    }
+  }
 
   // kt: the chunk's staged tiles; db: its decoded-tile buffer (quantised formats)
   auto step = [&](int32_t n, const uint8_t *kt, int db) {
@@ -777,14 +843,13 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
         for (int ks = 0; ks < KS; ++ks)
           kop[mb][ks] = *(const bf16x8 *)(kt + row * KROW + 16 * ((4 * ks + g4) ^ fk(row)));
       } else {
+        // staged piece (16 codes): first 8 -> step 2*kp2, last 8 -> step
+        // 2*kp2+1; rows 16 + i16 repeat row i16's swizzle 16 rows lower
 #pragma unroll
-        for (int kp2 = 0; kp2 < KS / 2; ++kp2) {
-          // staged piece (16 codes): first 8 -> step 2*kp2, last 8 -> step 2*kp2+1
-          const int q = (4 * kp2 + g4) ^ fk(row);
+        for (int kp2 = 0; kp2 < KS / 2; ++kp2)
 #pragma unroll
           for (int half = 0; half < 2; ++half)
-            kop[mb][2 * kp2 + half] = *(const bf16x8 *)(dk + row * kDecRow + 16 * ((2 * q + half) ^ (row & 15)));
-        }
+            kop[mb][2 * kp2 + half] = *(const bf16x8 *)(dk + 16 * mb * kDecRow + dko[kp2][half]);
       }
     }
     // ---- V^T operands: lane (i16 = d within block md, g4) takes the keys
@@ -807,12 +872,9 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
       }
     } else {
       // the decoded bf16 tile, read as for bf16 caches
-      const int rowA = 4 * g4 + (i16 >> 2);
-      const int F = fv0(rowA) >> 1;
-      const uint8_t *vb = dv + rowA * kDecRow + 8 * (i16 & 3);
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const uint8_t *pa = vb + 32 * (md ^ F);
+        const uint8_t *pa = dv + dvo[md];
         const u32x2 lo = lds_read_tr16(pa);
         const u32x2 hi = lds_read_tr16(pa + 16 * kDecRow);
         const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
@@ -830,14 +892,12 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
       s[mb] = acc;
     }
 
-    // ---- scale, boundary mask, row maximum ----
-    // (The exponent below subtracts the maximum from the same rounded
-    // products, so a row's largest key gets p = 1 exactly.)
+    // ---- boundary mask, this lane's maximum ----
     float x[8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * mb + e] = s[mb][e] * scale_log2;
+      for (int e = 0; e < 4; ++e) x[4 * mb + e] = s[mb][e];
     if (!(c0 >= full_lo && c0 + kChunk <= full_hi)) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -849,36 +909,43 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
         x[t] = ((in_row | in_tree) & 1u) ? x[t] : -INFINITY;
       }
     }
-    float mx = x[0];
+    float lm = x[0];
 #pragma unroll
-    for (int t = 1; t < 8; ++t) mx = fmaxf(mx, x[t]);
-    mx = wave_max16x4(mx);
+    for (int t = 1; t < 8; ++t) lm = fmaxf(lm, x[t]);
+    mlane = fmaxf(mlane, lm);
 
     // ---- lazy reference maximum ----
     // Exponents are taken against mref, which moves only when a row's chunk
     // maximum exceeds it by more than kTau (so every p stays <= 2^kTau);
     // moving it rescales that row's O and l (a rare, wave-uniform branch).
-    mtrue = fmaxf(mtrue, mx);
-    const bool need = (mref != -INFINITY) && (mx > mref + kTau);
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float nref = need ? mx : mref;
-      const float alpha = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - nref);
-      lrow *= alpha;
+    // The row maximum (across the row's lane groups) is formed only when
+    // some lane's own maximum could move its row's reference, or a row has
+    // none yet; otherwise no row's maximum exceeds mref + kTau either.
+    // Rounding is monotone, so max(x) * cs is the maximum of the scaled x.
+    if (__builtin_amdgcn_ballot_w64(mref == -INFINITY || lm * cs > mref + kTau) != 0) {
+      const float mx = wave_max16x4(lm) * cs;
+      const bool need = (mref != -INFINITY) && (mx > mref + kTau);
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float nref = need ? mx : mref;
+        const float alpha = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - nref);
+        lrow *= alpha;
 #pragma unroll
-      for (int md = 0; md < MD; ++md) o[md] *= alpha;
-      mref = nref;
+        for (int md = 0; md < MD; ++md) o[md] *= alpha;
+        mref = nref;
+      }
+      mref = (mref == -INFINITY) ? mx : mref;
     }
-    mref = (mref == -INFINITY) ? mx : mref;
 
     // ---- P^T (B operand of PV) and l ----
+    // One rounding per exponent: the product with the scale and the
+    // subtraction in one FMA (quantised caches: cs = 1, so a row's largest
+    // key gets p = 1 exactly).  The lane's eight weights are summed as a
+    // tree (three dependent adds instead of eight).
     const float m_use = (mref == -INFINITY) ? 0.f : mref;
-    float p[8], psum = 0.f;
+    float p[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      p[t] = __builtin_amdgcn_exp2f(x[t] - m_use);
-      psum += p[t];
-    }
-    lrow += psum;
+    for (int t = 0; t < 8; ++t) p[t] = __builtin_amdgcn_exp2f(fmaf(x[t], cs, -m_use));
+    lrow += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     u32x4 pw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
@@ -894,15 +961,29 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   // unrolled over the stages, so each copy reads LDS at constant offsets
   // from lane bases computed once (no address arithmetic per chunk).
   static_assert(NST % 2 == 0, "decoded buffers alternate with the chunk index");
+#ifdef VA_PHASE_TRACE
+  uint64_t t_bar = 0;  // wave 0's time at the barriers after its first chunk arrived
+#endif
   for (int32_t n0 = 0; n0 < nch; n0 += NST) {
 #pragma unroll
     for (int j = 0; j < NST; ++j) {
       if (n0 + j < nch) {
+#ifdef VA_PHASE_TRACE
+        const uint64_t tb0 = trace_now();
+#endif
         wg_barrier();  // chunk n0 + j is in LDS (decoded); every consumer has left the one before
-        if (active) step(n0 + j, smem + j * kStageB, j & 1);
+#ifdef VA_PHASE_TRACE
+        const uint64_t tb1 = trace_now();
+        if (n0 + j == 0) VA_TRACE_VAL(va_trace_split, 3, tb1, threadIdx.x == 0);  // first chunk in LDS
+        else t_bar += tb1 - tb0;
+#endif
+        if (active) step(n0 + j, ring + j * kStageB, j & 1);
       }
     }
   }
+  VA_TRACE(va_trace_split, 4, threadIdx.x == 0);  // last step issued
+  VA_TRACE_VAL(va_trace_split, 6, t_bar, threadIdx.x == 0);
+  VA_TRACE_VAL(va_trace_split, 7, (uint64_t)nch, threadIdx.x == 0);
 
   // ---------------- partials of this wave's live rows ----------------
   // Normalised to the true maximum M of the split: m = M, l = sum 2^(x - M),
@@ -910,6 +991,7 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
   // reads them.
   if (!active) return;
   const float lt = wave_sum16x4(lrow);
+  const float mtrue = wave_max16x4(mlane) * cs;
   const float f = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mref - mtrue);
   if (row_ok) {
     const int64_t unit = ((int64_t)split * kv_heads + kvh) * mrows + m;
@@ -918,6 +1000,10 @@ __global__ __launch_bounds__(64 * (W + NPW + (FMT == 1 ? 2 : 0))) void split_ker
 #pragma unroll
     for (int md = 0; md < MD; ++md) *(f32x4 *)(op + 16 * md + 4 * g4) = o[md] * f;
   }
+#ifdef VA_PHASE_TRACE
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  VA_TRACE(va_trace_split, 5, threadIdx.x == 0);  // this wave's partials written
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -952,6 +1038,9 @@ __device__ __forceinline__ float xor_sum3(float x) {
 
 template <int BATCH, int WAVES, bool STATE>
 __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a) {
+#ifdef VA_PHASE_TRACE
+  const uint64_t t_entry = trace_now();
+#endif
   constexpr int kCombNSG = 8 * WAVES;  // split groups
   __shared__ f32x4 wacc[WAVES][kCombDQ];
   __shared__ float wm[WAVES], wden[WAVES];
@@ -992,6 +1081,8 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
     if (lsep && blockIdx.y == 0 && t == 0) lsep[(int64_t)r * q_heads + h] = -INFINITY;
     return;
   }
+  VA_TRACE_VAL(va_trace_comb, 0, t_entry, t == 0);
+  VA_TRACE(va_trace_comb, 1, t == 0);  // arguments in registers (pin() waited for them)
   const int g = h / group;
   const int mrow = r * group + (h - g * group);
   const int64_t stride_unit = (int64_t)kv_heads * mrows;  // units between splits
@@ -1027,6 +1118,12 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
     float bm = M;
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) bm = fmaxf(bm, mlv[j][0]);
+#ifdef VA_PHASE_TRACE
+    if (s0 == sg) {
+      asm volatile("" ::"v"(bm), "v"(ov[BATCH - 1][3]));  // the batch has arrived
+      VA_TRACE(va_trace_comb, 2, t == 0);                // first batch in registers
+    }
+#endif
     if (bm > M) {
       const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - bm);
       den *= alpha;
@@ -1043,6 +1140,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
     }
   }
 
+  VA_TRACE(va_trace_comb, 3, t == 0);  // every batch folded
   // merge the eight split groups of this wave (lanes dq, dq + 8, ..., dq + 56)
   const float Mw = xor_max3(M);
   const float f = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mw);
@@ -1090,6 +1188,10 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
       *(f32x4 *)(outp + d0) = tot / dt;
       if (lse_lane) lsep[(int64_t)r * q_heads + h] = (Mu + __log2f(dt)) * LN2_F;
     }
+#ifdef VA_PHASE_TRACE
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    VA_TRACE(va_trace_comb, 4, t == 0);  // output written
+#endif
   }
 }
 
@@ -1253,7 +1355,7 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
   dim3 grid(a.splits, a.kv_heads);
-  constexpr int NDW = FMT == 1 ? 2 : 0;
+  constexpr int NDW = decoders_for<FMT>();
   hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE, APP>), grid, dim3(64 * (W + NDW + NPW)), 0, stream,
                      a);
   return hipGetLastError();
@@ -1399,6 +1501,20 @@ inline bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
 
 }  // namespace va_detail
 using namespace va_detail;
+
+#ifdef VA_PHASE_TRACE
+// Copies the phase records of the last launches: which = 0 for split_kernel,
+// 1 for combine_kernel; n_wg workgroups (8 uint64 each) to host memory.
+extern "C" int va_trace_read(int which, uint64_t *dst, int n_wg) {
+  if (!dst || n_wg < 0 || n_wg > va_detail::kTraceWG || (which != 0 && which != 1)) return 1;
+  const hipError_t e = which == 0
+                           ? hipMemcpyFromSymbol(dst, HIP_SYMBOL(va_detail::va_trace_split), (size_t)n_wg * 64, 0,
+                                                 hipMemcpyDeviceToHost)
+                           : hipMemcpyFromSymbol(dst, HIP_SYMBOL(va_detail::va_trace_comb), (size_t)n_wg * 64, 0,
+                                                 hipMemcpyDeviceToHost);
+  return e == hipSuccess ? 0 : 2;
+}
+#endif
 
 extern "C" va_status verify_attn_split(const va_plan *plan, const void *q, const void *k, const void *v,
                                        const float *v_scale, int64_t v_scale_head_stride,

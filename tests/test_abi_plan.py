@@ -25,6 +25,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)) - {"sizeof"})
 
 
+# declared in include/verify_probe.h for the trace build of the library only
+TRACE_ONLY = {"va_trace_read"}
+
+
 def test_library_exports_every_declared_symbol():
     lib = va.load_library()
     names = declared_functions()
@@ -32,9 +36,26 @@ def test_library_exports_every_declared_symbol():
                           "verify_attn_split_state", "verify_attn_combine_state",
                           "va_sample", "va_accept", "va_sample_accept", "va_sample_workspace_bytes", "va_read_probe",
                           "verify_attn_plan_query", "verify_attn_plan_split_range", "va_status_string"}
+    assert TRACE_ONLY <= set(names)
     for n in names:
+        if n in TRACE_ONLY:
+            assert not hasattr(lib, n), f"{n}: the product library carries no trace code"
+            continue
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_trace_build_exports_every_declared_symbol():
+    path = _binding.trace_library_path()
+    assert os.path.exists(path), "build() makes the trace library beside the product one"
+    lib = ctypes.CDLL(path)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    lib.va_trace_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+    buf = (ctypes.c_uint64 * 8)()
+    assert lib.va_trace_read(2, buf, 1) == 1          # which must be 0 or 1
+    assert lib.va_trace_read(0, None, 1) == 1         # no destination
+    assert lib.va_trace_read(0, buf, 8193) == 1       # more records than kept
 
 
 def test_status_strings():
