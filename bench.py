@@ -31,7 +31,8 @@ outputs of replica 0.
 Prints one JSON line, with a `provenance` object: GPU name and ISA, compute
 units, ROCm / HIP / torch versions, the library's build record (git revision,
 hipcc version, flags), hashes of the library and the kernel source, the
-command line, and the clocks amd-smi reads right after the timed region.
+command line, and the clock levels the driver's sysfs tables show right after
+the timed region.
 
 `--compare LIB [LIB ...]` times other builds of the library against the
 built one instead (split alone and split + combine pairs per context, cold
@@ -60,6 +61,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep_traffic
 UTIL_FILE = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep_util.json")
 UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT "
                  "SQ_LDS_IDX_ACTIVE")
+WAVE_COUNTERS = "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU"
+INST_COUNTERS = "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU"
 COPY_PROBE_MIB = 1024
 KERNEL_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "verify_attn.hip")
 SAMPLE_SRC = os.path.join(ROOT, "speculative_decode_verify_amd", "csrc", "sample.hip")
@@ -82,23 +85,51 @@ def cold_pool(torch, synth, dev, nbytes, seed, tail=0):
     return pool, n
 
 
-def _amd_smi_clocks():
-    """Current gfx clocks (mean over the XCDs) and the memory clock, from
-    amd-smi (None if it is not available)."""
-    import subprocess
+def _sysfs_device_dir(torch):
+    """The sysfs directory of the GPU torch uses (matched by PCI address),
+    else the first DRM card that exposes clock levels; None if neither."""
+    import glob
     try:
-        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=30)
-        d = json.loads(r.stdout[r.stdout.index("{"):])
-        clk = d["gpu_data"][0]["clock"]
-        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-        mem = clk.get("mem_0", {}).get("clk", {})
-        gmax = next((v["max_clk"]["value"] for k, v in clk.items()
-                     if k.startswith("gfx_") and isinstance(v.get("max_clk"), dict)), None)
-        return {"gfx_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
-                "gfx_mhz_max": gmax, "mem_mhz": mem.get("value") if isinstance(mem, dict) else None,
-                "source": "amd-smi metric --clock, read right after the timed region"}
-    except Exception as e:  # noqa: BLE001
-        return {"error": f"amd-smi unavailable: {type(e).__name__}"}
+        p = torch.cuda.get_device_properties(0)
+        d = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+            return d
+    except Exception:  # noqa: BLE001
+        pass
+    cards = [c for c in sorted(glob.glob("/sys/class/drm/card*/device")) if os.path.exists(os.path.join(c, "pp_dpm_sclk"))]
+    return cards[0] if cards else None
+
+
+def _sysfs_clocks(torch):
+    """Current gfx (sclk) and memory (mclk) clock levels from the driver's
+    sysfs tables (the level marked '*'), read right after the timed region.
+    A file read: the process that holds the GPU starts no other program."""
+    d = _sysfs_device_dir(torch)
+    if d is None:
+        return {"error": "no pp_dpm_sclk in sysfs"}
+
+    def current(name):
+        try:
+            for line in open(os.path.join(d, name)):
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].replace("*", "").strip()
+        except OSError:
+            return None
+        return None
+    return {"sclk": current("pp_dpm_sclk"), "mclk": current("pp_dpm_mclk"),
+            "source": f"{d}/pp_dpm_sclk and pp_dpm_mclk (current level), read right after the timed region"}
+
+
+def _sysfs_product(torch):
+    d = _sysfs_device_dir(torch)
+    for name in ("product_name", "device"):
+        try:
+            v = open(os.path.join(d, name)).read().strip() if d else ""
+            if v:
+                return v if name == "product_name" else f"PCI device {v}"
+        except OSError:
+            pass
+    return None
 
 
 def provenance(torch, clocks=None):
@@ -121,7 +152,7 @@ def provenance(torch, clocks=None):
     if os.path.exists(lib):
         with open(lib, "rb") as f:
             lib_hash = hashlib.sha256(f.read()).hexdigest()[:16]
-    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+    return {"gpu": props.name or _sysfs_product(torch), "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "rocm": rocm, "hip_runtime": torch.version.hip,
             "torch": torch.__version__, "git_revision": build.get("git_revision"),
             "worktree_modified": build.get("worktree_modified"), "hipcc": build.get("hipcc"),
@@ -138,6 +169,136 @@ def kv_bytes(hi):
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def wave_cycles(d, kname, py):
+    """Wave-cycle breakdown of the split kernels from a `--pmc` run of
+    WAVE_COUNTERS (pmc_waves/, log waves.log) and one of INST_COUNTERS
+    (pmc_insts/, insts.log) and, when present, the same two runs of an
+    earlier kernel source (pmc_waves_before/, pmc_insts_before/,
+    waves_before.log, with the revision it was built from in
+    waves_before.rev): the share of wave
+    cycles spent waiting on anything (barriers, memory and LDS counters),
+    waiting on instruction dependencies and issuing VALU, and the
+    instructions issued per MFMA instruction.  The counters are whole-GPU
+    totals per dispatch."""
+    import csv
+    import collections
+    kinds = [("split_kernel<128,3,0,4,2,false>", "sweep (D 128, 3 consumers, bf16)"),
+             ("split_kernel<128,6,0,4,2,false>", "tree (D 128, 6 consumers, bf16)"),
+             ("split_kernel<128,6,1,8,1,false>", "quantised tree (E4M3 keys, INT8 values)")]
+
+    def table(subs, log):
+        paths = [os.path.join(d, sub, "bench_counter_collection.csv") for sub in subs]
+        if not all(os.path.exists(p) for p in paths):
+            return None, None
+        line = None
+        for x in open(os.path.join(d, log)):
+            if x.startswith("{") and '"metric"' in x:
+                line = json.loads(x)
+        vals = collections.defaultdict(lambda: collections.defaultdict(list))
+        for path in paths:
+            for r in csv.DictReader(open(path)):
+                n = kname(r["Kernel_Name"])
+                wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+                for key, _ in kinds:
+                    if key in n:
+                        vals[(key, wgs)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        rows = {}
+        for (key, wgs), v in vals.items():
+            a = {c: sum(x) / len(x) for c, x in v.items()}
+            cyc = a.get("SQ_WAVE_CYCLES", 0.0)
+            mf = a.get("SQ_INSTS_MFMA", 0.0)
+            if not cyc or not mf:
+                continue
+            rows[(key, wgs)] = dict(
+                dispatches=len(v["SQ_WAVE_CYCLES"]), wait_any=100 * a["SQ_WAIT_ANY"] / cyc,
+                wait_inst=100 * a["SQ_WAIT_INST_ANY"] / cyc, valu_active=100 * a["SQ_ACTIVE_INST_VALU"] / cyc,
+                valu_per_mfma=a["SQ_INSTS_VALU"] / mf, lds_per_mfma=a["SQ_INSTS_LDS"] / mf,
+                salu_per_mfma=a["SQ_INSTS_SALU"] / mf, mfma=mf)
+        return rows, line
+
+    after, al = table(("pmc_waves", "pmc_insts"), "waves.log")
+    if after is None:
+        return
+    for log in ("waves.log", "insts.log"):
+        for x in open(os.path.join(d, log)):
+            if x.startswith("{") and '"metric"' in x and json.loads(x)["kernel_hash"] != kernel_hash():
+                raise SystemExit("wave counters of another kernel source")
+    before, bl = table(("pmc_waves_before", "pmc_insts_before"), "waves_before.log")
+    rev = None
+    if before is not None and os.path.exists(os.path.join(d, "waves_before.rev")):
+        rev = open(os.path.join(d, "waves_before.rev")).read().strip()
+    tail = f"-o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline"
+    o = ["# split_kernel wave cycles: waits, VALU and instructions per MFMA", "",
+         f"kernel source sha256[:16]: {kernel_hash()}", "",
+         f"command: rocprofv3 --pmc {WAVE_COUNTERS} -f csv -d <dir>/pmc_waves {tail}",
+         f"command: rocprofv3 --pmc {INST_COUNTERS} -f csv -d <dir>/pmc_insts {tail}", ""]
+    if before is not None:
+        o += [f"before: the same two commands in a checkout of {rev or 'an earlier revision'} "
+              f"(kernel source sha256[:16] {bl['kernel_hash'] if bl else '?'}), library built there with "
+              "`python -m speculative_decode_verify_amd.build`", ""]
+    o += ["Shares are of SQ_WAVE_CYCLES: wait any = SQ_WAIT_ANY (barriers, memory and LDS counters), "
+          "wait inst = SQ_WAIT_INST_ANY (instruction dependencies), VALU = SQ_ACTIVE_INST_VALU. "
+          "Per MFMA = SQ_INSTS_VALU, SQ_INSTS_LDS, SQ_INSTS_SALU over SQ_INSTS_MFMA.", "",
+          "| kernel | workgroups | source | dispatches | wait any % | wait inst % | VALU % | VALU per MFMA | "
+          "LDS per MFMA | SALU per MFMA |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for key, label in kinds:
+        wg = sorted({w for (k, w) in list(after) + list(before or {}) if k == key})
+        for w in wg:
+            for tag, t in (("before", before), ("after", after)):
+                r = (t or {}).get((key, w))
+                if r is None:
+                    continue
+                o.append(f"| {label} | {w} | {tag} | {r['dispatches']} | {r['wait_any']:.1f} | {r['wait_inst']:.1f} | "
+                         f"{r['valu_active']:.1f} | {r['valu_per_mfma']:.2f} | {r['lds_per_mfma']:.2f} | "
+                         f"{r['salu_per_mfma']:.2f} |")
+    name = os.path.join(ROOT, "profiles", "split_kernel_wave_cycles.md")
+    open(name, "w").write("\n".join(o) + "\n")
+    print(f"wrote {name}")
+
+
+def phase_table(d, py):
+    """profiles/split_kernel_phases.md from the `--phases` run (phases.log)."""
+    path = os.path.join(d, "phases.log")
+    if not os.path.exists(path):
+        return
+    line = None
+    for x in open(path):
+        if x.startswith("{") and '"phases"' in x:
+            line = json.loads(x)
+    if line is None:
+        raise SystemExit("no phases line in phases.log")
+    if line["kernel_hash"] != kernel_hash():
+        raise SystemExit("phase records of another kernel source")
+    cols = [("splits", "splits"), ("chunks_per_split", "chunks / split"), ("entry_spread", "entry spread"),
+            ("args", "args"), ("first_dma_issued", "1st DMA issued"), ("chunk0_in_lds", "chunk 0 in LDS"),
+            ("step", "later chunk step"), ("barrier_share", "barrier share of steps"),
+            ("last_step_issued", "last step issued"), ("partials_written", "partials written"),
+            ("split_span", "split span"), ("gap_to_combine", "gap to combine"), ("comb_args", "comb args"),
+            ("comb_first_batch", "comb 1st batch"), ("comb_folded", "comb folded"),
+            ("comb_written", "comb written"), ("comb_span", "comb span"), ("pair_span", "pair span"),
+            ("us_per_call", "us / call (events)")]
+    o = ["# split_kernel / combine_kernel phases (trace build, per-workgroup clock stamps)", "",
+         f"kernel source sha256[:16]: {line['kernel_hash']}", "",
+         f"command: {py} --phases", "",
+         "The trace build (lib/libverify_attn_trace.so, the same sources compiled with VA_PHASE_TRACE) stores "
+         "the 100 MHz constant-rate GPU clock (s_memrealtime, common to all CUs) at phase boundaries, one record "
+         "per workgroup (include/verify_probe.h). Each case replays graphs of 4 back-to-back split + combine "
+         "calls over cold replicas and reads the records of the last pair; values are medians over 12 replays, "
+         "in us. Per-workgroup phases are means over workgroups and measured from that workgroup's entry "
+         "(args, 1st DMA issued, chunk 0 in LDS, comb args / 1st batch / folded / written); 'later chunk step' "
+         "is (last step - chunk 0) / (chunks - 1); 'barrier share' is consumer wave 0's time at barriers over "
+         "that span; 'last step issued', 'partials written' (wave 0) and the spans are from the first "
+         "workgroup's entry; 'gap to combine' runs from the last split workgroup's partials to the first combine "
+         "workgroup's entry. The trace build's own time per call (events) is slightly longer than the "
+         "product's.", "",
+         "| case | " + " | ".join(c[1] for c in cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    for c in line["phases"]:
+        o.append(f"| {c['case']} | " + " | ".join(str(c.get(k)) for k, _ in cols) + " |")
+    name = os.path.join(ROOT, "profiles", "split_kernel_phases.md")
+    open(name, "w").write("\n".join(o) + "\n")
+    print(f"wrote {name}")
 
 
 def sample_hash():
@@ -290,7 +451,7 @@ def summarize_profiles(d):
         kinds = [("split_kernel<128,3,0,4,2,false>", "split: sweep (D 128, 3 consumers, bf16)"),
                  ("split_kernel<64,3,0,8,2,false>", "split: window ring (D 64, 3 consumers)"),
                  ("split_kernel<128,6,0,4,2,false>", "split: tree (D 128, 6 consumers, bf16)"),
-                 ("split_kernel<128,6,1,8,1,false>", "split: quantised tree (6 consumers, 1 decoder)")]
+                 ("split_kernel<128,6,1,8,1,false>", "split: quantised tree (6 consumers, 2 decoders)")]
         tdur = collections.defaultdict(list)
         for (kind, n, wgs), v in dur.items():
             tdur[(kind, wgs)] += v
@@ -341,6 +502,9 @@ def summarize_profiles(d):
     name = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep.md")
     open(name, "w").write("\n".join(out) + "\n")
     print(f"wrote {name} and {TRAFFIC_FILE}")
+
+    wave_cycles(d, kname, py)
+    phase_table(d, py)
 
     st = os.path.join(d, "trace_sampler", "sampler_kernel_trace.csv")
     if os.path.exists(st):
@@ -695,6 +859,164 @@ def bench_other_configs(torch, va, synth, dev, reps=200, replicas=4):
     return out
 
 
+def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
+    """Phase timestamps of split and combine launches from the trace build
+    of the library (lib/libverify_attn_trace.so; include/verify_probe.h):
+    the sweep's seven contexts (as timed above) and the bf16 and quantised
+    trees at 32K / 64K.  Each case captures `graphs` graphs of `pairs`
+    back-to-back split + combine calls over distinct cold replicas and
+    replays them in turn; after each replay the records of its last pair
+    are read.  Reported (us, medians over replays; "mean" over workgroups):
+    the spread of workgroup entries, the arguments' arrival, the first DMA
+    issue, chunk 0's arrival in LDS, the later chunks' steps, the last
+    step, the partials' stores, the gap to the combine's first workgroup
+    and the combine's phases; `us_per_call` times the same graphs with
+    events (the trace build's own speed, for comparison with the product's)."""
+    import ctypes
+    import statistics
+    import numpy as np
+    import speculative_decode_verify_amd._binding as binding
+    product = binding.load_library()
+    binding._LIB = None
+    saved = binding._LIB_PATH
+    binding._LIB_PATH = binding.trace_library_path()
+    lib = binding.load_library()
+    binding._LIB_PATH = saved
+    lib.va_trace_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+    stream = torch.cuda.current_stream()
+    tick_us = 0.01  # s_memrealtime runs at 100 MHz
+
+    def records(which, n):
+        buf = np.zeros((n, 8), dtype=np.uint64)
+        if lib.va_trace_read(which, buf.ctypes.data, n) != 0:
+            raise RuntimeError("va_trace_read failed")
+        return buf.astype(np.int64)
+
+    cases = []
+    for ctx in CONTEXTS:
+        g = synth.gen(2000 + ctx // 1024)
+        live = synth.live_count(g)
+        hi = ctx + live
+        nb = kv_bytes(hi)
+        pool, npool = cold_pool(torch, synth, dev, nb, seed=60_000 + ctx)
+        q = synth.normal_bf16((ROWS, HQ, D), g).to(dev)
+        sink = synth.normal_f32((HQ,), g).to(dev)
+        plan = va.Plan(rows=ROWS, live_rows=live, q_heads=HQ, kv_heads=HKV, head_dim=D, mask="causal",
+                       first_pos=ctx, kv_capacity=CAP, scale=1 / math.sqrt(D))
+
+        def kv_of(i, pool=pool, npool=npool, hi=hi):
+            fl = pool.view(torch.bfloat16)
+            kb = (i % npool) * hi * 2 * D
+            vb = kb + hi * D
+            return fl[kb:kb + hi * D].view(HKV, hi, D), fl[vb:vb + hi * D].view(HKV, hi, D), None
+        cases.append(dict(name=f"sweep {ctx // 1024}K", plan=plan, q=q, sink=sink, kv_of=kv_of, npool=npool,
+                          rows=ROWS, hq=HQ, d=D, live=live, keep=pool))
+    g = synth.gen(9500)
+    for quant, P in ((False, 32768), (True, 65536)):
+        kw = dict(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=P,
+                  parent=synth.random_tree(16, g), kv_capacity=P + 16 + 64, scale=1 / math.sqrt(128))
+        if quant:
+            kw["kv_fmt"] = "e4m3_wht_i8"
+        plan = va.Plan(**kw)
+        hkv, d, slots = 4, 128, kw["kv_capacity"]
+        kvb = hkv * slots * d * (1 if quant else 2)
+        per = 2 * kvb + (hkv * slots * 4 if quant else 0)
+        n = max(REPLICAS, -(-POOL_BYTES // per))
+        pool = torch.empty(n * per, dtype=torch.uint8, device=dev)
+        if quant:
+            kv_all = pool.view(n, per)
+            kv_all[:, :kvb] = torch.randint(0, 126, (n, kvb), dtype=torch.uint8, device=dev)
+            kv_all[:, kvb:2 * kvb] = torch.randint(-127, 128, (n, kvb), dtype=torch.int8, device=dev).view(torch.uint8)
+            kv_all[:, 2 * kvb:] = (torch.rand((n, hkv * slots), device=dev) * 0.02).view(torch.uint8)
+        else:
+            flat = pool.view(torch.bfloat16)
+            for off in range(0, flat.numel(), 1 << 27):
+                m = min(1 << 27, flat.numel() - off)
+                flat[off:off + m] = synth.normal_bf16_device((m,), 61_000 + off // (1 << 27), dev)
+
+        def kv_of(i, pool=pool, n=n, per=per, kvb=kvb, quant=quant, hkv=hkv, slots=slots, d=d):
+            base = pool[(i % n) * per:(i % n + 1) * per]
+            if quant:
+                return (base[:kvb].view(hkv, slots, d), base[kvb:2 * kvb].view(torch.int8).view(hkv, slots, d),
+                        base[2 * kvb:].view(torch.float32).view(hkv, slots))
+            kv = base.view(torch.bfloat16).view(2, hkv, slots, d)
+            return kv[0], kv[1], None
+        cases.append(dict(name=("quantised tree 64K" if quant else "tree 32K"), plan=plan,
+                          q=synth.normal_bf16((16, 24, 128), g).to(dev), sink=None, kv_of=kv_of, npool=n,
+                          rows=16, hq=24, d=128, live=16, keep=pool))
+
+    out = []
+    binding._LIB = lib
+    try:
+        for c in cases:
+            plan = c["plan"]
+            ws = va.workspace_for(plan, dev)
+            o = torch.empty((c["rows"], c["hq"], c["d"]), dtype=torch.float32, device=dev)
+            lse = torch.empty((c["rows"], c["hq"]), dtype=torch.float32, device=dev)
+            nsw = plan.splits * plan.problem.kv_heads
+            ncw = c["rows"] * c["hq"] * (c["d"] // 32)
+            grs = []
+            for gi in range(graphs):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    for j in range(pairs):
+                        k, v, vs = c["kv_of"](gi * pairs + j)
+                        cur = torch.cuda.current_stream()
+                        va.verify_attn_split(plan, c["q"], k, v, ws, v_scale=vs, stream=cur)
+                        va.verify_attn_combine(plan, ws, o, lse=lse, sink=c["sink"], stream=cur)
+                grs.append(gr)
+            for gr in grs:
+                gr.replay()
+            torch.cuda.synchronize()
+            rows = []
+            for r in range(replays):
+                grs[r % graphs].replay()
+                torch.cuda.synchronize()
+                sp = records(0, nsw)
+                cb = records(1, ncw)
+                live_wg = (np.arange(ncw) % (c["rows"] * c["hq"])) // c["hq"] < c["live"]
+                cb = cb[live_wg]
+                t0 = sp[:, 0].min()
+                busy = sp[:, 7] > 0
+                steps = np.maximum(sp[busy, 7] - 1, 1)
+                rows.append(dict(
+                    entry_spread=(sp[:, 0].max() - t0),
+                    args=(sp[:, 1] - sp[:, 0]).mean(),
+                    first_dma_issued=(sp[busy, 2] - sp[busy, 0]).mean(),
+                    chunk0_in_lds=(sp[busy, 3] - sp[busy, 0]).mean(),
+                    chunk0_in_lds_last=(sp[busy, 3].max() - t0),
+                    step=((sp[busy, 4] - sp[busy, 3]) / steps).mean(),
+                    barrier_share=(sp[busy, 6] / np.maximum(sp[busy, 4] - sp[busy, 3], 1)).mean(),
+                    last_step_issued=(sp[busy, 4] - t0).mean(),
+                    partials_written=(sp[busy, 5] - t0).mean(),
+                    split_span=(sp[busy, 5].max() - t0),
+                    gap_to_combine=(cb[:, 0].min() - sp[busy, 5].max()),
+                    comb_entry_spread=(cb[:, 0].max() - cb[:, 0].min()),
+                    comb_args=(cb[:, 1] - cb[:, 0]).mean(),
+                    comb_first_batch=(cb[:, 2] - cb[:, 0]).mean(),
+                    comb_folded=(cb[:, 3] - cb[:, 0]).mean(),
+                    comb_written=(cb[:, 4] - cb[:, 0]).mean(),
+                    comb_span=(cb[:, 4].max() - cb[:, 0].min()),
+                    pair_span=(cb[:, 4].max() - t0)))
+            med = {k: round(statistics.median(float(x[k]) for x in rows) * (1 if k == "barrier_share" else tick_us), 3)
+                   for k in rows[0]}
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for gr in grs:
+                gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            med["us_per_call"] = round(a.elapsed_time(b) * 1e3 / (graphs * pairs), 3)
+            out.append(dict(case=c["name"], splits=plan.splits, workgroups=nsw, chunks_per_split=
+                            round(float(plan.info["chunks"]) / plan.splits, 2) if "chunks" in plan.info else None,
+                            **med))
+            print(json.dumps(out[-1]), flush=True)
+            del grs, ws
+    finally:
+        binding._LIB = product
+    return out
+
+
 def compare_libraries(torch, va, synth, dev, args):
     """Split alone and split + combine pairs of several library builds, per
     context, over cold pools (as pass B), in alternating order with the
@@ -806,6 +1128,8 @@ def main():
     ap.add_argument("--compare", nargs="+", metavar="LIB",
                     help="time these builds of the library against the built one (ABBA rounds, A/A arm)")
     ap.add_argument("--rounds", type=int, default=4, help="--compare: rounds (alternating order)")
+    ap.add_argument("--phases", action="store_true",
+                    help="phase timestamps of split and combine from the trace build of the library")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles)
@@ -841,6 +1165,11 @@ def main():
         return
     if args.compare:
         compare_libraries(torch, va, synth, dev, args)
+        return
+    if args.phases:
+        res = bench_phases(torch, va, synth, dev)
+        print(json.dumps({"phases": res, "kernel_hash": kernel_hash(), "unit": "us",
+                          "library": "lib/libverify_attn_trace.so", "provenance": provenance(torch)}), flush=True)
         return
     contexts = args.ctx or CONTEXTS
     stream = torch.cuda.current_stream()
@@ -1092,7 +1421,7 @@ def main():
                                  "avg_launch_us": round(probe_ms / launches * 1e3, 2),
                                  "split_frac_of_ceiling": round(achieved / read_ceiling, 4)}}
 
-    clocks = _amd_smi_clocks()
+    clocks = _sysfs_clocks(torch)
 
     # ---------------- pass D: the other configurations ----------------
     other = bench_other_configs(torch, va, synth, dev)
