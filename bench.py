@@ -152,7 +152,7 @@ def provenance(torch, clocks=None):
     if os.path.exists(lib):
         with open(lib, "rb") as f:
             lib_hash = hashlib.sha256(f.read()).hexdigest()[:16]
-    return {"gpu": props.name or _sysfs_product(torch), "arch": getattr(props, "gcnArchName", None),
+    return {"gpu": _sysfs_product(torch) or props.name, "gpu_runtime_name": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "rocm": rocm, "hip_runtime": torch.version.hip,
             "torch": torch.__version__, "git_revision": build.get("git_revision"),
             "worktree_modified": build.get("worktree_modified"), "hipcc": build.get("hipcc"),
@@ -278,7 +278,7 @@ def phase_table(d, py):
             ("split_span", "split span"), ("gap_to_combine", "gap to combine"), ("comb_args", "comb args"),
             ("comb_first_batch", "comb 1st batch"), ("comb_folded", "comb folded"),
             ("comb_written", "comb written"), ("comb_span", "comb span"), ("pair_span", "pair span"),
-            ("us_per_call", "us / call (events)")]
+            ("us_per_call", "us / call, 4-call graphs")]
     o = ["# split_kernel / combine_kernel phases (trace build, per-workgroup clock stamps)", "",
          f"kernel source sha256[:16]: {line['kernel_hash']}", "",
          f"command: {py} --phases", "",
@@ -291,8 +291,8 @@ def phase_table(d, py):
          "is (last step - chunk 0) / (chunks - 1); 'barrier share' is consumer wave 0's time at barriers over "
          "that span; 'last step issued', 'partials written' (wave 0) and the spans are from the first "
          "workgroup's entry; 'gap to combine' runs from the last split workgroup's partials to the first combine "
-         "workgroup's entry. The trace build's own time per call (events) is slightly longer than the "
-         "product's.", "",
+         "workgroup's entry. 'us / call' divides the event time of the 6 graph replays by their 24 calls, graph "
+         "launches included (longer than back-to-back calls of one long graph).", "",
          "| case | " + " | ".join(c[1] for c in cols) + " |", "|---" * (len(cols) + 1) + "|"]
     for c in line["phases"]:
         o.append(f"| {c['case']} | " + " | ".join(str(c.get(k)) for k, _ in cols) + " |")
@@ -513,7 +513,8 @@ def summarize_profiles(d):
         by = collections.defaultdict(list)
         for r in rows:
             n = r["Kernel_Name"]
-            name = n[n.index("sample_detail::") + len("sample_detail::"):n.index("(")].replace(" ", "")
+            i = n.index("sample_detail::") + len("sample_detail::")
+            name = n[i:n.index("(") if "(" in n else len(n)].replace(" ", "")
             wgs = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_X"])
             by[(name, wgs)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
 
