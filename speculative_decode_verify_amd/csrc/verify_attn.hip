@@ -231,13 +231,25 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 }
 
 // LDS DMA: lane l copies `bytes` from its global address to lds + bytes*l
-// (the LDS base is wave-uniform).  Kept out of the kernel templates: the
-// builtin exists only for the device.
-__device__ __forceinline__ void dma16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+// (the LDS base is wave-uniform, an LDS byte address).  Kept out of the
+// kernel templates: the builtin exists only for the device.  The LDS
+// address travels as an integer: a generic pointer cast to LDS at every
+// call costs a null test and a select per instruction.
+__device__ __forceinline__ uint32_t lds_addr(const void *shared_array) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)shared_array;
 }
-__device__ __forceinline__ void dma4(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(uintptr_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(uintptr_t)lds, 4, 0, 0);
+}
+// A 32-bit per-lane offset, opaque to the compiler at each use: added to a
+// wave-uniform base it selects the DMA's scalar-base form (base in SGPRs,
+// offset in one VGPR) instead of a 64-bit address add per instruction.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
@@ -372,10 +384,16 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   // consumers' reads of them take their buffer offset as an instruction
   // immediate; the staged ring follows.
   uint8_t *const ring = smem + kDecB;
+  const uint32_t ring_lds = lds_addr(smem) + kDecB;  // the ring as an LDS byte address
 
   const int lane = threadIdx.x & 63;
   // wave-uniform: keeps chunk indices and mask decisions in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Roles by hardware wave: the producers first (a workgroup's waves start
+  // in order, and the producers' first DMA is what every other wave waits
+  // for), then the decoders, then the consumers; `wave` is the role index
+  // (consumers 0 .. W-1, decoders W .. W+NDW-1, producers after).
+  const int hw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = hw_wave < NPW ? W + NDW + hw_wave : (hw_wave < NPW + NDW ? W + hw_wave - NPW : hw_wave - NPW - NDW);
   const int i16 = lane & 15;
   const int g4 = lane >> 4;
   const int split = blockIdx.x;
@@ -606,22 +624,22 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         const int64_t row0 = chunk_row(c0);
         const uint8_t *kc = kbase + row0 * row_stride;
         const uint8_t *vc = vbase + row0 * row_stride;
-        uint8_t *stg = ring + st * kStageB + 1024 * PW * U;
+        const uint32_t stg = ring_lds + st * kStageB + 1024 * PW * U;
         if (c0 >= rel_lo && c0 + kChunk <= rel_hi) {
 #pragma unroll
-          for (int i = 0; i < U; ++i) dma16((PW * U + i >= NDMA ? vc : kc) + off[i], stg + 1024 * i);
+          for (int i = 0; i < U; ++i) dma16((PW * U + i >= NDMA ? vc : kc) + opaque(off[i]), stg + 1024 * i);
         } else {
 #pragma unroll
           for (int i = 0; i < U; ++i) {
             const int u = PW * U + i;
             const int row = (u >= NDMA ? u - NDMA : u) * RPI + lane / PIECES;
             const uint32_t x = (uint32_t)clampx(row, c0) * rs;
-            dma16((u >= NDMA ? vc : kc) + x + (off[i] - (uint32_t)row * rs), stg + 1024 * i);
+            dma16((u >= NDMA ? vc : kc) + (x + (off[i] - (uint32_t)row * rs)), stg + 1024 * i);
           }
         }
         if constexpr (FMT == 1) {
           const float *sc = vsc + (int64_t)kvh * vsc_stride + row0;
-          dma4(sc + clampx(lane & 31, c0), ring + st * kStageB + 2 * kTileB);
+          dma4(sc + clampx(lane & 31, c0), ring_lds + st * kStageB + 2 * kTileB);
         }
       };
 #pragma unroll
@@ -684,8 +702,8 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
 
   // ================= consumers =================
   chunk_range();
-  VA_TRACE_VAL(va_trace_split, 0, t_entry, threadIdx.x == 0);  // kernel entry
-  VA_TRACE(va_trace_split, 1, threadIdx.x == 0 && nch >= 0);   // arguments in registers
+  VA_TRACE_VAL(va_trace_split, 0, t_entry, wave == 0 && lane == 0);  // kernel entry
+  VA_TRACE(va_trace_split, 1, wave == 0 && lane == 0);   // arguments in registers
 
   // lane column i16 of this wave is query matrix row m = 16*wave + i16 =
   // r*G + (h - kvh*G); live matrix rows are [0, live_rows * G).
@@ -974,16 +992,16 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         wg_barrier();  // chunk n0 + j is in LDS (decoded); every consumer has left the one before
 #ifdef VA_PHASE_TRACE
         const uint64_t tb1 = trace_now();
-        if (n0 + j == 0) VA_TRACE_VAL(va_trace_split, 3, tb1, threadIdx.x == 0);  // first chunk in LDS
+        if (n0 + j == 0) VA_TRACE_VAL(va_trace_split, 3, tb1, wave == 0 && lane == 0);  // first chunk in LDS
         else t_bar += tb1 - tb0;
 #endif
         if (active) step(n0 + j, ring + j * kStageB, j & 1);
       }
     }
   }
-  VA_TRACE(va_trace_split, 4, threadIdx.x == 0);  // last step issued
-  VA_TRACE_VAL(va_trace_split, 6, t_bar, threadIdx.x == 0);
-  VA_TRACE_VAL(va_trace_split, 7, (uint64_t)nch, threadIdx.x == 0);
+  VA_TRACE(va_trace_split, 4, wave == 0 && lane == 0);  // last step issued
+  VA_TRACE_VAL(va_trace_split, 6, t_bar, wave == 0 && lane == 0);
+  VA_TRACE_VAL(va_trace_split, 7, (uint64_t)nch, wave == 0 && lane == 0);
 
   // ---------------- partials of this wave's live rows ----------------
   // Normalised to the true maximum M of the split: m = M, l = sum 2^(x - M),
@@ -1002,7 +1020,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   }
 #ifdef VA_PHASE_TRACE
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  VA_TRACE(va_trace_split, 5, threadIdx.x == 0);  // this wave's partials written
+  VA_TRACE(va_trace_split, 5, wave == 0 && lane == 0);  // this wave's partials written
 #endif
 }
 
