@@ -593,14 +593,27 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
           const int32_t x = new0 + rr;  // this row's key (relative)
           const int jx = x - c0;
           if (rr < live_rows && jx >= 0 && jx < kChunk) {
-            // tile rows whose key is clamped to x read x's slot too (keys past
-            // rel_hi - 1, or before rel_lo): they take this row as well, so no
-            // masked key carries the slot's stale contents into P V
-            const int jlo = x == rel_lo ? 0 : jx;
-            const int jhi = x == rel_hi - 1 ? kChunk - 1 : jx;
-            for (int j = jlo; j <= jhi; ++j) {
-              const int f = PW == 0 ? (j & (PIECES - 1)) : ((2 * j) & (PIECES - 2));
-              *(u32x4 *)(tile + j * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
+            const int f = PW == 0 ? (jx & (PIECES - 1)) : ((2 * jx) & (PIECES - 2));
+            *(u32x4 *)(tile + jx * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
+          }
+        }
+        if constexpr (PW == 1) {
+          // Tile rows whose key is clamped into [rel_lo, rel_hi) (past rel_hi
+          // - 1, or before rel_lo) were read from the slot of an edge key,
+          // which this launch may be about to overwrite (stale contents, NaN
+          // included).  Every row masks those keys (p = 0), and a stale K only
+          // gives a score the mask replaces; a stale V would still give
+          // 0 * NaN in P V.  So their V rows become zero, one 16-byte piece
+          // per lane and pass.
+          const int zlo = rel_lo - c0 > 0 ? rel_lo - c0 : 0;
+          const int zhi = rel_hi - c0 < kChunk ? rel_hi - c0 : kChunk;
+          if (zlo > 0 || zhi < kChunk) {
+#pragma unroll
+            for (int pz = 0; pz < kChunk * PIECES / 64; ++pz) {
+              const int idx = 64 * pz + lane;
+              const int j = idx / PIECES, pc = idx % PIECES;
+              if (j < zlo || j >= zhi)
+                *(u32x4 *)(tile + j * KROW + 16 * (pc ^ ((2 * j) & (PIECES - 2)))) = (u32x4){0u, 0u, 0u, 0u};
             }
           }
         }
