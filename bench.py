@@ -975,7 +975,8 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
                 torch.cuda.synchronize()
                 sp = records(0, nsw)
                 cb = records(1, ncw)
-                live_wg = (np.arange(ncw) % (c["rows"] * c["hq"])) // c["hq"] < c["live"]
+                # combine record index: h + Hq * (row * D/32 + d slice)
+                live_wg = (np.arange(ncw) // c["hq"]) // (c["d"] // 32) < c["live"]
                 cb = cb[live_wg]
                 t0 = sp[:, 0].min()
                 busy = sp[:, 7] > 0

@@ -34,7 +34,9 @@ va_status va_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream
  * constant-rate GPU clock (s_memrealtime, common to all CUs) at phase
  * boundaries into a per-workgroup record of 8 uint64 in a static device
  * array; each launch overwrites the records of the workgroups it runs
- * (workgroup index blockIdx.x + gridDim.x * blockIdx.y, at most 8,192).
+ * (workgroup index blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y *
+ * blockIdx.z), at most 8,192: for split_kernel split + S * KV head, for
+ * combine_kernel h + Hq * (row * D/32 + d slice)).
  *   split_kernel:   0 kernel entry, 1 arguments in registers, 2 first
  *                   producer wave has issued the first chunks' DMA, 3 chunk
  *                   0 in LDS (consumer wave 0 leaves its first barrier),

@@ -340,7 +340,7 @@ __device__ uint64_t va_trace_split[kTraceWG * 8];
 __device__ uint64_t va_trace_comb[kTraceWG * 8];
 __device__ __forceinline__ uint64_t trace_now() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ void trace_put(uint64_t *rec, int slot, uint64_t v, bool lane0) {
-  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   if (lane0 && wg < kTraceWG) rec[wg * 8 + slot] = v;
 }
 #define VA_TRACE(rec, slot, lane0) trace_put(rec, slot, trace_now(), lane0)
@@ -1038,8 +1038,8 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: grid (rows * Hq, D / 32), WAVES wave64s; a workgroup merges
-// 32 consecutive d of one (row, query head).  Thread t owns four of them
+// Combine kernel: grid (G, Hkv, rows * D/32), WAVES wave64s; a workgroup
+// merges 32 consecutive d of one (row, query head).  Thread t owns four of them
 // (dq = t % 8) and the splits s = sg, sg + NSG, sg + 2*NSG, ... (sg = t / 8,
 // NSG = 8 * WAVES split groups), which it folds into four FP32 chains (one
 // per d) against a running maximum that moves only when a batch brings a
@@ -1089,9 +1089,11 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
     if (!g.valid) {  // a state outside the bucket: every output is NaN
       const int t = threadIdx.x;
       if (t < kCombDQ) {
-        const int rh = blockIdx.x;
-        *(f32x4 *)(outb + (int64_t)rh * D + kCombD * blockIdx.y + 4 * t) = (f32x4){NAN, NAN, NAN, NAN};
-        if (lsep && blockIdx.y == 0 && t == 0) lsep[rh] = NAN;
+        const int sh = D == 128 ? 2 : 1;  // log2 of the 32-wide d slices
+        const int rh = (blockIdx.z >> sh) * q_heads + blockIdx.y * group + blockIdx.x;
+        const int ds = blockIdx.z & ((1 << sh) - 1);
+        *(f32x4 *)(outb + (int64_t)rh * D + kCombD * ds + 4 * t) = (f32x4){NAN, NAN, NAN, NAN};
+        if (lsep && ds == 0 && t == 0) lsep[rh] = NAN;
       }
       return;
     }
@@ -1099,23 +1101,26 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
     S = g.splits;
   }
 
-  const int rh = blockIdx.x;
-  const int r = rh / q_heads, h = rh % q_heads;
+  // grid (G, Hkv, rows * D/32): query head h = g*G + j of KV head g, row r,
+  // d slice ds (D/32 is 2 or 4, so no division on the way to the loads)
+  const int sh = D == 128 ? 2 : 1;
+  const int j = blockIdx.x, g = blockIdx.y;
+  const int r = blockIdx.z >> sh, ds = blockIdx.z & ((1 << sh) - 1);
+  const int h = g * group + j;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int dq = t % kCombDQ, sg = t / kCombDQ;
-  const int d0 = kCombD * blockIdx.y + 4 * dq;
+  const int d0 = kCombD * ds + 4 * dq;
   float *outp = outb + ((int64_t)r * q_heads + h) * D;
 
   if (r >= live_rows) {  // padding row: no read of the workspace
     if (sg == 0) *(f32x4 *)(outp + d0) = (f32x4){0.f, 0.f, 0.f, 0.f};
-    if (lsep && blockIdx.y == 0 && t == 0) lsep[(int64_t)r * q_heads + h] = -INFINITY;
+    if (lsep && ds == 0 && t == 0) lsep[(int64_t)r * q_heads + h] = -INFINITY;
     return;
   }
   VA_TRACE_VAL(va_trace_comb, 0, t_entry, t == 0);
   VA_TRACE(va_trace_comb, 1, t == 0);  // arguments in registers (pin() waited for them)
-  const int g = h / group;
-  const int mrow = r * group + (h - g * group);
+  const int mrow = r * group + j;
   const int64_t stride_unit = (int64_t)kv_heads * mrows;  // units between splits
   const int64_t unit0 = (int64_t)g * mrows + mrow;
   // split s of this (row, head): (m, l) at mlb + s*ml_step, O at ob + s*o_step
@@ -1211,7 +1216,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
       for (int k = 0; k < 4; ++k) tot[k] = fmaf(fi, c[k], tot[k]);
     }
     dt += __builtin_amdgcn_exp2f(sink2 - Mu);  // 0 without a sink
-    const bool lse_lane = lsep && blockIdx.y == 0 && dq == 0;
+    const bool lse_lane = lsep && ds == 0 && dq == 0;
     if (Mt == -INFINITY) {  // nothing visible and no sink
       *(f32x4 *)(outp + d0) = (f32x4){0.f, 0.f, 0.f, 0.f};
       if (lse_lane) lsep[(int64_t)r * q_heads + h] = -INFINITY;
@@ -1522,7 +1527,7 @@ va_status combine_impl(const va_plan *plan, const va_state *state, const void *w
   a.window = (d->mask == VA_MASK_WINDOW) ? d->window : 0;
   a.ring_slots = d->ring_slots;
   a.bucket_hi = d->hi;
-  dim3 grid(d->rows * d->q_heads, d->head_dim / kCombD);
+  dim3 grid(d->group, d->kv_heads, d->rows * (d->head_dim / kCombD));
   const hipError_t e = state ? launch_combine<true>(a, grid, d->splits, stream)
                              : launch_combine<false>(a, grid, d->splits, stream);
   return e == hipSuccess ? VA_OK : VA_ERR_HIP;

@@ -106,8 +106,9 @@ def test_trace_build_matches_product_and_orders_phases(case):
     assert 0 < span_us < 1000, span_us
 
     # combine records of the live rows
-    rh = np.arange(n_comb) % (plan.rows * plan.q_heads)
-    c = cb[rh // plan.q_heads < live]
+    # record index h + Hq * (row * D/32 + d slice)
+    row = (np.arange(n_comb) // plan.q_heads) // (plan.head_dim // 32)
+    c = cb[row < live]
     assert np.all(c[:, 0] <= c[:, 1]) and np.all(c[:, 1] <= c[:, 2])
     assert np.all(c[:, 2] <= c[:, 3]) and np.all(c[:, 3] <= c[:, 4])
     # the combine starts after the split's partials are written
