@@ -278,7 +278,7 @@ def phase_table(d, py):
             ("split_span", "split span"), ("gap_to_combine", "gap to combine"), ("comb_args", "comb args"),
             ("comb_first_batch", "comb 1st batch"), ("comb_folded", "comb folded"),
             ("comb_written", "comb written"), ("comb_span", "comb span"), ("pair_span", "pair span"),
-            ("us_per_call", "us / call, 4-call graphs")]
+            ("us_per_call", "us / call, 4-call graphs"), ("waits", "barrier wait per step: consumers c0.. / producer (its DMA wait) / decoder (converting)")]
     o = ["# split_kernel / combine_kernel phases (trace build, per-workgroup clock stamps)", "",
          f"kernel source sha256[:16]: {line['kernel_hash']}", "",
          f"command: {py} --phases", "",
@@ -289,12 +289,18 @@ def phase_table(d, py):
          "in us. Per-workgroup phases are means over workgroups and measured from that workgroup's entry "
          "(args, 1st DMA issued, chunk 0 in LDS, comb args / 1st batch / folded / written); 'later chunk step' "
          "is (last step - chunk 0) / (chunks - 1); 'barrier share' is consumer wave 0's time at barriers over "
-         "that span; 'last step issued', 'partials written' (wave 0) and the spans are from the first "
+         "that span; 'barrier wait per step' is each role's time at the later barriers (consumer waves in order, "
+         "the first producer wave, with its wait for its DMA in brackets, the first decoder wave, with its "
+         "conversion time per chunk in brackets) per step: the role that waits least at the barriers holds the step; 'last step issued', 'partials written' (wave 0) and the spans are from the first "
          "workgroup's entry; 'gap to combine' runs from the last split workgroup's partials to the first combine "
          "workgroup's entry. 'us / call' divides the event time of the 6 graph replays by their 24 calls, graph "
          "launches included (longer than back-to-back calls of one long graph).", "",
          "| case | " + " | ".join(c[1] for c in cols) + " |", "|---" * (len(cols) + 1) + "|"]
     for c in line["phases"]:
+        nw = sum(1 for k in c if k.startswith("wait_c"))
+        c = dict(c, waits=", ".join(f"{c[f'wait_c{w}']:.3f}" for w in range(nw))
+                 + f" / {c['wait_prod']:.3f} ({c['dma_prod']:.3f})"
+                 + (f" / {c['wait_dec']:.3f} ({c['conv_dec']:.3f})" if "wait_dec" in c else ""))
         o.append(f"| {c['case']} | " + " | ".join(str(c.get(k)) for k, _ in cols) + " |")
     name = os.path.join(ROOT, "profiles", "split_kernel_phases.md")
     open(name, "w").write("\n".join(o) + "\n")
@@ -888,7 +894,7 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
     tick_us = 0.01  # s_memrealtime runs at 100 MHz
 
     def records(which, n):
-        buf = np.zeros((n, 8), dtype=np.uint64)
+        buf = np.zeros((n, 24 if which == 0 else 8), dtype=np.uint64)
         if lib.va_trace_read(which, buf.ctypes.data, n) != 0:
             raise RuntimeError("va_trace_read failed")
         return buf.astype(np.int64)
@@ -911,7 +917,7 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
             vb = kb + hi * D
             return fl[kb:kb + hi * D].view(HKV, hi, D), fl[vb:vb + hi * D].view(HKV, hi, D), None
         cases.append(dict(name=f"sweep {ctx // 1024}K", plan=plan, q=q, sink=sink, kv_of=kv_of, npool=npool,
-                          rows=ROWS, hq=HQ, d=D, live=live, keep=pool))
+                          rows=ROWS, hq=HQ, d=D, live=live, keep=pool, waves=-(-ROWS * (HQ // HKV) // 16)))
     g = synth.gen(9500)
     for quant, P in ((False, 32768), (True, 65536)):
         kw = dict(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=P,
@@ -944,7 +950,7 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
             return kv[0], kv[1], None
         cases.append(dict(name=("quantised tree 64K" if quant else "tree 32K"), plan=plan,
                           q=synth.normal_bf16((16, 24, 128), g).to(dev), sink=None, kv_of=kv_of, npool=n,
-                          rows=16, hq=24, d=128, live=16, keep=pool))
+                          rows=16, hq=24, d=128, live=16, keep=pool, waves=6, quant=quant))
 
     out = []
     binding._LIB = lib
@@ -999,7 +1005,14 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
                     comb_folded=(cb[:, 3] - cb[:, 0]).mean(),
                     comb_written=(cb[:, 4] - cb[:, 0]).mean(),
                     comb_span=(cb[:, 4].max() - cb[:, 0].min()),
-                    pair_span=(cb[:, 4].max() - t0)))
+                    pair_span=(cb[:, 4].max() - t0),
+                    # each role's time at the later barriers per step: the
+                    # role that waits least holds the chunk's step
+                    **{f"wait_c{w}": (sp[busy, 8 + w] / steps).mean() for w in range(c["waves"])},
+                    dma_prod=(sp[busy, 14] / steps).mean(),
+                    wait_prod=(sp[busy, 15] / steps).mean(),
+                    **({"wait_dec": (sp[busy, 16] / steps).mean(),
+                        "conv_dec": (sp[busy, 17] / np.maximum(sp[busy, 7], 1)).mean()} if c.get("quant") else {})))
             med = {k: round(statistics.median(float(x[k]) for x in rows) * (1 if k == "barrier_share" else tick_us), 3)
                    for k in rows[0]}
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

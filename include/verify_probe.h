@@ -32,8 +32,9 @@ va_status va_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream
  * library has no trace code).  There, lane 0 of a fixed wave of every
  * workgroup of split_kernel and combine_kernel stores the 100 MHz
  * constant-rate GPU clock (s_memrealtime, common to all CUs) at phase
- * boundaries into a per-workgroup record of 8 uint64 in a static device
- * array; each launch overwrites the records of the workgroups it runs
+ * boundaries into a per-workgroup record (24 uint64 for split_kernel, 8 for
+ * combine_kernel) in a static device array; each launch overwrites the
+ * records of the workgroups it runs
  * (workgroup index blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y *
  * blockIdx.z), at most 8,192: for split_kernel split + S * KV head, for
  * combine_kernel h + Hq * (row * D/32 + d slice)).
@@ -44,13 +45,20 @@ va_status va_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream
  *                   6 wave 0's clock ticks at the later barriers (a
  *                   duration), 7 the workgroup's chunk count (a count);
  *                   slots 3-6 of a workgroup without live rows in wave 0
- *                   are not written.
+ *                   are not written.  Durations, each over the chunks
+ *                   after chunk 0: 8 + w consumer wave w's clock ticks at
+ *                   the barriers (w < W; 8 equals 6); the first producer
+ *                   wave's ticks waiting for its DMA (14) and at the
+ *                   barriers (15); the first decoder wave's ticks at the
+ *                   barriers (16) and converting (17; quantised caches
+ *                   only); 18-23 unused.  The role that waits least at the
+ *                   barriers holds each chunk's step.
  *   combine_kernel: 0 entry, 1 arguments in registers, 2 first batch of
  *                   partials in registers, 3 every batch folded, 4 output
  *                   written (thread 0; padding rows and invalid states
  *                   return before slot 2).
- * which = 0 (split) or 1 (combine); copies n_wg records (64 bytes each) to
- * host memory dst.  Returns 0, 1 for bad arguments, 2 for a HIP error.  The
+ * which = 0 (split) or 1 (combine); copies n_wg records (192 or 64 bytes
+ * each) to host memory dst.  Returns 0, 1 for bad arguments, 2 for a HIP error.  The
  * records are the last writer's: run one launch, or read after a sequence
  * whose last launch is the one of interest. */
 int va_trace_read(int which, uint64_t *dst, int n_wg);

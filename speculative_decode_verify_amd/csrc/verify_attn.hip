@@ -333,18 +333,20 @@ __device__ __forceinline__ void pin(const void *x) { asm volatile("" ::"s"(x)); 
 // Phase trace (builds with VA_PHASE_TRACE only; see include/verify_probe.h):
 // lane 0 of a chosen wave stores the 100 MHz constant-rate clock
 // (s_memrealtime, the same on every CU) into slot `slot` of its workgroup's
-// record.  Records: split_kernel 8 slots per workgroup, combine_kernel 8.
+// record.  Records: split_kernel 24 slots per workgroup (phases, then each
+// role's waits), combine_kernel 8.
 #ifdef VA_PHASE_TRACE
 constexpr int kTraceWG = 8192;
-__device__ uint64_t va_trace_split[kTraceWG * 8];
-__device__ uint64_t va_trace_comb[kTraceWG * 8];
+constexpr int va_trace_split_len = 24, va_trace_comb_len = 8;
+__device__ uint64_t va_trace_split[kTraceWG * va_trace_split_len];
+__device__ uint64_t va_trace_comb[kTraceWG * va_trace_comb_len];
 __device__ __forceinline__ uint64_t trace_now() { return __builtin_amdgcn_s_memrealtime(); }
-__device__ __forceinline__ void trace_put(uint64_t *rec, int slot, uint64_t v, bool lane0) {
+__device__ __forceinline__ void trace_put(uint64_t *rec, int len, int slot, uint64_t v, bool lane0) {
   const int wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if (lane0 && wg < kTraceWG) rec[wg * 8 + slot] = v;
+  if (lane0 && wg < kTraceWG && slot < len) rec[wg * len + slot] = v;
 }
-#define VA_TRACE(rec, slot, lane0) trace_put(rec, slot, trace_now(), lane0)
-#define VA_TRACE_VAL(rec, slot, v, lane0) trace_put(rec, slot, v, lane0)
+#define VA_TRACE(rec, slot, lane0) trace_put(rec, rec##_len, slot, trace_now(), lane0)
+#define VA_TRACE_VAL(rec, slot, v, lane0) trace_put(rec, rec##_len, slot, v, lane0)
 #else
 #define VA_TRACE(rec, slot, lane0) ((void)0)
 #define VA_TRACE_VAL(rec, slot, v, lane0) ((void)0)
@@ -482,7 +484,15 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
       for (int i = 0; i < NU; ++i) {
         const int u = lane + 64 * (NDW * i + d);
         const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
-        const u32x4 c = codes[i];
+        // A unit's 16 codes become two 16-byte bf16 pieces, 2pc and 2pc + 1
+        // of its row.  Lanes with pc >= 4 convert and store their second
+        // piece first: one store instruction then puts a row's eight lanes
+        // on eight different 16-byte bank groups, where storing every
+        // lane's first piece together meets pc and pc ^ 4 in one group (a
+        // two-way conflict on each store).  hf: the piece converted first.
+        const int hf = pc >> 2;
+        const u32x4 c0 = codes[i];
+        const u32x4 c = hf ? (u32x4){c0[2], c0[3], c0[0], c0[1]} : c0;
         if (64 * (NDW * i + d) < 8 * kChunk) {  // INT8 values times the token's scale, rounded to bf16
           const float sc = ((const float *)(qs + 2 * kTileB))[row];
           u32x4 h[2];
@@ -495,8 +505,8 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
             h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
           }
           uint8_t *dst = dv + row * kDecRow + 16 * ((2 * pc) ^ fv0(row));
-          *(u32x4 *)dst = h[0];
-          *(u32x4 *)(dst + 16) = h[1];
+          *(u32x4 *)(dst + 16 * hf) = h[0];
+          *(u32x4 *)(dst + 16 * (hf ^ 1)) = h[1];
         } else {  // E4M3 keys: exact in bf16
           u32x4 h[2];
 #pragma unroll
@@ -505,8 +515,8 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
             h[e >> 1][2 * (e & 1) + 1] = e4m3x2_to_bf16x2<true>(c[e]);
           }
 #pragma unroll
-          for (int half = 0; half < 2; ++half)
-            *(u32x4 *)(dk + row * kDecRow + 16 * ((2 * pc + half) ^ (row & 15))) = h[half];
+          for (int k = 0; k < 2; ++k)
+            *(u32x4 *)(dk + row * kDecRow + 16 * ((2 * pc + (k ^ hf)) ^ (row & 15))) = h[k];
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tiles are whole at the next barrier
@@ -522,10 +532,25 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
       chunk_range();
       wg_barrier();  // chunk 0 is staged
       if (nch > 0) decode(0, wave - W);
+#ifdef VA_PHASE_TRACE
+      uint64_t t_wait = 0, t_conv = 0;  // at the barriers after chunk 0's; converting the later chunks
+#endif
       for (int32_t n = 0; n < nch; ++n) {
+#ifdef VA_PHASE_TRACE
+        const uint64_t tw0 = trace_now();
+#endif
         wg_barrier();
+#ifdef VA_PHASE_TRACE
+        const uint64_t tw1 = trace_now();
+        if (n > 0) t_wait += tw1 - tw0;
+#endif
         if (n + 1 < nch) decode(n + 1, wave - W);
+#ifdef VA_PHASE_TRACE
+        t_conv += trace_now() - tw1;
+#endif
       }
+      VA_TRACE_VAL(va_trace_split, 16, t_wait, wave == W && lane == 0);
+      VA_TRACE_VAL(va_trace_split, 17, t_conv, wave == W && lane == 0);
       return;
     }
   }
@@ -668,7 +693,13 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         wg_barrier();
       }
       int st_prev = NST - 1;  // stage of chunk n - 1
+#ifdef VA_PHASE_TRACE
+      uint64_t t_dma = 0, t_wait = 0;  // waiting for its DMA, at the barriers (after chunk 0's)
+#endif
       for (int32_t n = 0; n < nch; ++n) {
+#ifdef VA_PHASE_TRACE
+        const uint64_t tw0 = trace_now();
+#endif
         // chunks issued after n: n+1 .. min(n + NST - 2, nch - 1); DMA groups
         // complete in issue order, so this wait leaves exactly those in flight
         // (for the quantised formats, those after n + 1).
@@ -680,10 +711,18 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
           const int32_t after = later - 1;
           wait_chunks<kVmP, NST - 3>(after < NST - 3 ? (after > 0 ? after : 0) : NST - 3);
         }
+#ifdef VA_PHASE_TRACE
+        const uint64_t tw1 = trace_now();
+#endif
         wg_barrier();
+#ifdef VA_PHASE_TRACE
+        if (n > 0) t_dma += tw1 - tw0, t_wait += trace_now() - tw1;
+#endif
         if (n + NST - 1 < nch) issue(n + NST - 1, st_prev);
         st_prev = st_prev + 1 == NST ? 0 : st_prev + 1;
       }
+      VA_TRACE_VAL(va_trace_split, 14, t_dma, PW == 0 && lane == 0);
+      VA_TRACE_VAL(va_trace_split, 15, t_wait, PW == 0 && lane == 0);
       // split 0 stores every row (padding included) to the cache; nothing in
       // this launch reads those slots from memory: the live rows' keys were
       // put into the tiles above, and the padding rows' slots lie outside
@@ -993,7 +1032,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   // from lane bases computed once (no address arithmetic per chunk).
   static_assert(NST % 2 == 0, "decoded buffers alternate with the chunk index");
 #ifdef VA_PHASE_TRACE
-  uint64_t t_bar = 0;  // wave 0's time at the barriers after its first chunk arrived
+  uint64_t t_bar = 0;  // this wave's time at the barriers after its first chunk arrived
 #endif
   for (int32_t n0 = 0; n0 < nch; n0 += NST) {
 #pragma unroll
@@ -1014,6 +1053,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   }
   VA_TRACE(va_trace_split, 4, wave == 0 && lane == 0);  // last step issued
   VA_TRACE_VAL(va_trace_split, 6, t_bar, wave == 0 && lane == 0);
+  VA_TRACE_VAL(va_trace_split, 8 + wave, t_bar, lane == 0);
   VA_TRACE_VAL(va_trace_split, 7, (uint64_t)nch, wave == 0 && lane == 0);
 
   // ---------------- partials of this wave's live rows ----------------
@@ -1539,14 +1579,17 @@ inline bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
 using namespace va_detail;
 
 #ifdef VA_PHASE_TRACE
-// Copies the phase records of the last launches: which = 0 for split_kernel,
-// 1 for combine_kernel; n_wg workgroups (8 uint64 each) to host memory.
+// Copies the phase records of the last launches: which = 0 for split_kernel
+// (24 uint64 per workgroup), 1 for combine_kernel (8); n_wg workgroups to
+// host memory.
 extern "C" int va_trace_read(int which, uint64_t *dst, int n_wg) {
   if (!dst || n_wg < 0 || n_wg > va_detail::kTraceWG || (which != 0 && which != 1)) return 1;
   const hipError_t e = which == 0
-                           ? hipMemcpyFromSymbol(dst, HIP_SYMBOL(va_detail::va_trace_split), (size_t)n_wg * 64, 0,
+                           ? hipMemcpyFromSymbol(dst, HIP_SYMBOL(va_detail::va_trace_split),
+                                                 (size_t)n_wg * 8 * va_detail::va_trace_split_len, 0,
                                                  hipMemcpyDeviceToHost)
-                           : hipMemcpyFromSymbol(dst, HIP_SYMBOL(va_detail::va_trace_comb), (size_t)n_wg * 64, 0,
+                           : hipMemcpyFromSymbol(dst, HIP_SYMBOL(va_detail::va_trace_comb),
+                                                 (size_t)n_wg * 8 * va_detail::va_trace_comb_len, 0,
                                                  hipMemcpyDeviceToHost);
   return e == hipSuccess ? 0 : 2;
 }

@@ -6,7 +6,10 @@ on the same inputs (the stamps change no arithmetic), and every record of
 the launch is ordered as the phases run: split entry <= arguments <= chunk 0
 in LDS <= last step <= partials written, the first DMA issued (by another
 wave) before chunk 0 is in LDS, each workgroup's chunk count equal to the
-plan's split table and its barrier time within its steps' span; combine
+plan's split table and its barrier time within its steps' span, every
+role's waits (consumers at barriers; first producer for DMA and at
+barriers; first decoder at barriers and converting) within that span and
+wave 0's equal to slot 6; combine
 entry <= arguments <= first batch <= fold <= output written for every live
 row, after the split's last partial.
 """
@@ -41,7 +44,7 @@ def _trace_lib():
 
 
 def _records(lib, which, n):
-    buf = np.zeros((n, 8), dtype=np.uint64)
+    buf = np.zeros((n, 24 if which == 0 else 8), dtype=np.uint64)
     assert lib.va_trace_read(which, buf.ctypes.data, n) == 0
     return buf.astype(np.int64)
 
@@ -102,6 +105,14 @@ def test_trace_build_matches_product_and_orders_phases(case):
     assert np.all(e <= a) and np.all(a <= c0) and np.all(dma <= c0)
     assert np.all(c0 <= last) and np.all(last <= wr)
     assert np.all((bar >= 0) & (bar <= last - c0))
+    # each role's time at the later barriers (a duration inside the steps'
+    # span); consumer wave 0's is the one already checked
+    W = -(-plan.rows * (plan.q_heads // plan.kv_heads) // 16)
+    roles = [8 + w for w in range(W)] + [14, 15] + ([16, 17] if case == 1 else [])
+    span = (wr - e)[:, None]
+    waits = sp[busy][:, roles]
+    assert np.array_equal(sp[busy, 8], bar)
+    assert np.all((waits >= 0) & (waits <= span)), waits.max(axis=0)
     span_us = (wr.max() - e.min()) * 0.01
     assert 0 < span_us < 1000, span_us
 
