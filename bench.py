@@ -258,6 +258,17 @@ def wave_cycles(d, kname, py):
     print(f"wrote {name}")
 
 
+def trace_workgroups(r):
+    """Workgroups of one kernel-trace row: each grid dimension (in work-items)
+    over the workgroup's extent in it; a dimension the file omits counts 1."""
+    n = 1
+    for ax in "XYZ":
+        g, w = r.get(f"Grid_Size_{ax}"), r.get(f"Workgroup_Size_{ax}")
+        if g and w:
+            n *= int(g) // int(w)
+    return n
+
+
 def phase_table(d, py):
     """profiles/split_kernel_phases.md from the `--phases` run (phases.log)."""
     path = os.path.join(d, "phases.log")
@@ -379,7 +390,7 @@ def summarize_profiles(d):
         if kind and "<" in n:
             kind += n[n.index("<"):n.index(">") + 1].replace(" ", "")
         if kind:
-            dur[(kind, n, int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_X"]))].append(
+            dur[(kind, n, trace_workgroups(r))].append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     bl = bench_line("trace.log")
     py = "python -u bench.py"
@@ -521,7 +532,7 @@ def summarize_profiles(d):
             n = r["Kernel_Name"]
             i = n.index("sample_detail::") + len("sample_detail::")
             name = n[i:n.index("(") if "(" in n else len(n)].replace(" ", "")
-            wgs = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_X"])
+            wgs = trace_workgroups(r)
             by[(name, wgs)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
 
         def sampler_line(log):

@@ -296,6 +296,20 @@ struct StageGeom {
   static constexpr int kScaleB = FMT == 1 ? 256 : 0;
   static constexpr int kStageB = 2 * kTileB + kScaleB;
   static constexpr int kVm = 2 * NDMA + (FMT == 1 ? 1 : 0);  // DMA instructions per chunk
+  // Piece swizzles of the staged tiles: piece P of row r sits at position
+  // P ^ f(r).  K: f = r mod PIECES, so the 16 lanes reading one A operand
+  // (16 keys, one piece) hit 16 different positions.  V (bf16): an even f,
+  // so a pair of pieces {2k, 2k+1} stays a pair, the same for rows r and
+  // r + 16, and spreading the 16 rows of one transpose read over all bank
+  // groups: 2r mod PIECES for 256-byte rows; r mod 8 with its low bit
+  // cleared for 128-byte rows, where two rows share a 256-byte bank window
+  // and 2r mod 8 would put rows r and r + 4 on the same banks (a two-way
+  // conflict on every transpose read).  V (INT8) is read bytewise,
+  // unswizzled.
+  static __device__ constexpr int fk(int row) { return row & (PIECES - 1); }
+  static __device__ constexpr int fv(int row) {
+    return FMT != 0 ? 0 : (PIECES == 8 ? row & 6 : (2 * row) & (PIECES - 2));
+  }
 };
 
 // s_waitcnt vmcnt(KV * k) for a run-time k in [0, K] (the count is an
@@ -575,12 +589,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
       const int32_t lo = rel_lo - c0, hi = rel_hi - 1 - c0;
       return x < lo ? lo : (x > hi ? hi : x);
     };
-    // Piece swizzles inside the staged tiles (position = piece ^ f(row)):
-    //   K: f = row % PIECES -> the 16 lanes reading one A operand (16 keys,
-    //      same piece) hit 16 different positions.
-    //   V (bf16): f = 2 * (row % (PIECES/2)), an even value, so a pair of
-    //      pieces {2k, 2k+1} stays a pair; the 16 rows of one transpose read
-    //      spread over all bank groups.  V (INT8) is read bytewise, unswizzled.
+    // Piece swizzles inside the staged tiles: G::fk, G::fv.
     // A chunk's DMA is 2*NDMA instructions: u < NDMA copies K rows
     // [u*RPI, u*RPI + RPI), the rest V; instruction u lands at stage + 1024*u
     // (the V tile starts NDMA KiB into the stage).  Producer wave PW issues
@@ -618,7 +627,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
           const int32_t x = new0 + rr;  // this row's key (relative)
           const int jx = x - c0;
           if (rr < live_rows && jx >= 0 && jx < kChunk) {
-            const int f = PW == 0 ? (jx & (PIECES - 1)) : ((2 * jx) & (PIECES - 2));
+            const int f = PW == 0 ? G::fk(jx) : G::fv(jx);
             *(u32x4 *)(tile + jx * KROW + 16 * ((lane % PIECES) ^ f)) = nrow[i];
           }
         }
@@ -638,7 +647,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
               const int idx = 64 * pz + lane;
               const int j = idx / PIECES, pc = idx % PIECES;
               if (j < zlo || j >= zhi)
-                *(u32x4 *)(tile + j * KROW + 16 * (pc ^ ((2 * j) & (PIECES - 2)))) = (u32x4){0u, 0u, 0u, 0u};
+                *(u32x4 *)(tile + j * KROW + 16 * (pc ^ G::fv(j))) = (u32x4){0u, 0u, 0u, 0u};
             }
           }
         }
@@ -652,7 +661,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         const int t = isv ? u - NDMA : u;
         const int row = t * RPI + lane / PIECES;
         const int pos = lane % PIECES;
-        const int f = isv ? (FMT == 0 ? (2 * row) & (PIECES - 2) : 0) : (row & (PIECES - 1));
+        const int f = isv ? G::fv(row) : G::fk(row);
         off[i] = (uint32_t)row * rs + 16u * (uint32_t)(pos ^ f);
       }
       // Chunk n into stage `st` (lane l of instruction u stores 16 bytes at
@@ -869,8 +878,8 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   const float cs = FMT == 1 ? 1.f : scale_log2;
 
   // Swizzles of the staged tiles (must match the producer's).
-  auto fk = [](int row) { return row & (PIECES - 1); };
-  auto fv = [](int row) { return FMT == 0 ? (2 * row) & (PIECES - 2) : 0; };
+  auto fk = [](int row) { return G::fk(row); };
+  auto fv = [](int row) { return G::fv(row); };
 
   // Quantised formats: each lane's byte offsets of its decoded K and V
   // operands within a buffer, computed once; the buffer's own offset is a
