@@ -305,8 +305,13 @@ struct StageGeom {
   // cleared for 128-byte rows, where two rows share a 256-byte bank window
   // and 2r mod 8 would put rows r and r + 4 on the same banks (a two-way
   // conflict on every transpose read).  V (INT8) is read bytewise,
-  // unswizzled.
-  static __device__ constexpr int fk(int row) { return row & (PIECES - 1); }
+  // unswizzled.  K codes (E4M3, eight pieces a row) are read only by the
+  // decoders, a lane taking pieces 2k and 2k + 1 of one row: r mod 8 with
+  // its low bit flipped when bit 1 of r is set puts each load's 16 lanes
+  // (four rows) on 16 different bank groups.
+  static __device__ constexpr int fk(int row) {
+    return FMT != 0 ? ((row & 7) ^ ((row >> 1) & 1)) : row & (PIECES - 1);
+  }
   static __device__ constexpr int fv(int row) {
     return FMT != 0 ? 0 : (PIECES == 8 ? row & 6 : (2 * row) & (PIECES - 2));
   }
@@ -470,34 +475,42 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
 
   // Decoded tiles (quantised formats): buffer b holds K at dec + b*2*kDecTile
   // and V after it.  V is bf16 in the bf16 layout (piece P of a row at
-  // 16*(P ^ fv0(row)), fv0 = 2*(row % 8)); K keeps each staged 16-code piece
-  // in its staged slot q, expanded to two bf16 halves at 16-byte positions
-  // (2q + half) ^ (row % 16), so that the 16 lanes reading one operand hit
-  // 16 different positions.
+  // 16*(P ^ fv0(row)), fv0 = 2*(row % 8)).  K is bf16 in the contraction
+  // order of the rotated query: its 16-byte piece (k, g) holds d = 32k + 4g
+  // + 0..3 and 32k + 16 + 4g + 0..3 (four codes from each of staged pieces
+  // 2k and 2k + 1), at position (4k + g) ^ (row % 16), so that the 16 lanes
+  // reading one operand hit 16 different positions.
   uint8_t *const dec = smem;
   auto fv0 = [](int row) { return (2 * row) & 14; };
-  // Decoder d converts its share of chunk n: of the 16 * kChunk units of 16
-  // codes (V first, then K), the blocks of 64 consecutive units with index
-  // = d (mod NDW), unit u on lane u % 64, so each load and store is one
-  // kind; all of a lane's code loads are issued before it converts.
-  constexpr int kUnits = 16 * kChunk;
-  constexpr int NU = kUnits / 64 / (NDW > 0 ? NDW : 1);
+  // Decoder d converts its share of chunk n.  Values: of the 8 * kChunk
+  // units of 16 codes, the blocks of 64 consecutive units with index = d
+  // (mod NDW), unit u on lane u % 64.  Keys: one unit of 32 codes per lane,
+  // pieces 2k and 2k + 1 of row t / 4 (t = lane + 64 d, k = t % 4), which
+  // become the four decoded pieces (k, 0..3).  All of a lane's code loads
+  // are issued before it converts.
+  constexpr int NUV = 8 * kChunk / 64 / (NDW > 0 ? NDW : 1);
+  static_assert(FMT == 0 || (NDW == 2 && NUV * 64 * NDW == 8 * kChunk),
+                "two decoders: two value units and one key unit per lane");
   auto decode = [&](int32_t n, int d) {
     if constexpr (FMT == 1) {
       const uint8_t *qs = ring + (n % NST) * kStageB;
       uint8_t *dk = dec + (n & 1) * 2 * kDecTile;
       uint8_t *dv = dk + kDecTile;
-      u32x4 codes[NU];
+      u32x4 codes[NUV];
 #pragma unroll
-      for (int i = 0; i < NU; ++i) {
+      for (int i = 0; i < NUV; ++i) {
         const int u = lane + 64 * (NDW * i + d);
-        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
-        codes[i] = *(const u32x4 *)(qs + (u < 8 * kChunk ? kTileB : 0) + row * KROW + 16 * pc);
+        const int row = u >> 3, pc = u & 7;
+        codes[i] = *(const u32x4 *)(qs + kTileB + row * KROW + 16 * pc);
       }
+      const int t = lane + 64 * d;
+      const int krow = t >> 2, kk = t & 3;
+      const u32x4 ka = *(const u32x4 *)(qs + krow * KROW + 16 * ((2 * kk) ^ G::fk(krow)));
+      const u32x4 kb = *(const u32x4 *)(qs + krow * KROW + 16 * ((2 * kk + 1) ^ G::fk(krow)));
 #pragma unroll
-      for (int i = 0; i < NU; ++i) {
+      for (int i = 0; i < NUV; ++i) {
         const int u = lane + 64 * (NDW * i + d);
-        const int row = (u & (8 * kChunk - 1)) >> 3, pc = u & 7;
+        const int row = u >> 3, pc = u & 7;
         // A unit's 16 codes become two 16-byte bf16 pieces, 2pc and 2pc + 1
         // of its row.  Lanes with pc >= 4 convert and store their second
         // piece first: one store instruction then puts a row's eight lanes
@@ -507,31 +520,28 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         const int hf = pc >> 2;
         const u32x4 c0 = codes[i];
         const u32x4 c = hf ? (u32x4){c0[2], c0[3], c0[0], c0[1]} : c0;
-        if (64 * (NDW * i + d) < 8 * kChunk) {  // INT8 values times the token's scale, rounded to bf16
-          const float sc = ((const float *)(qs + 2 * kTileB))[row];
-          u32x4 h[2];
+        // INT8 values times the token's scale, rounded to bf16
+        const float sc = ((const float *)(qs + 2 * kTileB))[row];
+        u32x4 h[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = c[e];
-            const float f0 = (float)((int32_t)(w << 24) >> 24) * sc, f1 = (float)((int32_t)(w << 16) >> 24) * sc;
-            const float f2 = (float)((int32_t)(w << 8) >> 24) * sc, f3 = (float)((int32_t)w >> 24) * sc;
-            h[e >> 1][2 * (e & 1)] = pack_bf16x2(f0, f1);
-            h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
-          }
-          uint8_t *dst = dv + row * kDecRow + 16 * ((2 * pc) ^ fv0(row));
-          *(u32x4 *)(dst + 16 * hf) = h[0];
-          *(u32x4 *)(dst + 16 * (hf ^ 1)) = h[1];
-        } else {  // E4M3 keys: exact in bf16
-          u32x4 h[2];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            h[e >> 1][2 * (e & 1)] = e4m3x2_to_bf16x2<false>(c[e]);
-            h[e >> 1][2 * (e & 1) + 1] = e4m3x2_to_bf16x2<true>(c[e]);
-          }
-#pragma unroll
-          for (int k = 0; k < 2; ++k)
-            *(u32x4 *)(dk + row * kDecRow + 16 * ((2 * pc + (k ^ hf)) ^ (row & 15))) = h[k];
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = c[e];
+          const float f0 = (float)((int32_t)(w << 24) >> 24) * sc, f1 = (float)((int32_t)(w << 16) >> 24) * sc;
+          const float f2 = (float)((int32_t)(w << 8) >> 24) * sc, f3 = (float)((int32_t)w >> 24) * sc;
+          h[e >> 1][2 * (e & 1)] = pack_bf16x2(f0, f1);
+          h[e >> 1][2 * (e & 1) + 1] = pack_bf16x2(f2, f3);
         }
+        uint8_t *dst = dv + row * kDecRow + 16 * ((2 * pc) ^ fv0(row));
+        *(u32x4 *)(dst + 16 * hf) = h[0];
+        *(u32x4 *)(dst + 16 * (hf ^ 1)) = h[1];
+      }
+      // E4M3 keys (exact in bf16): decoded piece (kk, g) is code word g of
+      // staged piece 2kk, then code word g of piece 2kk + 1
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 h = {e4m3x2_to_bf16x2<false>(ka[g]), e4m3x2_to_bf16x2<true>(ka[g]),
+                         e4m3x2_to_bf16x2<false>(kb[g]), e4m3x2_to_bf16x2<true>(kb[g])};
+        *(u32x4 *)(dk + krow * kDecRow + 16 * ((4 * kk + g) ^ (krow & 15))) = h;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tiles are whole at the next barrier
     }
@@ -787,57 +797,63 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
       qop[ks] = __builtin_bit_cast(bf16x8, w);
     }
   } else {
-    // q' = H q / sqrt(128) in FP32 (natural-order Walsh-Hadamard), then bf16.
-    // Quantised keys use the contraction order in which piece p holds
-    // d = 64*(p/8) + 16*(p%4) + 8*((p/4)%2) + e, so lane (i16, g4) needs
-    // d = 64*(j/16) + 16*g4 + j%16 for j = 0..31 -- and those 32 values are
-    // closed under the butterflies on d bits 0-3 and 6, which stay in the
-    // lane; d bits 4 and 5 (g4) pair lanes 16 and 32 apart.
-    float x[32];
+    // q' = H q / sqrt(128) (natural-order Walsh-Hadamard, H[i][j] =
+    // (-1)^popcount(i & j)), summed in FP32 on the MFMA, then bf16.  Output
+    // block nb (d = 16nb .. 16nb + 15) is the sum over the four 32-d steps
+    // ks of H[16nb + m][32ks + k] times q[row][32ks + k]: the A operand (m
+    // = i16, k = 8g4 + e) is that block of H, the B operand the raw query
+    // as loaded (lane (i16, g4) holds row i16, d = 32ks + 8g4 + e).  With
+    // the bits of both indices, popcount((16nb + m) & (32ks + 8g4 + e)) =
+    // popcount(m & e & 7) + (m bit 3 & g4 bit 0) + (nb bit 0 & g4 bit 1) +
+    // popcount((nb >> 1) & ks): the first two terms are this lane's, the
+    // third picks one of two operands, and the last, uniform per product,
+    // negates the query instead.  Every product is exact (+-1 times a bf16
+    // value); the sums round in FP32.
+    bf16x8 qb[KS], qn[KS];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 w = *(const u32x4 *)(qrow + (64 * (c >> 1) + 16 * g4 + 8 * (c & 1)) * 2);
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = *(const u32x4 *)(qrow + (32 * ks + 8 * g4) * 2);
       if (!row_ok) w = (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
-        x[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
+      qb[ks] = __builtin_bit_cast(bf16x8, w);
+      qn[ks] = __builtin_bit_cast(bf16x8, w ^ 0x80008000u);
     }
+    bf16x8 ha[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {  // d bits 0..3 (butterfly widths 1, 2, 4, 8)
+    for (int par = 0; par < 2; ++par) {
+      u32x4 w;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (j & (1 << b)) continue;
-        const float u = x[j], v = x[j | (1 << b)];
-        x[j] = u + v;
-        x[j | (1 << b)] = u - v;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t h2 = 0u;
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const int e = 2 * e2 + hi;
+          const uint32_t neg = (__builtin_popcount(i16 & e & 7) + ((i16 >> 3) & g4 & 1) + par * ((g4 >> 1) & 1)) & 1;
+          h2 |= (0x3f80u | (neg << 15)) << (16 * hi);  // bf16 +1 or -1
+        }
+        w[e2] = h2;
       }
+      ha[par] = __builtin_bit_cast(bf16x8, w);
     }
+    f32x4 qr[8];  // lane (i16, g4): q'[row i16][16nb + 4g4 + i], i = 0..3
 #pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {  // d bits 4, 5 (widths 16, 32)
-      const bool upper = (lane & sh) != 0;
+    for (int nb = 0; nb < 8; ++nb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float p = __shfl_xor(x[j], sh, 64);
-        x[j] = upper ? p - x[j] : x[j] + p;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {  // d bit 6 (width 64)
-      const float u = x[j], v = x[j + 16];
-      x[j] = u + v;
-      x[j + 16] = u - v;
+      for (int ks = 0; ks < KS; ++ks)
+        acc = mfma16(ha[nb & 1], (__builtin_popcount((nb >> 1) & ks) & 1) ? qn[ks] : qb[ks], acc);
+      qr[nb] = acc;
     }
     // 1/sqrt(128) and the softmax scale (log2 units) in one factor: the
     // rotated q is rounded to bf16 either way, and the scores then come
-    // out of the MFMA already scaled.
+    // out of the MFMA already scaled.  Step ks contracts d = 32ks + 4g4 +
+    // 0..3 (block 2ks) and 32ks + 16 + 4g4 + 0..3 (block 2ks + 1), the
+    // order of the decoded key pieces.
     const float inv = 0.08838834764831845f * scale_log2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * ks + 2 * e] * inv, x[8 * ks + 2 * e + 1] * inv);
+      const f32x4 a = qr[2 * ks] * inv, b = qr[2 * ks + 1] * inv;
+      const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                       pack_bf16x2(b[2], b[3])};
       qop[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -886,16 +902,13 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   // constant of each unrolled step, so a read needs no address arithmetic.
   // (The empty asm keeps each sum in a register instead of letting the
   // compiler re-add its two parts at every read.)
-  uint32_t dko[KS / 2][2], dvo[MD];
+  uint32_t dko[KS], dvo[MD];
   if constexpr (FMT == 1) {
 #pragma unroll
-    for (int kp2 = 0; kp2 < KS / 2; ++kp2)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int q = (4 * kp2 + g4) ^ fk(i16);
-        dko[kp2][half] = (uint32_t)(i16 * kDecRow + 16 * ((2 * q + half) ^ (i16 & 15)));
-        asm volatile("" : "+v"(dko[kp2][half]));
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      dko[ks] = (uint32_t)(i16 * kDecRow + 16 * ((4 * ks + g4) ^ i16));
+      asm volatile("" : "+v"(dko[ks]));
+    }
     const int rowA = 4 * g4 + (i16 >> 2);
     const int F = fv0(rowA) >> 1;
 #pragma unroll
@@ -922,13 +935,10 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         for (int ks = 0; ks < KS; ++ks)
           kop[mb][ks] = *(const bf16x8 *)(kt + row * KROW + 16 * ((4 * ks + g4) ^ fk(row)));
       } else {
-        // staged piece (16 codes): first 8 -> step 2*kp2, last 8 -> step
-        // 2*kp2+1; rows 16 + i16 repeat row i16's swizzle 16 rows lower
+        // decoded piece (ks, g4); rows 16 + i16 repeat row i16's swizzle 16
+        // rows lower
 #pragma unroll
-        for (int kp2 = 0; kp2 < KS / 2; ++kp2)
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-            kop[mb][2 * kp2 + half] = *(const bf16x8 *)(dk + 16 * mb * kDecRow + dko[kp2][half]);
+        for (int ks = 0; ks < KS; ++ks) kop[mb][ks] = *(const bf16x8 *)(dk + 16 * mb * kDecRow + dko[ks]);
       }
     }
     // ---- V^T operands: lane (i16 = d within block md, g4) takes the keys
