@@ -536,12 +536,19 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
         *(u32x4 *)(dst + 16 * (hf ^ 1)) = h[1];
       }
       // E4M3 keys (exact in bf16): decoded piece (kk, g) is code word g of
-      // staged piece 2kk, then code word g of piece 2kk + 1
+      // staged piece 2kk, then code word g of piece 2kk + 1.  Lanes with kk
+      // >= 2 take their pieces in the order g ^ 2: a store instruction's
+      // eight lanes (two rows, kk = 0..3) then land on eight different
+      // 16-byte bank groups of the 128-byte write window, where storing
+      // piece g everywhere meets kk and kk ^ 2 in one group.
+      const int sw = kk >> 1;
+      const u32x4 a = sw ? (u32x4){ka[2], ka[3], ka[0], ka[1]} : ka;
+      const u32x4 b = sw ? (u32x4){kb[2], kb[3], kb[0], kb[1]} : kb;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x4 h = {e4m3x2_to_bf16x2<false>(ka[g]), e4m3x2_to_bf16x2<true>(ka[g]),
-                         e4m3x2_to_bf16x2<false>(kb[g]), e4m3x2_to_bf16x2<true>(kb[g])};
-        *(u32x4 *)(dk + krow * kDecRow + 16 * ((4 * kk + g) ^ (krow & 15))) = h;
+        const u32x4 h = {e4m3x2_to_bf16x2<false>(a[g]), e4m3x2_to_bf16x2<true>(a[g]),
+                         e4m3x2_to_bf16x2<false>(b[g]), e4m3x2_to_bf16x2<true>(b[g])};
+        *(u32x4 *)(dk + krow * kDecRow + 16 * ((4 * kk + (g ^ (2 * sw))) ^ (krow & 15))) = h;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tiles are whole at the next barrier
     }
