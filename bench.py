@@ -284,7 +284,7 @@ def phase_table(d, py):
         raise SystemExit("phase records of another kernel source")
     cols = [("splits", "splits"), ("chunks_per_split", "chunks / split"), ("entry_spread", "entry spread"),
             ("args", "args"), ("first_dma_issued", "1st DMA issued"), ("chunk0_in_lds", "chunk 0 in LDS"),
-            ("step", "later chunk step"), ("barrier_share", "barrier share of steps"),
+            ("step", "chunk step"), ("barrier_share", "barrier share of steps"),
             ("last_step_issued", "last step issued"), ("partials_written", "partials written"),
             ("split_span", "split span"), ("gap_to_combine", "gap to combine"), ("comb_args", "comb args"),
             ("comb_first_batch", "comb 1st batch"), ("comb_folded", "comb folded"),
@@ -298,9 +298,9 @@ def phase_table(d, py):
          "per workgroup (include/verify_probe.h). Each case replays graphs of 4 back-to-back split + combine "
          "calls over cold replicas and reads the records of the last pair; values are medians over 12 replays, "
          "in us. Per-workgroup phases are means over workgroups and measured from that workgroup's entry "
-         "(args, 1st DMA issued, chunk 0 in LDS, comb args / 1st batch / folded / written); 'later chunk step' "
-         "is (last step - chunk 0) / (chunks - 1); 'barrier share' is consumer wave 0's time at barriers over "
-         "that span; 'barrier wait per step' is each role's time at the later barriers (consumer waves in order, "
+         "(args, 1st DMA issued, chunk 0 in LDS, comb args / 1st batch / folded / written); 'chunk step' "
+         "is (last step issued - chunk 0 in LDS) / chunks (the span holds every chunk's step); 'barrier "
+         "share' is consumer wave 0's time at barriers over that span; 'barrier wait per step' is each role's time at the later barriers (consumer waves in order, "
          "the first producer wave, with its wait for its DMA in brackets, the first decoder wave, with its "
          "conversion time per chunk in brackets) per step: the role that waits least at the barriers holds the step; 'last step issued', 'partials written' (wave 0) and the spans are from the first "
          "workgroup's entry; 'gap to combine' runs from the last split workgroup's partials to the first combine "
@@ -886,7 +886,7 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
     replays them in turn; after each replay the records of its last pair
     are read.  Reported (us, medians over replays; "mean" over workgroups):
     the spread of workgroup entries, the arguments' arrival, the first DMA
-    issue, chunk 0's arrival in LDS, the later chunks' steps, the last
+    issue, chunk 0's arrival in LDS, the chunks' steps, the last
     step, the partials' stores, the gap to the combine's first workgroup
     and the combine's phases; `us_per_call` times the same graphs with
     events (the trace build's own speed, for comparison with the product's)."""
@@ -1004,7 +1004,7 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
                     first_dma_issued=(sp[busy, 2] - sp[busy, 0]).mean(),
                     chunk0_in_lds=(sp[busy, 3] - sp[busy, 0]).mean(),
                     chunk0_in_lds_last=(sp[busy, 3].max() - t0),
-                    step=((sp[busy, 4] - sp[busy, 3]) / steps).mean(),
+                    step=((sp[busy, 4] - sp[busy, 3]) / np.maximum(sp[busy, 7], 1)).mean(),
                     barrier_share=(sp[busy, 6] / np.maximum(sp[busy, 4] - sp[busy, 3], 1)).mean(),
                     last_step_issued=(sp[busy, 4] - t0).mean(),
                     partials_written=(sp[busy, 5] - t0).mean(),
