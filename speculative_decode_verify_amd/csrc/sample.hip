@@ -10,12 +10,13 @@
 // in which the tile maxima bound what can still contribute).
 //
 // Kernels:
-//   topk_tile_kernel     grid (tiles, rows) x 256 threads: one tile's exact
-//                        top-k as a sorted list of 64-bit composites.
-//   sample_finish_kernel grid rows x 64: merge of a row's tile lists, softmax,
-//                        top-p, the draw; with ACCEPT the last row to finish
-//                        also runs the acceptance.
-//   accept_kernel        one wave: the acceptance alone.
+//   sample_kernel<ACCEPT>  grid (tiles, rows) x 256 threads: each workgroup
+//                          writes one tile's exact top-k as a sorted list of
+//                          64-bit composites; the last workgroup of a row to
+//                          finish merges the row's lists and runs the softmax,
+//                          top-p and the draw; with ACCEPT the last row to be
+//                          merged also runs the acceptance.
+//   accept_kernel          one wave: the acceptance alone.
 //
 // Every element of a row is ranked by a composite key: the FP32 logit mapped
 // to an order-preserving uint32 in the high word and the complemented token id
