@@ -329,7 +329,10 @@ def summarize_profiles(d):
     (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
     plain copy of known size).  `d` holds trace/, pmc_fetch/, pmc_write/,
     pmc_copy_fetch/, pmc_copy_write/ and the bench logs trace.log, fetch.log,
-    write.log written by the commands listed in the summaries."""
+    write.log written by the commands listed in the summaries.  Each summary
+    is written only when its own runs are in `d` (the sampler's from
+    trace_sampler/ and sampler_trace.log, the KV write's from trace_kvw/ and
+    kvw.log), so one part can be refreshed alone."""
     import csv
     import collections
 
@@ -357,171 +360,174 @@ def summarize_profiles(d):
         return [(r["Kernel_Name"], int(r["Grid_Size"]) // int(r["Workgroup_Size"]), float(r["Counter_Value"]))
                 for r in rows]
 
-    hashes = {bench_line(x)["kernel_hash"] for x in ("trace.log", "fetch.log", "write.log")}
-    if len(hashes) != 1 or kernel_hash() not in hashes:
-        raise SystemExit(f"profiles were taken of another kernel source: {hashes} vs {kernel_hash()}")
-    copy_bytes = COPY_PROBE_MIB << 20
-    cf = [v for n, g, v in counters("pmc_copy_fetch", "copy_counter_collection.csv") if "copyBuffer" in n]
-    cw = [v for n, g, v in counters("pmc_copy_write", "copy_counter_collection.csv") if "copyBuffer" in n]
-    f_scale = copy_bytes / (sum(cf) / len(cf) * 1024)
-    w_scale = copy_bytes / (sum(cw) / len(cw) * 1024)
-    def static_split(n):  # the sweep's kernel: static plan, D 128, 3 consumer waves, bf16
-        return "split_kernel<128,3,0,4,2,false>" in kname(n)
-
-    fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if static_split(n)]
-    wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if static_split(n)]
-    if len(fe) != len(wr):
-        raise SystemExit("fetch and write runs saw different split launches")
-    per_launch = [f * f_scale * 1024 + w * w_scale * 1024 for (_, f), (_, w) in zip(fe, wr)]
-    traffic = sum(per_launch) / len(per_launch)
-    contexts = bench_line("fetch.log")["config"]["contexts"]
-    splits = [e["splits"] for e in bench_line("fetch.log")["sweep"]]
-    json.dump({"kernel_hash": kernel_hash(), "contexts": contexts, "splits": splits,
-               "hbm_bytes_per_launch": round(traffic),
-               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "launches": len(per_launch)},
-              open(TRAFFIC_FILE, "w"), indent=1)
-
-    trace = list(csv.DictReader(open(os.path.join(d, "trace", "bench_kernel_trace.csv"))))
-    dur = collections.defaultdict(list)
-    for r in trace:
-        n = kname(r["Kernel_Name"])
-        kind = ("split_kernel" if "split_kernel" in n else "combine_kernel" if "combine_kernel" in n
-                else "read_probe_kernel" if "read_probe_kernel" in n else None)
-        if kind and "<" in n:
-            kind += n[n.index("<"):n.index(">") + 1].replace(" ", "")
-        if kind:
-            dur[(kind, n, trace_workgroups(r))].append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-    bl = bench_line("trace.log")
     py = "python -u bench.py"
-    out = []
-    out.append("# split_kernel / combine_kernel, full-attention verify sweep (Hkv 1, Hq 6, D 128, 8 rows, ctx 1K-192K)")
-    out.append("")
-    out.append(f"kernel source sha256[:16]: {kernel_hash()}")
-    out.append("")
-    out.append("## Kernel durations (rocprofv3 kernel trace)")
-    out.append("")
-    out.append(f"command: rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace -o bench -- {py} --steps 10 --warmup 3")
-    out.append("")
-    out.append("| kernel | workgroups | launches | avg us | min us | max us |")
-    out.append("|---|---|---|---|---|---|")
-    tot = collections.defaultdict(list)
-    for (kind, n, wgs), v in sorted(dur.items(), key=lambda x: (x[0][0], x[0][2])):
-        tot[kind] += v
-        out.append(f"| {kind} | {wgs} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-    for kind in ("split_kernel", "combine_kernel"):
-        for flag, label in (("false>", "static plan"), ("true>", "device state")):
-            v = [x for k, x in tot.items() if k.startswith(kind) and k.endswith(flag) for x in x]
-            if v:
-                out.append(f"| {kind} ({label}, all) | all | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} "
-                           f"| {max(v):.2f} |")
-    v = tot.get("read_probe_kernel")
-    if v:
-        out.append(f"| read_probe_kernel (plain read of the same bytes, all) | all | {len(v)} | "
-                   f"{sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-    out.append("")
-    out.append("bench line of the same command (events; the trace itself slows the launches): "
-               f"roofline avg_launch_us {bl['roofline']['avg_launch_us']}, value {bl['value']} GB/s")
-    sw = [x for (kind, n, wgs), v in dur.items() if static_split(n) for x in v]
-    line = (f"roofline kernel (sweep split launches, static plan, D 128, 3 consumers): trace average "
-            f"{sum(sw) / len(sw):.2f} us over {len(sw)} launches")
-    if os.path.exists(os.path.join(d, "bench.log")):
-        pl = bench_line("bench.log")
-        if pl["kernel_hash"] == kernel_hash():
-            line += (f"; the same bench without the profiler ({py} --steps 10 --warmup 3): avg_launch_us "
-                     f"{pl['roofline']['avg_launch_us']}, value {pl['value']} GB/s")
-    out.append("")
-    out.append(line)
-    out.append("")
-    out.append("## HBM traffic of split_kernel (rocprofv3 --pmc, one counter per run)")
-    out.append("")
-    out.append(f"command: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/pmc_fetch -o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline")
-    out.append(f"command: rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/pmc_write -o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline")
-    out.append(f"calibration: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE ... -- {py} --copy-probe {COPY_PROBE_MIB}"
-               f" (device copy of {COPY_PROBE_MIB} MiB: FETCH_SIZE reads {sum(cf) / len(cf):.0f} KiB,"
-               f" WRITE_SIZE {sum(cw) / len(cw):.0f} KiB -> scale {f_scale:.4f} / {w_scale:.4f})")
-    out.append("")
-    out.append("| workgroups | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |")
-    out.append("|---|---|---|---|---|")
-    byg = collections.defaultdict(list)
-    for (g, f), (_, w) in zip(fe, wr):
-        byg[g].append((f, w))
-    for g in sorted(byg):
-        v = byg[g]
-        fa = sum(x[0] for x in v) / len(v)
-        wa = sum(x[1] for x in v) / len(v)
-        out.append(f"| {g} | {len(v)} | {fa:.1f} | {wa:.1f} | {(fa * f_scale + wa * w_scale) * 1024:.0f} |")
-    out.append("")
-    out.append(f"mean HBM bytes per split launch over the sweep: {traffic:.0f}"
-               f" (algorithmic KV bytes per launch: {bl['roofline']['algorithmic_bytes_per_launch']})")
+    # the attention sweep's summaries need its kernel trace and traffic runs;
+    # the sampler and kv-write summaries below need only their own runs
+    if os.path.exists(os.path.join(d, "trace.log")):
+        hashes = {bench_line(x)["kernel_hash"] for x in ("trace.log", "fetch.log", "write.log")}
+        if len(hashes) != 1 or kernel_hash() not in hashes:
+            raise SystemExit(f"profiles were taken of another kernel source: {hashes} vs {kernel_hash()}")
+        copy_bytes = COPY_PROBE_MIB << 20
+        cf = [v for n, g, v in counters("pmc_copy_fetch", "copy_counter_collection.csv") if "copyBuffer" in n]
+        cw = [v for n, g, v in counters("pmc_copy_write", "copy_counter_collection.csv") if "copyBuffer" in n]
+        f_scale = copy_bytes / (sum(cf) / len(cf) * 1024)
+        w_scale = copy_bytes / (sum(cw) / len(cw) * 1024)
+        def static_split(n):  # the sweep's kernel: static plan, D 128, 3 consumer waves, bf16
+            return "split_kernel<128,3,0,4,2,false>" in kname(n)
 
-    up = os.path.join(d, "pmc_util", "bench_counter_collection.csv")
-    if os.path.exists(up):
-        if bench_line("util.log")["kernel_hash"] != kernel_hash():
-            raise SystemExit("utilisation counters of another kernel source")
-        # Counter values are whole-GPU totals per dispatch (SQ_INSTS_MFMA of
-        # the 33-workgroup launch is exactly 33 x 3 waves x 16).  Busy
-        # fractions divide by the kernel-trace duration of the same kernel
-        # and grid at the 2.4 GHz peak clock (a lower bound if the clock ran
-        # lower); GRBM_GUI_ACTIVE is not used, since under --pmc it also
-        # counts the serialised launch around each dispatch.
-        kinds = [("split_kernel<128,3,0,4,2,false>", "split: sweep (D 128, 3 consumers, bf16)"),
-                 ("split_kernel<64,3,0,8,2,false>", "split: window ring (D 64, 3 consumers)"),
-                 ("split_kernel<128,6,0,4,2,false>", "split: tree (D 128, 6 consumers, bf16)"),
-                 ("split_kernel<128,6,1,8,1,false>", "split: quantised tree (6 consumers, 2 decoders)")]
-        tdur = collections.defaultdict(list)
-        for (kind, n, wgs), v in dur.items():
-            tdur[(kind, wgs)] += v
-        vals = collections.defaultdict(lambda: collections.defaultdict(list))
-        for r in csv.DictReader(open(up)):
+        fe = [(g, v) for n, g, v in counters("pmc_fetch", "bench_counter_collection.csv") if static_split(n)]
+        wr = [(g, v) for n, g, v in counters("pmc_write", "bench_counter_collection.csv") if static_split(n)]
+        if len(fe) != len(wr):
+            raise SystemExit("fetch and write runs saw different split launches")
+        per_launch = [f * f_scale * 1024 + w * w_scale * 1024 for (_, f), (_, w) in zip(fe, wr)]
+        traffic = sum(per_launch) / len(per_launch)
+        contexts = bench_line("fetch.log")["config"]["contexts"]
+        splits = [e["splits"] for e in bench_line("fetch.log")["sweep"]]
+        json.dump({"kernel_hash": kernel_hash(), "contexts": contexts, "splits": splits,
+                   "hbm_bytes_per_launch": round(traffic),
+                   "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "launches": len(per_launch)},
+                  open(TRAFFIC_FILE, "w"), indent=1)
+
+        trace = list(csv.DictReader(open(os.path.join(d, "trace", "bench_kernel_trace.csv"))))
+        dur = collections.defaultdict(list)
+        for r in trace:
             n = kname(r["Kernel_Name"])
-            wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
-            for key, _ in kinds:
-                if key in n:
-                    vals[(key, wgs)][r["Counter_Name"]].append(float(r["Counter_Value"]))
-        out += ["", "## MFMA and LDS activity of split_kernel (rocprofv3 --pmc, one run)", "",
-                f"command: rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d <dir>/pmc_util -o bench -- {py} --steps 2 "
-                "--warmup 0 --kernel-reps 4 --no-cpu-baseline", "",
-                "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x trace duration x 2.4 GHz); MFMA TFLOP/s = "
-                "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / trace duration; LDS conflict = SQ_LDS_BANK_CONFLICT / "
-                "(SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT).", "",
-                "| kernel | workgroups | dispatches | MFMA per dispatch | trace us | MFMA busy % | MFMA TFLOP/s | "
-                "LDS conflict |", "|---|---|---|---|---|---|---|---|"]
-        summary = {}
-        tot_busy = tot_us = 0.0
-        for key, label in kinds:
-            for (k2, wgs) in sorted(x for x in vals if x[0] == key):
-                v = vals[(k2, wgs)]
-                t = tdur.get((key, wgs))
-                if not t or not v.get("SQ_VALU_MFMA_BUSY_CYCLES"):
-                    continue
-                us = sum(t) / len(t)
-                busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(v["SQ_VALU_MFMA_BUSY_CYCLES"])
-                mops = sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) / len(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
-                ninst = sum(v["SQ_INSTS_MFMA"]) / len(v["SQ_INSTS_MFMA"])
-                conf = sum(v["SQ_LDS_BANK_CONFLICT"])
-                act = sum(v["SQ_LDS_IDX_ACTIVE"])
-                pct = 100 * busy / (1024 * us * 1e-6 * 2.4e9)
-                tf = mops * 512 / (us * 1e-6) / 1e12
-                lc = conf / (act - conf) if act > conf else 0.0
-                out.append(f"| {label} | {wgs} | {len(v['SQ_VALU_MFMA_BUSY_CYCLES'])} | {ninst:.0f} | {us:.2f} | "
-                           f"{pct:.1f} | {tf:.1f} | {lc:.3f} |")
-                summary[f"{key}@{wgs}"] = {"mfma_busy_pct": round(pct, 2), "mfma_tflops": round(tf, 1),
-                                           "lds_conflict": round(lc, 4)}
-                if key == kinds[0][0]:
-                    tot_busy += busy * len(t)
-                    tot_us += us * len(t)
-        if tot_us:
-            sweep_pct = 100 * tot_busy / (1024 * tot_us * 1e-6 * 2.4e9)
-            out += ["", f"sweep kernel, launches weighted as in the trace: MFMA busy {sweep_pct:.1f}%"]
-            json.dump({"kernel_hash": kernel_hash(), "kernel": kinds[0][0], "mfma_busy_pct": round(sweep_pct, 2),
-                       "clock_ghz": 2.4, "by_kernel": summary}, open(UTIL_FILE, "w"), indent=1)
-    name = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep.md")
-    open(name, "w").write("\n".join(out) + "\n")
-    print(f"wrote {name} and {TRAFFIC_FILE}")
+            kind = ("split_kernel" if "split_kernel" in n else "combine_kernel" if "combine_kernel" in n
+                    else "read_probe_kernel" if "read_probe_kernel" in n else None)
+            if kind and "<" in n:
+                kind += n[n.index("<"):n.index(">") + 1].replace(" ", "")
+            if kind:
+                dur[(kind, n, trace_workgroups(r))].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        bl = bench_line("trace.log")
+        out = []
+        out.append("# split_kernel / combine_kernel, full-attention verify sweep (Hkv 1, Hq 6, D 128, 8 rows, ctx 1K-192K)")
+        out.append("")
+        out.append(f"kernel source sha256[:16]: {kernel_hash()}")
+        out.append("")
+        out.append("## Kernel durations (rocprofv3 kernel trace)")
+        out.append("")
+        out.append(f"command: rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace -o bench -- {py} --steps 10 --warmup 3")
+        out.append("")
+        out.append("| kernel | workgroups | launches | avg us | min us | max us |")
+        out.append("|---|---|---|---|---|---|")
+        tot = collections.defaultdict(list)
+        for (kind, n, wgs), v in sorted(dur.items(), key=lambda x: (x[0][0], x[0][2])):
+            tot[kind] += v
+            out.append(f"| {kind} | {wgs} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        for kind in ("split_kernel", "combine_kernel"):
+            for flag, label in (("false>", "static plan"), ("true>", "device state")):
+                v = [x for k, x in tot.items() if k.startswith(kind) and k.endswith(flag) for x in x]
+                if v:
+                    out.append(f"| {kind} ({label}, all) | all | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} "
+                               f"| {max(v):.2f} |")
+        v = tot.get("read_probe_kernel")
+        if v:
+            out.append(f"| read_probe_kernel (plain read of the same bytes, all) | all | {len(v)} | "
+                       f"{sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        out.append("")
+        out.append("bench line of the same command (events; the trace itself slows the launches): "
+                   f"roofline avg_launch_us {bl['roofline']['avg_launch_us']}, value {bl['value']} GB/s")
+        sw = [x for (kind, n, wgs), v in dur.items() if static_split(n) for x in v]
+        line = (f"roofline kernel (sweep split launches, static plan, D 128, 3 consumers): trace average "
+                f"{sum(sw) / len(sw):.2f} us over {len(sw)} launches")
+        if os.path.exists(os.path.join(d, "bench.log")):
+            pl = bench_line("bench.log")
+            if pl["kernel_hash"] == kernel_hash():
+                line += (f"; the same bench without the profiler ({py} --steps 10 --warmup 3): avg_launch_us "
+                         f"{pl['roofline']['avg_launch_us']}, value {pl['value']} GB/s")
+        out.append("")
+        out.append(line)
+        out.append("")
+        out.append("## HBM traffic of split_kernel (rocprofv3 --pmc, one counter per run)")
+        out.append("")
+        out.append(f"command: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/pmc_fetch -o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline")
+        out.append(f"command: rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/pmc_write -o bench -- {py} --steps 2 --warmup 0 --kernel-reps 4 --no-cpu-baseline")
+        out.append(f"calibration: rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE ... -- {py} --copy-probe {COPY_PROBE_MIB}"
+                   f" (device copy of {COPY_PROBE_MIB} MiB: FETCH_SIZE reads {sum(cf) / len(cf):.0f} KiB,"
+                   f" WRITE_SIZE {sum(cw) / len(cw):.0f} KiB -> scale {f_scale:.4f} / {w_scale:.4f})")
+        out.append("")
+        out.append("| workgroups | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |")
+        out.append("|---|---|---|---|---|")
+        byg = collections.defaultdict(list)
+        for (g, f), (_, w) in zip(fe, wr):
+            byg[g].append((f, w))
+        for g in sorted(byg):
+            v = byg[g]
+            fa = sum(x[0] for x in v) / len(v)
+            wa = sum(x[1] for x in v) / len(v)
+            out.append(f"| {g} | {len(v)} | {fa:.1f} | {wa:.1f} | {(fa * f_scale + wa * w_scale) * 1024:.0f} |")
+        out.append("")
+        out.append(f"mean HBM bytes per split launch over the sweep: {traffic:.0f}"
+                   f" (algorithmic KV bytes per launch: {bl['roofline']['algorithmic_bytes_per_launch']})")
 
-    wave_cycles(d, kname, py)
-    phase_table(d, py)
+        up = os.path.join(d, "pmc_util", "bench_counter_collection.csv")
+        if os.path.exists(up):
+            if bench_line("util.log")["kernel_hash"] != kernel_hash():
+                raise SystemExit("utilisation counters of another kernel source")
+            # Counter values are whole-GPU totals per dispatch (SQ_INSTS_MFMA of
+            # the 33-workgroup launch is exactly 33 x 3 waves x 16).  Busy
+            # fractions divide by the kernel-trace duration of the same kernel
+            # and grid at the 2.4 GHz peak clock (a lower bound if the clock ran
+            # lower); GRBM_GUI_ACTIVE is not used, since under --pmc it also
+            # counts the serialised launch around each dispatch.
+            kinds = [("split_kernel<128,3,0,4,2,false>", "split: sweep (D 128, 3 consumers, bf16)"),
+                     ("split_kernel<64,3,0,8,2,false>", "split: window ring (D 64, 3 consumers)"),
+                     ("split_kernel<128,6,0,4,2,false>", "split: tree (D 128, 6 consumers, bf16)"),
+                     ("split_kernel<128,6,1,8,1,false>", "split: quantised tree (6 consumers, 2 decoders)")]
+            tdur = collections.defaultdict(list)
+            for (kind, n, wgs), v in dur.items():
+                tdur[(kind, wgs)] += v
+            vals = collections.defaultdict(lambda: collections.defaultdict(list))
+            for r in csv.DictReader(open(up)):
+                n = kname(r["Kernel_Name"])
+                wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+                for key, _ in kinds:
+                    if key in n:
+                        vals[(key, wgs)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            out += ["", "## MFMA and LDS activity of split_kernel (rocprofv3 --pmc, one run)", "",
+                    f"command: rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d <dir>/pmc_util -o bench -- {py} --steps 2 "
+                    "--warmup 0 --kernel-reps 4 --no-cpu-baseline", "",
+                    "MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x trace duration x 2.4 GHz); MFMA TFLOP/s = "
+                    "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / trace duration; LDS conflict = SQ_LDS_BANK_CONFLICT / "
+                    "(SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT).", "",
+                    "| kernel | workgroups | dispatches | MFMA per dispatch | trace us | MFMA busy % | MFMA TFLOP/s | "
+                    "LDS conflict |", "|---|---|---|---|---|---|---|---|"]
+            summary = {}
+            tot_busy = tot_us = 0.0
+            for key, label in kinds:
+                for (k2, wgs) in sorted(x for x in vals if x[0] == key):
+                    v = vals[(k2, wgs)]
+                    t = tdur.get((key, wgs))
+                    if not t or not v.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                        continue
+                    us = sum(t) / len(t)
+                    busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(v["SQ_VALU_MFMA_BUSY_CYCLES"])
+                    mops = sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) / len(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+                    ninst = sum(v["SQ_INSTS_MFMA"]) / len(v["SQ_INSTS_MFMA"])
+                    conf = sum(v["SQ_LDS_BANK_CONFLICT"])
+                    act = sum(v["SQ_LDS_IDX_ACTIVE"])
+                    pct = 100 * busy / (1024 * us * 1e-6 * 2.4e9)
+                    tf = mops * 512 / (us * 1e-6) / 1e12
+                    lc = conf / (act - conf) if act > conf else 0.0
+                    out.append(f"| {label} | {wgs} | {len(v['SQ_VALU_MFMA_BUSY_CYCLES'])} | {ninst:.0f} | {us:.2f} | "
+                               f"{pct:.1f} | {tf:.1f} | {lc:.3f} |")
+                    summary[f"{key}@{wgs}"] = {"mfma_busy_pct": round(pct, 2), "mfma_tflops": round(tf, 1),
+                                               "lds_conflict": round(lc, 4)}
+                    if key == kinds[0][0]:
+                        tot_busy += busy * len(t)
+                        tot_us += us * len(t)
+            if tot_us:
+                sweep_pct = 100 * tot_busy / (1024 * tot_us * 1e-6 * 2.4e9)
+                out += ["", f"sweep kernel, launches weighted as in the trace: MFMA busy {sweep_pct:.1f}%"]
+                json.dump({"kernel_hash": kernel_hash(), "kernel": kinds[0][0], "mfma_busy_pct": round(sweep_pct, 2),
+                           "clock_ghz": 2.4, "by_kernel": summary}, open(UTIL_FILE, "w"), indent=1)
+        name = os.path.join(ROOT, "profiles", "split_kernel_verify_sweep.md")
+        open(name, "w").write("\n".join(out) + "\n")
+        print(f"wrote {name} and {TRAFFIC_FILE}")
+
+        wave_cycles(d, kname, py)
+        phase_table(d, py)
 
     st = os.path.join(d, "trace_sampler", "sampler_kernel_trace.csv")
     if os.path.exists(st):
