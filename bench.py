@@ -526,8 +526,8 @@ def summarize_profiles(d):
         open(name, "w").write("\n".join(out) + "\n")
         print(f"wrote {name} and {TRAFFIC_FILE}")
 
-        wave_cycles(d, kname, py)
-        phase_table(d, py)
+    wave_cycles(d, kname, py)
+    phase_table(d, py)
 
     st = os.path.join(d, "trace_sampler", "sampler_kernel_trace.csv")
     if os.path.exists(st):
