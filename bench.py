@@ -977,7 +977,7 @@ def bench_phases(torch, va, synth, dev, graphs=6, pairs=4, replays=12):
             ws = va.workspace_for(plan, dev)
             o = torch.empty((c["rows"], c["hq"], c["d"]), dtype=torch.float32, device=dev)
             lse = torch.empty((c["rows"], c["hq"]), dtype=torch.float32, device=dev)
-            nsw = plan.splits * plan.problem.kv_heads
+            nsw = plan.splits * plan.problem.kv_heads * plan.info["row_groups"]
             ncw = c["rows"] * c["hq"] * (c["d"] // 32)
             grs = []
             for gi in range(graphs):

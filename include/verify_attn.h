@@ -119,6 +119,9 @@ typedef struct {
   int64_t row_hi[VA_MAX_ROWS];
   uint32_t anc[VA_MAX_ROWS];   /* tree: bit j set iff node j is node r or its ancestor     */
   size_t workspace_bytes;
+  int32_t row_groups;          /* workgroups per (split, KV head): 2 when the matrix rows
+                                  fill more than four 16-row blocks and 2 * S * Hkv <=
+                                  num_cus, each taking half the row blocks; else 1         */
 } va_plan_info;
 
 /* Validate *p and build *plan.  Writes the workspace size the split needs to

@@ -66,6 +66,7 @@ class va_plan_info(ctypes.Structure):
         ("chunk_lo", ctypes.c_int64), ("chunks", ctypes.c_int64),
         ("row_lo", ctypes.c_int64 * VA_MAX_ROWS), ("row_hi", ctypes.c_int64 * VA_MAX_ROWS),
         ("anc", ctypes.c_uint32 * VA_MAX_ROWS), ("workspace_bytes", ctypes.c_size_t),
+        ("row_groups", ctypes.c_int32),
     ]
 
 
@@ -184,7 +185,7 @@ def verify_attn_plan_query(plan):
     return {
         "splits": info.splits, "matrix_rows": info.matrix_rows, "lo": info.lo, "hi": info.hi,
         "chunk_lo": info.chunk_lo, "chunks": info.chunks, "row_lo": list(info.row_lo), "row_hi": list(info.row_hi),
-        "anc": list(info.anc), "workspace_bytes": info.workspace_bytes,
+        "anc": list(info.anc), "workspace_bytes": info.workspace_bytes, "row_groups": info.row_groups,
     }
 
 

@@ -182,6 +182,22 @@ extern "C" va_status verify_attn_plan(const va_problem *p, va_plan *plan, size_t
   d.splits = p->splits > 0 ? p->splits
                            : choose_splits(d.chunks, d.kv_heads, p->num_cus, granule_bytes, partial_bytes);
 
+  // Row groups.  A consumer wave owns 16 matrix rows and one SIMD runs the
+  // producers' and up to four consumers' work side by side; from five
+  // 16-row blocks on (80 or 96 matrix rows: the 16-node tree at G = 6) two
+  // consumers share a SIMD and each step takes about twice as long.  When
+  // twice the workgroups still fit one per CU, each (split, KV head) is run
+  // by two workgroups that stream the same keys and take half the row
+  // blocks each (bf16 tree, ABBA on MI355X: calls 10.55 -> 9.12 us at 2K
+  // keys and 14.2 -> 12.5 us at 8K).  Every row's partials are the same
+  // either way: a row block's arithmetic does not depend on the workgroup
+  // that runs it.
+  {
+    const int32_t blocks = (d.matrix_rows + 15) / 16;
+    const int64_t cus = p->num_cus > 0 ? p->num_cus : 256;
+    d.row_groups = (blocks >= 5 && (int64_t)d.splits * d.kv_heads * 2 <= cus) ? 2 : 1;
+  }
+
   const uint64_t units = (uint64_t)d.splits * d.kv_heads * d.matrix_rows;
   d.ml_bytes = ((units * 2 * sizeof(float)) + 255) / 256 * 256;
   d.workspace_bytes = d.ml_bytes + units * d.head_dim * sizeof(float);
@@ -213,6 +229,7 @@ extern "C" va_status verify_attn_plan_query(const va_plan *plan, va_plan_info *i
     info->anc[r] = d->anc[r];
   }
   info->workspace_bytes = (size_t)d->workspace_bytes;
+  info->row_groups = d->row_groups;
   return VA_OK;
 }
 

@@ -14,6 +14,7 @@ struct va_plan_data {
   int32_t matrix_rows;  // rows * G
   int32_t mask, kv_fmt, window, ring_slots, splits;
   int32_t ring_base_slot;  // (chunk_lo * 32) mod ring_slots, 0 for a linear cache
+  int32_t row_groups;      // workgroups per (split, KV head), each taking a share of the matrix rows
   int64_t first_pos, prefix_len, kv_capacity;
   int64_t lo, hi;          // union extent of the live rows' visible keys
   int64_t chunk_lo, chunks;  // 32-key granules [chunk_lo, chunk_lo + chunks) cover [lo, hi)

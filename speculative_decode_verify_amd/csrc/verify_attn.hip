@@ -99,6 +99,7 @@ struct SplitArgs {
   int64_t new_row_stride_b;
   int64_t kv_capacity;
   int64_t append_pos0;  // absolute position of row 0's key (first_pos, or prefix_len for a tree)
+  int32_t row_groups;   // grid z: workgroups per (split, KV head), W row blocks each
 };
 
 struct CombineArgs {
@@ -753,7 +754,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
       // this launch reads those slots from memory: the live rows' keys were
       // put into the tiles above, and the padding rows' slots lie outside
       // every row's keys
-      if (APP && split == 0) {
+      if (APP && split == 0 && blockIdx.z == 0) {
         uint8_t *dst = (PW == 0 ? const_cast<uint8_t *>(kptr) : const_cast<uint8_t *>(vptr)) +
                        (int64_t)kvh * head_stride + 16 * (lane % PIECES);
 #pragma unroll
@@ -783,12 +784,14 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   VA_TRACE_VAL(va_trace_split, 0, t_entry, wave == 0 && lane == 0);  // kernel entry
   VA_TRACE(va_trace_split, 1, wave == 0 && lane == 0);   // arguments in registers
 
-  // lane column i16 of this wave is query matrix row m = 16*wave + i16 =
-  // r*G + (h - kvh*G); live matrix rows are [0, live_rows * G).
-  const int m = 16 * wave + i16;
+  // lane column i16 of this wave is query matrix row m = 16*(wave + z*W) +
+  // i16 = r*G + (h - kvh*G), z = blockIdx.z the workgroup's row group; live
+  // matrix rows are [0, live_rows * G).
+  const int mb = 16 * (wave + (int)blockIdx.z * W);  // first matrix row of this wave
+  const int m = mb + i16;
   const int r = (int)(((float)m + 0.5f) * inv_group);  // m / G: exact for every m < 96, G <= 96
   const bool row_ok = (m < mrows) && (r < live_rows);
-  const bool active = 16 * wave < live_rows * group;  // wave-uniform
+  const bool active = mb < live_rows * group;  // wave-uniform
   const int rr = row_ok ? r : 0;
   const int h = kvh * group + (row_ok ? m - r * group : 0);
   const uint8_t *qrow = qptr + (int64_t)(rr * q_heads + h) * D * 2;
@@ -1456,7 +1459,7 @@ template <int D, int W, int FMT, bool STATE, bool APP>
 hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
-  dim3 grid(a.splits, a.kv_heads);
+  dim3 grid(a.splits, a.kv_heads, a.row_groups);
   constexpr int NDW = decoders_for<FMT>();
   hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE, APP>), grid, dim3(64 * (W + NDW + NPW)), 0, stream,
                      a);
@@ -1553,7 +1556,9 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
     a.kv_capacity = d->kv_capacity;
     a.append_pos0 = d->mask == VA_MASK_TREE ? d->prefix_len : d->first_pos;
   }
-  const int nb_total = (d->matrix_rows + 15) / 16;
+  a.row_groups = d->row_groups;
+  // 16-row blocks per workgroup (the consumer waves W)
+  const int nb_total = (d->matrix_rows + 16 * d->row_groups - 1) / (16 * d->row_groups);
   hipError_t e;
   if (k_new && state) {  // bf16 only (checked by the entry points)
     e = d->head_dim == 64 ? dispatch_rows<64, 0, true, true>(a, nb_total, stream)

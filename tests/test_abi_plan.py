@@ -69,6 +69,9 @@ def test_struct_sizes_match_c_layout():
     # va_problem: eleven int32, int32[16], (pad), three int64, float, int32
     assert ctypes.sizeof(_binding.va_problem) == 144
     assert ctypes.sizeof(_binding.va_plan) == 2048
+    # va_plan_info: two int32, four int64, int64[16] x 2, uint32[16], size_t,
+    # int32 (+ tail padding)
+    assert ctypes.sizeof(_binding.va_plan_info) == 8 + 32 + 256 + 64 + 8 + 8
 
 
 def _status(**kw):
@@ -270,3 +273,30 @@ def test_chosen_splits_are_sane():
     plan = va.Plan(rows=16, live_rows=16, q_heads=24, kv_heads=4, head_dim=128, mask="tree", prefix_len=200000,
                    parent=[-1] * 16, kv_capacity=200100, num_cus=40)
     assert plan.splits == 8
+
+
+def test_row_groups_rule():
+    """Two workgroups per (split, KV head) exactly when the matrix rows fill
+    more than four 16-row blocks and twice the workgroups fit one per CU:
+    the 16-node tree over four KV heads at 2K and 8K keys (16 and 32
+    splits), not at 32K (64 splits) or for the 48-row sweep."""
+    def tree(P, num_cus=256, live=16, rows=16, q_heads=24, fmt="bf16"):
+        return va.Plan(rows=rows, live_rows=live, q_heads=q_heads, kv_heads=4, head_dim=128, mask="tree",
+                       prefix_len=P, parent=[-1] * rows, kv_capacity=P + 100, num_cus=num_cus, kv_fmt=fmt)
+    for P, want in ((2048, 2), (8192, 2), (32768, 1)):
+        plan = tree(P)
+        assert plan.info["row_groups"] == want, (P, plan.splits, plan.info["row_groups"])
+        assert (2 * plan.splits * 4 <= 256) == (want == 2)
+    assert tree(8192, num_cus=128).info["row_groups"] == 1  # 2 * 32 * 4 > 128
+    assert tree(2048, fmt="e4m3_wht_i8").info["row_groups"] == 2
+    # 80 matrix rows (five blocks) qualify, 64 (four blocks) do not
+    assert tree(2048, rows=16, q_heads=20).info["row_groups"] == 2
+    assert tree(2048, rows=16, q_heads=16).info["row_groups"] == 1
+    for P in (1024, 16384, 196608):
+        plan = va.Plan(rows=8, live_rows=8, q_heads=6, kv_heads=1, head_dim=128, first_pos=P,
+                       kv_capacity=262144, num_cus=256)
+        assert plan.info["row_groups"] == 1
+    # the workspace does not depend on the row groups
+    plan = tree(2048)
+    units = plan.splits * 4 * 96
+    assert plan.workspace_bytes == (units * 8 + 255) // 256 * 256 + units * 128 * 4

@@ -83,7 +83,7 @@ def test_trace_build_matches_product_and_orders_phases(case):
     binding._LIB = lib
     try:
         o_t, l_t, ws_t = run(plan, qd, kd, vd, sd, vsd)
-        n_split = plan.splits * plan.kv_heads
+        n_split = plan.splits * plan.kv_heads * plan.info["row_groups"]
         n_comb = plan.rows * plan.q_heads * (plan.head_dim // 32)
         sp = _records(lib, 0, n_split)
         cb = _records(lib, 1, n_comb)
@@ -97,7 +97,7 @@ def test_trace_build_matches_product_and_orders_phases(case):
     # split records: the split table's chunk counts and ordered phases
     S = plan.splits
     C = plan.info["chunks"]
-    want_nch = np.array([C // S + (1 if s < C % S else 0) for s in range(S)] * plan.kv_heads)
+    want_nch = np.array([C // S + (1 if s < C % S else 0) for s in range(S)] * plan.kv_heads * plan.info["row_groups"])
     assert np.array_equal(sp[:, 7], want_nch)
     busy = sp[:, 7] > 0
     assert busy.any()
@@ -107,7 +107,7 @@ def test_trace_build_matches_product_and_orders_phases(case):
     assert np.all((bar >= 0) & (bar <= last - c0))
     # each role's time at the later barriers (a duration inside the steps'
     # span); consumer wave 0's is the one already checked
-    W = -(-plan.rows * (plan.q_heads // plan.kv_heads) // 16)
+    W = -(-plan.rows * (plan.q_heads // plan.kv_heads) // (16 * plan.info["row_groups"]))
     roles = [8 + w for w in range(W)] + [14, 15] + ([16, 17] if case == 1 else [])
     span = (wr - e)[:, None]
     waits = sp[busy][:, roles]
