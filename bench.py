@@ -186,6 +186,7 @@ def wave_cycles(d, kname, py):
     import collections
     kinds = [("split_kernel<128,3,0,4,2,false>", "sweep (D 128, 3 consumers, bf16)"),
              ("split_kernel<128,6,0,4,2,false>", "tree (D 128, 6 consumers, bf16)"),
+             ("split_kernel<128,3,0,4,2,false,rows2>", "tree, two row groups (D 128, 3 consumers each, bf16)"),
              ("split_kernel<128,6,1,8,1,false>", "quantised tree (E4M3 keys, INT8 values)")]
 
     def table(subs, log):
@@ -269,6 +270,53 @@ def trace_workgroups(r):
     return n
 
 
+IC_COUNTERS = "SQC_ICACHE_MISSES SQC_ICACHE_HITS SQC_ICACHE_MISSES_DUPLICATE SQC_DCACHE_MISSES SQC_DCACHE_HITS SQ_WAVES"
+
+
+def icache_table(d, kname, py):
+    """profiles/split_kernel_icache.md from a `--pmc` run of IC_COUNTERS
+    (pmc_ic/, log ic.log) at 1K and 64K: instruction- and scalar-cache
+    misses of the sweep's split kernel, the combine and the plain read."""
+    import csv
+    import collections
+    path = os.path.join(d, "pmc_ic", "ic_counter_collection.csv")
+    if not os.path.exists(path):
+        return
+    for x in open(os.path.join(d, "ic.log")):
+        if x.startswith("{") and '"metric"' in x and json.loads(x)["kernel_hash"] != kernel_hash():
+            raise SystemExit("cache counters of another kernel source")
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        n = kname(r["Kernel_Name"])
+        if "split_kernel<128,3,0,4,2,false>" in n:
+            name = "split_kernel<128,3,0,4,2,false>"
+        elif "combine_kernel<" in n:
+            name = n[n.index("combine_kernel<"):n.index(">", n.index("combine_kernel<")) + 1]
+        elif "read_probe_kernel" in n:
+            name = "read_probe_kernel"
+        else:
+            continue
+        wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+        agg[(name, wgs)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    o = ["# split_kernel instruction- and scalar-cache counters (sweep, 1K and 64K)", "",
+         f"kernel source sha256[:16]: {kernel_hash()}", "",
+         f"command: rocprofv3 --pmc {IC_COUNTERS} -f csv -d <dir>/pmc_ic -o ic -- {py} --steps 2 --warmup 0 "
+         "--kernel-reps 4 --no-cpu-baseline --ctx 1024 --ctx 65536", "",
+         "Whole-GPU totals per dispatch, averaged over the dispatches of each kernel and grid (the SQC "
+         "counters are summed over every instruction and scalar cache).", "",
+         "| kernel | workgroups | dispatches | I-cache misses | per workgroup | I-cache hits | duplicate misses "
+         "| K-cache misses | K-cache hits |", "|---|---|---|---|---|---|---|---|---|"]
+    for (name, wgs), v in sorted(agg.items()):
+        a = {c: sum(x) / len(x) for c, x in v.items()}
+        o.append(f"| {name} | {wgs} | {len(v['SQ_WAVES'])} | {a['SQC_ICACHE_MISSES']:.0f} | "
+                 f"{a['SQC_ICACHE_MISSES'] / wgs:.1f} | {a['SQC_ICACHE_HITS']:.0f} | "
+                 f"{a['SQC_ICACHE_MISSES_DUPLICATE']:.0f} | {a['SQC_DCACHE_MISSES']:.0f} | {a['SQC_DCACHE_HITS']:.0f} |")
+    name = os.path.join(ROOT, "profiles", "split_kernel_icache.md")
+    open(name, "w").write("\n".join(o) + "\n")
+    print(f"wrote {name}")
+
+
+
 def phase_table(d, py):
     """profiles/split_kernel_phases.md from the `--phases` run (phases.log)."""
     path = os.path.join(d, "phases.log")
@@ -337,15 +385,17 @@ def summarize_profiles(d):
     import collections
 
     def kname(n):
-        """Kernel name without spaces; split_kernel's last template flag (the
-        fused append) becomes ",append" when set and is dropped otherwise."""
+        """Kernel name without spaces; split_kernel's last two template
+        arguments, the fused append and the row groups, become ",append"
+        when set and ",rows2" for two row groups, and are dropped otherwise."""
         n = n.replace(" ", "")
         if "split_kernel<" in n:
             i = n.index("split_kernel<") + len("split_kernel<")
             j = n.index(">", i)
             args = n[i:j].split(",")
-            if len(args) == 7:
-                args = args[:6] + (["append"] if args[6] == "true" else [])
+            if len(args) >= 7:  # earlier sources have no row-group argument
+                args = (args[:6] + (["append"] if args[6] == "true" else [])
+                        + ([f"rows{args[7]}"] if len(args) > 7 and args[7] != "1" else []))
             n = n[:i] + ",".join(args) + n[j:]
         return n
 
@@ -474,6 +524,7 @@ def summarize_profiles(d):
             kinds = [("split_kernel<128,3,0,4,2,false>", "split: sweep (D 128, 3 consumers, bf16)"),
                      ("split_kernel<64,3,0,8,2,false>", "split: window ring (D 64, 3 consumers)"),
                      ("split_kernel<128,6,0,4,2,false>", "split: tree (D 128, 6 consumers, bf16)"),
+                     ("split_kernel<128,3,0,4,2,false,rows2>", "split: tree, two row groups (3 consumers each)"),
                      ("split_kernel<128,6,1,8,1,false>", "split: quantised tree (6 consumers, 2 decoders)")]
             tdur = collections.defaultdict(list)
             for (kind, n, wgs), v in dur.items():
@@ -528,6 +579,7 @@ def summarize_profiles(d):
 
     wave_cycles(d, kname, py)
     phase_table(d, py)
+    icache_table(d, kname, py)
 
     st = os.path.join(d, "trace_sampler", "sampler_kernel_trace.csv")
     if os.path.exists(st):

@@ -99,7 +99,6 @@ struct SplitArgs {
   int64_t new_row_stride_b;
   int64_t kv_capacity;
   int64_t append_pos0;  // absolute position of row 0's key (first_pos, or prefix_len for a tree)
-  int32_t row_groups;   // grid z: workgroups per (split, KV head), W row blocks each
 };
 
 struct CombineArgs {
@@ -376,7 +375,7 @@ __device__ __forceinline__ void trace_put(uint64_t *rec, int len, int slot, uint
 template <int FMT>
 constexpr int decoders_for() { return FMT == 1 ? 2 : 0; }
 
-template <int D, int W, int FMT, int NST, int NPW, bool STATE, bool APP>
+template <int D, int W, int FMT, int NST, int NPW, bool STATE, bool APP, int RG>
 __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_kernel(const SplitArgs a) {
   static_assert(!APP || (FMT == 0 && NPW == 2), "append: bf16 tiles, one producer per tile kind");
 #ifdef VA_PHASE_TRACE
@@ -754,7 +753,7 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
       // this launch reads those slots from memory: the live rows' keys were
       // put into the tiles above, and the padding rows' slots lie outside
       // every row's keys
-      if (APP && split == 0 && blockIdx.z == 0) {
+      if (APP && split == 0 && (RG == 1 || blockIdx.z == 0)) {
         uint8_t *dst = (PW == 0 ? const_cast<uint8_t *>(kptr) : const_cast<uint8_t *>(vptr)) +
                        (int64_t)kvh * head_stride + 16 * (lane % PIECES);
 #pragma unroll
@@ -785,9 +784,9 @@ __global__ __launch_bounds__(64 * (W + NPW + decoders_for<FMT>())) void split_ke
   VA_TRACE(va_trace_split, 1, wave == 0 && lane == 0);   // arguments in registers
 
   // lane column i16 of this wave is query matrix row m = 16*(wave + z*W) +
-  // i16 = r*G + (h - kvh*G), z = blockIdx.z the workgroup's row group; live
-  // matrix rows are [0, live_rows * G).
-  const int mb = 16 * (wave + (int)blockIdx.z * W);  // first matrix row of this wave
+  // i16 = r*G + (h - kvh*G), z = blockIdx.z < RG the workgroup's row group;
+  // live matrix rows are [0, live_rows * G).
+  const int mb = 16 * (wave + (RG > 1 ? (int)blockIdx.z * W : 0));  // first matrix row of this wave
   const int m = mb + i16;
   const int r = (int)(((float)m + 0.5f) * inv_group);  // m / G: exact for every m < 96, G <= 96
   const bool row_ok = (m < mrows) && (r < live_rows);
@@ -1455,19 +1454,24 @@ constexpr int producers_for() { return FMT == 1 ? 1 : 2; }
 template <int D, int FMT>
 constexpr int stages_for() { return FMT == 1 ? 8 : (D == 64 ? 8 : 4); }
 
-template <int D, int W, int FMT, bool STATE, bool APP>
+template <int D, int W, int FMT, bool STATE, bool APP, int RG = 1>
 hipError_t launch_split(const SplitArgs &a, hipStream_t stream) {
   constexpr int NPW = producers_for<FMT>();
   constexpr int NST = stages_for<D, FMT>();
-  dim3 grid(a.splits, a.kv_heads, a.row_groups);
+  dim3 grid(a.splits, a.kv_heads, RG);
   constexpr int NDW = decoders_for<FMT>();
-  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE, APP>), grid, dim3(64 * (W + NDW + NPW)), 0, stream,
+  hipLaunchKernelGGL((split_kernel<D, W, FMT, NST, NPW, STATE, APP, RG>), grid, dim3(64 * (W + NDW + NPW)), 0, stream,
                      a);
   return hipGetLastError();
 }
 
+// nb_total: 16-row blocks per workgroup (the consumer waves W); rg: row
+// groups, the workgroups per (split, KV head).  The plan makes two groups
+// only from five blocks up (at most six), so a group then has three.
 template <int D, int FMT, bool STATE, bool APP = false>
-hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
+hipError_t dispatch_rows(const SplitArgs &a, int nb_total, int rg, hipStream_t stream) {
+  if (rg == 2) return nb_total == 3 ? launch_split<D, 3, FMT, STATE, APP, 2>(a, stream) : hipErrorInvalidValue;
+  if (rg != 1) return hipErrorInvalidValue;
   switch (nb_total) {
     case 1: return launch_split<D, 1, FMT, STATE, APP>(a, stream);
     case 2: return launch_split<D, 2, FMT, STATE, APP>(a, stream);
@@ -1480,10 +1484,10 @@ hipError_t dispatch_rows(const SplitArgs &a, int nb_total, hipStream_t stream) {
 }
 
 template <bool STATE>
-hipError_t dispatch_split(const SplitArgs &a, int nb_total, bool quant, int head_dim, hipStream_t stream) {
-  if (quant) return dispatch_rows<128, 1, STATE>(a, nb_total, stream);
-  if (head_dim == 64) return dispatch_rows<64, 0, STATE>(a, nb_total, stream);
-  return dispatch_rows<128, 0, STATE>(a, nb_total, stream);
+hipError_t dispatch_split(const SplitArgs &a, int nb_total, int rg, bool quant, int head_dim, hipStream_t stream) {
+  if (quant) return dispatch_rows<128, 1, STATE>(a, nb_total, rg, stream);
+  if (head_dim == 64) return dispatch_rows<64, 0, STATE>(a, nb_total, rg, stream);
+  return dispatch_rows<128, 0, STATE>(a, nb_total, rg, stream);
 }
 
 va_status split_impl(const va_plan *plan, const va_state *state, const void *q, const void *k, const void *v,
@@ -1556,19 +1560,19 @@ va_status split_impl(const va_plan *plan, const va_state *state, const void *q, 
     a.kv_capacity = d->kv_capacity;
     a.append_pos0 = d->mask == VA_MASK_TREE ? d->prefix_len : d->first_pos;
   }
-  a.row_groups = d->row_groups;
   // 16-row blocks per workgroup (the consumer waves W)
-  const int nb_total = (d->matrix_rows + 16 * d->row_groups - 1) / (16 * d->row_groups);
+  const int rg = d->row_groups;
+  const int nb_total = (d->matrix_rows + 16 * rg - 1) / (16 * rg);
   hipError_t e;
   if (k_new && state) {  // bf16 only (checked by the entry points)
-    e = d->head_dim == 64 ? dispatch_rows<64, 0, true, true>(a, nb_total, stream)
-                          : dispatch_rows<128, 0, true, true>(a, nb_total, stream);
+    e = d->head_dim == 64 ? dispatch_rows<64, 0, true, true>(a, nb_total, rg, stream)
+                          : dispatch_rows<128, 0, true, true>(a, nb_total, rg, stream);
   } else if (k_new) {
-    e = d->head_dim == 64 ? dispatch_rows<64, 0, false, true>(a, nb_total, stream)
-                          : dispatch_rows<128, 0, false, true>(a, nb_total, stream);
+    e = d->head_dim == 64 ? dispatch_rows<64, 0, false, true>(a, nb_total, rg, stream)
+                          : dispatch_rows<128, 0, false, true>(a, nb_total, rg, stream);
   } else {
-    e = state ? dispatch_split<true>(a, nb_total, quant, d->head_dim, stream)
-              : dispatch_split<false>(a, nb_total, quant, d->head_dim, stream);
+    e = state ? dispatch_split<true>(a, nb_total, rg, quant, d->head_dim, stream)
+              : dispatch_split<false>(a, nb_total, rg, quant, d->head_dim, stream);
   }
   return e == hipSuccess ? VA_OK : VA_ERR_HIP;
 }
